@@ -1,0 +1,384 @@
+"""The routed-expert MoE MLP forward, written out plainly in float64 numpy.
+
+Test infrastructure only (see ``oracle/__init__.py``).
+
+Pages cited (titles as published):
+  [TS70]   TileScale PR #70, "SM90 FP8 distributed MegaMoE example"
+  [FI5129] FlashInfer PR #5129, expert-sorted I/O for the cuTile BF16 fused MoE
+  [FI6465] FlashInfer PR #6465, Hopper MXFP4 x FP8 MegaMoE tuning candidates
+  [GCMOE]  "GC-MoE on SM120" (arXiv 2611.16219), Abstract
+  [LIG]    Liger-Kernel PR #1463, "Specialize SM90 MoE communication and fix
+           backward synchronization"
+
+What the method computes (every page agrees; [TS70] Summary/Design, [FI5129]
+Description, [FI6465] Benchmark configuration, [LIG] MoEBenchmark results): a
+router picks k experts per token; each picked expert applies a gate/up
+projection, SwiGLU and a down projection; the k expert outputs are summed
+with the top-k weights. Implemented as: route -> expert-sorted padded
+permutation -> grouped GEMM1 + SwiGLU -> grouped GEMM2 -> weighted combine.
+
+Readings where the pages are silent (each listed in the design doc):
+  * top-k ties go to the lower expert index; slots are in descending score;
+  * weights are softmax over the k selected logits (== softmax over all E,
+    renormalised over the top k), or sigmoid(logit) without renormalisation;
+  * W1 is [E, 2I, H]: gate rows [0, I), up rows [I, 2I); h = silu(gate) * up;
+  * the top-k weights are applied in the combine, in slot order j = 0..k-1;
+  * storage points: h is bf16 (BF16 path), FP8 E4M3 + fp32 1x128 scale along
+    I (FP8 path) or E4M3 + E8M0 1x32 along I (MX path); Y and out are bf16.
+Everything between two storage points is float64.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from . import formats as F
+
+SCORE_SOFTMAX = 0      # softmax over the selected logits (top-k renormalised)
+SCORE_SIGMOID = 1      # sigmoid(logit), no renormalisation (top-1 gate)
+
+DTYPE_BF16 = 0
+DTYPE_FP8_BLOCK128 = 1
+DTYPE_MXFP4W_MXFP8A = 2
+
+
+# ============================================================================ route
+def route(logits: np.ndarray, k: int, score: int = SCORE_SOFTMAX):
+    """Top-k routing. [TS70] Design, "Kernel 1: dispatch + L1 + SwiGLU" routes
+    inside the first kernel; the weighting follows the tiny-config statement
+    "softmax then top-k renormalized".
+
+    logits: fp32 values [T, E] (any float dtype; compared as given).
+    Returns ids int32 [T, k] (descending score, ties -> lower expert id) and
+    w fp32 [T, k] (computed in float64, rounded RN to fp32).
+    """
+    logits = np.asarray(logits)
+    T, E = logits.shape
+    if not (1 <= k <= E):
+        raise ValueError("route: need 1 <= k <= E")
+    l64 = logits.astype(np.float64)
+    # stable sort on the negated logit: equal logits keep ascending expert id
+    order = np.argsort(-l64, axis=1, kind="stable")
+    ids = order[:, :k].astype(np.int32)
+    sel = np.take_along_axis(l64, ids.astype(np.int64), axis=1)
+    if score == SCORE_SOFTMAX:
+        z = np.exp(sel - sel[:, :1])
+        w = z / z.sum(axis=1, keepdims=True)
+    elif score == SCORE_SIGMOID:
+        w = 1.0 / (1.0 + np.exp(-sel))
+    else:
+        raise ValueError("route: unknown score function")
+    return ids, F.round_fp32(w).astype(np.float32)
+
+
+# ============================================================================ align / sort
+def sorted_capacity(T: int, k: int, E: int, block_m: int) -> int:
+    """Upper bound on the padded sorted row count, a multiple of block_m.
+
+    Each non-empty expert pads its rows up to a multiple of block_m, adding at
+    most block_m - 1 rows, and at most min(E, T*k) experts are non-empty.
+    """
+    A = T * k
+    bound = A + min(E, A) * (block_m - 1)
+    return -(-bound // block_m) * block_m
+
+
+def align_sort(ids: np.ndarray, E: int, block_m: int):
+    """Expert-sorted, tile-padded permutation of the assignments.
+
+    [FI5129] Description: GEMM1 writes into the padded expert-sorted row space,
+    GEMM2 reads it contiguously and scatters back to assignment order; padded
+    rows feed only output rows that are dropped. [TS70] (first commit note):
+    one flat list of m-tasks replaces the per-tile rescan of experts. [LIG]
+    Summary: empty experts must not stall the schedule (they own no tiles).
+
+    Assignment a = t*k + j (token t, slot j). Returns
+      counts[E], offsets[E+1] (padded, exclusive), sorted_ids[cap]
+      (assignment ids sorted by (expert, a), pad entries = T*k),
+      tile_expert[cap // block_m] (expert of each tile, -1 past the last),
+      num_tiles.
+    """
+    T, k = ids.shape
+    A = T * k
+    flat = ids.reshape(-1).astype(np.int64)
+    if A and (flat.min() < 0 or flat.max() >= E):
+        raise ValueError("align_sort: expert id out of range")
+    cap = sorted_capacity(T, k, E, block_m)
+    counts = np.bincount(flat, minlength=E).astype(np.int64)
+    padded = -(-counts // block_m) * block_m
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(padded)
+    order = np.argsort(flat, kind="stable")          # by expert, then by a
+    sorted_ids = np.full(cap, A, dtype=np.int64)
+    start = 0
+    for e in range(E):
+        c = counts[e]
+        sorted_ids[offsets[e]:offsets[e] + c] = order[start:start + c]
+        start += c
+    num_tiles = int(offsets[E] // block_m)
+    tile_expert = np.full(cap // block_m, -1, dtype=np.int64)
+    for e in range(E):
+        tile_expert[offsets[e] // block_m:offsets[e + 1] // block_m] = e
+    return (counts.astype(np.int32), offsets.astype(np.int32), sorted_ids.astype(np.int32),
+            tile_expert.astype(np.int32), num_tiles)
+
+
+# ============================================================================ quantizers
+def quantize_fp8_block(v: np.ndarray, block_rows: int, block_cols: int = 128):
+    """FP8 E4M3 with one fp32 scale per block_rows x block_cols block.
+
+    [TS70] Design: FP8 E4M3 inputs and weights with FP32 per-128-element
+    scales. Activations use 1x128 blocks, weights 128x128 blocks.
+    Per block: amax = max|v|; s = RN_fp32(amax / 448), s = 1 when amax = 0;
+    code = E4M3_RN_SAT(RN_fp32(v / s)).
+    v: float64 values [R, C] with R % block_rows == 0 and C % block_cols == 0.
+    Returns codes uint8 [R, C], scales fp32 [R / block_rows, C / block_cols].
+    """
+    v = np.asarray(v, dtype=np.float64)
+    R, C = v.shape
+    if R % block_rows or C % block_cols:
+        raise ValueError("quantize_fp8_block: shape not a multiple of the block")
+    blocks = v.reshape(R // block_rows, block_rows, C // block_cols, block_cols)
+    amax = np.abs(blocks).max(axis=(1, 3))
+    s = F.round_fp32(amax / F.E4M3_MAX)
+    s = np.where(amax == 0, 1.0, s)
+    q = F.round_fp32(blocks / s[:, None, :, None])
+    codes = F.e4m3_encode(q).reshape(R, C)
+    return codes, s.astype(np.float32)
+
+
+def dequantize_fp8_block(codes, scales, block_rows: int, block_cols: int = 128) -> np.ndarray:
+    vals = F.e4m3_decode(codes)
+    s = np.repeat(np.repeat(np.asarray(scales, np.float64), block_rows, axis=0), block_cols, axis=1)
+    return vals * s
+
+
+def _mx_shared_exponent(blocks: np.ndarray, emax_elem: int) -> np.ndarray:
+    """OCP MX v1.0: X = 2^(floor(log2 amax) - emax_elem), exponent clamped to [-127, 127].
+
+    Returns the E8M0 byte (exponent + 127); an all-zero block gives byte 0.
+    """
+    amax = np.abs(blocks).max(axis=-1)
+    e = np.where(amax > 0, np.frexp(np.where(amax > 0, amax, 1.0))[1].astype(np.int64) - 1, -127)
+    x = np.where(amax > 0, np.clip(e - emax_elem, -127, 127), -127)
+    return (x + 127).astype(np.uint8)
+
+
+def quantize_mxfp8(v: np.ndarray):
+    """MXFP8 along the last axis: E4M3 elements, one E8M0 scale per 32.
+
+    [FI6465] Benchmark configuration: FP8 activations against MXFP4 K32
+    weights; the activations take the same 1x32 E8M0 block form (reading:
+    the MX block-scaled matrix op takes E8M0 scales on both operands, as in
+    [GCMOE] Abstract). Rule: OCP MX v1.0 (floor of log2 amax, emax_elem = 8).
+    v: [R, C], C % 32 == 0. Returns codes uint8 [R, C], e8m0 uint8 [R, C/32].
+    """
+    v = np.asarray(v, dtype=np.float64)
+    R, C = v.shape
+    if C % 32:
+        raise ValueError("quantize_mxfp8: columns must be a multiple of 32")
+    blocks = v.reshape(R, C // 32, 32)
+    sb = _mx_shared_exponent(blocks, 8)
+    x = np.ldexp(1.0, sb.astype(np.int64) - 127)
+    codes = F.e4m3_encode(blocks / x[..., None]).reshape(R, C)   # division by 2^n is exact
+    return codes, sb
+
+
+def quantize_mxfp4(v: np.ndarray):
+    """MXFP4 along the last axis: E2M1 elements, one E8M0 scale per 32.
+
+    [FI6465] Benchmark configuration: MXFP4 weights with K32 scaling.
+    Rule: OCP MX v1.0 (emax_elem = 2). Two codes per byte, even column in the
+    low nibble. v: [R, C], C % 32 == 0.
+    Returns packed uint8 [R, C/2], e8m0 uint8 [R, C/32].
+    """
+    v = np.asarray(v, dtype=np.float64)
+    R, C = v.shape
+    if C % 32:
+        raise ValueError("quantize_mxfp4: columns must be a multiple of 32")
+    blocks = v.reshape(R, C // 32, 32)
+    sb = _mx_shared_exponent(blocks, 2)
+    x = np.ldexp(1.0, sb.astype(np.int64) - 127)
+    codes = F.e2m1_encode(blocks / x[..., None]).reshape(R, C)
+    return F.pack_e2m1(codes), sb
+
+
+def dequantize_mxfp8(codes, e8m0) -> np.ndarray:
+    vals = F.e4m3_decode(codes)
+    return vals * np.repeat(F.e8m0_decode(e8m0), 32, axis=-1)
+
+
+def dequantize_mxfp4(packed, e8m0) -> np.ndarray:
+    vals = F.e2m1_decode(F.unpack_e2m1(packed))
+    return vals * np.repeat(F.e8m0_decode(e8m0), 32, axis=-1)
+
+
+# ============================================================================ expert MLP
+def silu(g: np.ndarray) -> np.ndarray:
+    return g / (1.0 + np.exp(-g))
+
+
+def _store_h(h: np.ndarray, dtype: int):
+    """Storage point of the intermediate (reading listed in the module docstring).
+
+    Returns (stored representation, its float64 value)."""
+    if dtype == DTYPE_BF16:
+        hb = F.round_bf16(h)
+        return (hb, None), hb
+    if dtype == DTYPE_FP8_BLOCK128:
+        codes, s = quantize_fp8_block(h, 1, 128)
+        return (codes, s), dequantize_fp8_block(codes, s, 1, 128)
+    if dtype == DTYPE_MXFP4W_MXFP8A:
+        codes, sb = quantize_mxfp8(h)
+        return (codes, sb), dequantize_mxfp8(codes, sb)
+    raise ValueError("unknown dtype")
+
+
+def grouped_gemm_swiglu(x_hat: np.ndarray, w1_hat: np.ndarray, sorted_ids: np.ndarray,
+                        tile_expert: np.ndarray, num_tiles: int, block_m: int, k: int,
+                        dtype: int):
+    """GEMM1 + SwiGLU over the sorted rows, then the h storage point.
+
+    [TS70] Design, Kernel 1 (L1 GEMM + SwiGLU, quantised intermediate);
+    [FI5129] Description (GEMM1 writes padded expert-sorted rows).
+    x_hat [T, H] and w1_hat [E, 2I, H] are the (dequantised) float64 operands.
+    Sorted row r (r < num_tiles * block_m) holding assignment a < T*k reads
+    token a // k; pad rows read a zero row, so their h is 0.
+    Returns (stored h, float64 value of stored h), both with num_tiles*block_m rows.
+    """
+    E, twoI, H = w1_hat.shape
+    I = twoI // 2
+    A = x_hat.shape[0] * k
+    rows = num_tiles * block_m
+    h = np.zeros((rows, I), dtype=np.float64)
+    for tile in range(num_tiles):
+        e = int(tile_expert[tile])
+        r0 = tile * block_m
+        a = sorted_ids[r0:r0 + block_m].astype(np.int64)
+        valid = a < A
+        xa = np.zeros((block_m, H), dtype=np.float64)
+        xa[valid] = x_hat[a[valid] // k]
+        g = xa @ w1_hat[e, :I].T
+        u = xa @ w1_hat[e, I:].T
+        h[r0:r0 + block_m] = silu(g) * u
+    return _store_h(h, dtype)
+
+
+def grouped_gemm_down(h_val: np.ndarray, w2_hat: np.ndarray, sorted_ids: np.ndarray,
+                      tile_expert: np.ndarray, num_tiles: int, block_m: int, A: int):
+    """GEMM2 over the sorted rows; each real row lands in assignment order.
+
+    [FI5129] Description: GEMM2 reads A contiguously from the sorted rows and
+    its epilogue scatters to assignment order; pad rows are dropped.
+    [TS70] Design, Kernel 2: rows land per (token, top-k slot).
+    h_val [rows, I] float64, w2_hat [E, H, I]. Returns Y float64 (bf16
+    values) [A, H].
+    """
+    E, H, I = w2_hat.shape
+    y = np.zeros((A, H), dtype=np.float64)
+    for tile in range(num_tiles):
+        e = int(tile_expert[tile])
+        r0 = tile * block_m
+        a = sorted_ids[r0:r0 + block_m].astype(np.int64)
+        valid = a < A
+        yt = h_val[r0:r0 + block_m] @ w2_hat[e].T
+        y[a[valid]] = F.round_bf16(yt[valid])
+    return y
+
+
+def combine(y: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """out[t] = bf16( sum_j w[t, j] * Y[t*k + j] ), summed in float64.
+
+    [TS70] review thread "reduce tail" (the reduce over top-k slots to a BF16
+    output) and [FI5129] Description (the combine follows GEMM2 unchanged).
+    """
+    T, k = w.shape
+    H = y.shape[1]
+    acc = np.zeros((T, H), dtype=np.float64)
+    for j in range(k):
+        acc += np.asarray(w[:, j], np.float64)[:, None] * y[j::k]
+    return F.round_bf16(acc)
+
+
+# ============================================================================ whole forward
+def moe_forward(logits, x_bf16, w1_bf16, w2_bf16, k: int, score: int, dtype: int,
+                block_m: int = 16, w1_q=None, w2_q=None):
+    """The whole routed forward for one batch.
+
+    x_bf16 [T, H], w1_bf16 [E, 2I, H], w2_bf16 [E, H, I]: float64 arrays of
+    bf16 values. For the FP8 path x is quantised 1x128 and the weights
+    128x128 (w1_q / w2_q may pass precomputed (codes, scales)); for the MX
+    path x is MXFP8 1x32 and the weights MXFP4 1x32 along K.
+    Returns a dict of every intermediate.
+    """
+    x_bf16 = np.asarray(x_bf16, np.float64)
+    T, H = x_bf16.shape
+    E, twoI, _ = w1_bf16.shape
+    I = twoI // 2
+    ids, w = route(logits, k, score)
+    counts, offsets, sorted_ids, tile_expert, num_tiles = align_sort(ids, E, block_m)
+    out = {"ids": ids, "w": w, "counts": counts, "offsets": offsets,
+           "sorted_ids": sorted_ids, "tile_expert": tile_expert, "num_tiles": num_tiles}
+    if dtype == DTYPE_BF16:
+        x_hat = x_bf16
+        w1_hat = np.asarray(w1_bf16, np.float64)
+        w2_hat = np.asarray(w2_bf16, np.float64)
+    elif dtype == DTYPE_FP8_BLOCK128:
+        xq, xs = quantize_fp8_block(x_bf16, 1, 128)
+        x_hat = dequantize_fp8_block(xq, xs, 1, 128)
+        if w1_q is None:
+            w1_q = quantize_fp8_block(np.asarray(w1_bf16).reshape(E * twoI, H), 128, 128)
+        if w2_q is None:
+            w2_q = quantize_fp8_block(np.asarray(w2_bf16).reshape(E * H, I), 128, 128)
+        w1_hat = dequantize_fp8_block(*w1_q, 128, 128).reshape(E, twoI, H)
+        w2_hat = dequantize_fp8_block(*w2_q, 128, 128).reshape(E, H, I)
+        out.update(xq=xq, xs=xs)
+    elif dtype == DTYPE_MXFP4W_MXFP8A:
+        xq, xs = quantize_mxfp8(x_bf16)
+        x_hat = dequantize_mxfp8(xq, xs)
+        if w1_q is None:
+            w1_q = quantize_mxfp4(np.asarray(w1_bf16).reshape(E * twoI, H))
+        if w2_q is None:
+            w2_q = quantize_mxfp4(np.asarray(w2_bf16).reshape(E * H, I))
+        w1_hat = dequantize_mxfp4(*w1_q).reshape(E, twoI, H)
+        w2_hat = dequantize_mxfp4(*w2_q).reshape(E, H, I)
+        out.update(xq=xq, xs=xs)
+    else:
+        raise ValueError("unknown dtype")
+    (h_store, h_val) = grouped_gemm_swiglu(x_hat, w1_hat, sorted_ids, tile_expert, num_tiles,
+                                           block_m, k, dtype)
+    y = grouped_gemm_down(h_val, w2_hat, sorted_ids, tile_expert, num_tiles, block_m, T * k)
+    out.update(h=h_store, h_val=h_val, y=y, out=combine(y, w))
+    return out
+
+
+def routed_flops(T: int, k: int, H: int, I: int) -> int:
+    """Routed FLOPs of one forward: the two grouped GEMMs, 6*T*k*H*I.
+
+    [LIG] MoEBenchmark results: shared experts and attention are not counted;
+    the router projection, SwiGLU and combine are not GEMM work either.
+    """
+    return 6 * T * k * H * I
+
+
+def token_forward(x_row, w1_hat, w2_hat, ids_row, w_row, dtype: int = DTYPE_BF16):
+    """One token's output computed on its own (used for sampled checks at
+    full size: same arithmetic as moe_forward restricted to one token).
+
+    x_row [H] dequantised input, ids_row/w_row [k]. Returns float64 bf16 values [H].
+    """
+    e0 = int(ids_row[0])
+    I = np.asarray(w1_hat[e0]).shape[0] // 2
+    acc = np.zeros(np.asarray(w2_hat[e0]).shape[0], dtype=np.float64)
+    for j, e in enumerate(ids_row):
+        w1e = np.asarray(w1_hat[e], np.float64)      # array [E,...] or a dict of experts
+        g = w1e[:I] @ x_row
+        u = w1e[I:] @ x_row
+        _, hv = _store_h((silu(g) * u)[None, :], dtype)
+        y = F.round_bf16(np.asarray(w2_hat[e], np.float64) @ hv[0])
+        acc += float(w_row[j]) * y
+    return F.round_bf16(acc)
+
+
+__all__ = [n for n in dir() if not n.startswith("_") and n not in ("math", "np", "F")]
