@@ -1,0 +1,208 @@
+"""Routed MoE-MLP forward throughput on one MI355X.
+
+A step is one whole forward over one batch of synthetic input, with every
+step of the path on the GPU: route -> align_sort -> [quantise x] ->
+GEMM1 + SwiGLU -> GEMM2 -> combine. Throughput is the routed GEMM FLOPs
+(6 * T * k * H * I per step) over the measured time. Inputs and prepared
+weights are resident in HBM before the timed region starts.
+
+Prints one JSON line. Default workload: the Qwen3-30B-A3B-shaped BF16 MoE at
+T=8192 tokens (H=2048, 128 experts, top-8, I=768), uniform routing.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {0: 2500.0, 1: 5000.0, 2: 5000.0}      # MI355X dense MFMA: bf16, fp8, fp8 (MX f8f6f4 at fp8 rate)
+PEAK_FP4_TFLOPS = 10100.0
+PEAK_HBM_GBS = 8000.0
+DTYPE_NAME = {0: "bf16", 1: "fp8_e4m3 (128-block scales)", 2: "mxfp4 weights x mxfp8 activations"}
+# The pages' own 1-GPU forward figure for this workload (other hardware, context only):
+# Liger-Kernel PR #1463, MoEBenchmark results, H200, Qwen3-30B-A3B, T=8192, BF16 forward.
+PAGE_BASELINE = {"qwen3_30b_a3b_bf16": (354.38, "H200 1-GPU BF16 forward, Liger-Kernel PR #1463 MoEBenchmark"),
+                 "llama4_scout_bf16": (511.36, "H200 1-GPU BF16 forward, Liger-Kernel PR #1463 MoEBenchmark")}
+STAGES = ["route", "align_sort", "quantize_x", "gemm1_swiglu", "gemm2_down", "combine"]
+KERNEL_SRC = {"gemm1_swiglu": {0: "gemm_bf16.hip", 1: "gemm_fp8.hip", 2: "gemm_mx.hip"},
+              "gemm2_down": {0: "gemm_bf16.hip", 1: "gemm_fp8.hip", 2: "gemm_mx.hip"}}
+
+
+def _src_hash(fname: str) -> str:
+    path = os.path.join(ROOT, "mixture_experts_routed_top_amd", "csrc", fname)
+    h = hashlib.sha256()
+    for f in (path, os.path.join(os.path.dirname(path), "moe_common.cuh")):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(workload: str, kernel: str, dtype: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("src_hash") != _src_hash(KERNEL_SRC[kernel][dtype]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, inp, budget_s: float = 15.0):
+    """The oracle as it stands, timed on this host on a bounded prefix of the
+    same batch (same weights, the first T' tokens), scaled to TFLOP/s."""
+    import numpy as np
+    from oracle import moe as O
+    from workloads import to_f64
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    w1 = to_f64(inp.w1)
+    w2 = to_f64(inp.w2)
+
+    def run(t):
+        logits = inp.logits[:t].numpy()
+        x = to_f64(inp.x[:t])
+        t0 = time.perf_counter()
+        O.moe_forward(logits, x, w1, w2, cfg.k, cfg.score, cfg.dtype, block_m=16)
+        return time.perf_counter() - t0
+
+    # grow the token prefix until one oracle run takes about budget_s
+    t_sample = min(cfg.T, 64)
+    dt = run(t_sample)
+    while dt < 0.5 * budget_s and t_sample < cfg.T:
+        t_sample = int(min(cfg.T, max(t_sample + 1, t_sample * budget_s / max(dt, 1e-3))))
+        dt = run(t_sample)
+    flops = 6 * t_sample * cfg.k * cfg.H * cfg.I
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 numpy oracle on the first {t_sample} of {cfg.T} tokens of the same batch "
+                      f"(same weights), {dt:.2f} s"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3_30b_a3b_bf16")
+    ap.add_argument("--tokens", type=int, default=None, help="override T (parity-size runs)")
+    ap.add_argument("--block-m", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args(argv)
+
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the routed forward here is the "
+              "single-GPU path and has no multi-GPU mode.", file=sys.stderr)
+        return 2
+
+    import torch
+    import mixture_experts_routed_top_amd as M
+    from workloads import get_config, make_inputs
+
+    cfg = get_config(a.workload)
+    if a.tokens:
+        cfg = cfg.with_(T=a.tokens)
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    inp = make_inputs(cfg)
+    layer = M.MoeLayer(cfg.dtype, inp.w1.to(dev), inp.w2.to(dev), cfg.k, cfg.score)
+    x, logits = inp.x.to(dev), inp.logits.to(dev)
+    plan = layer.plan(cfg.T, block_m=a.block_m)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    stage_fns = _stage_fns(layer, plan, x, logits)
+    for _ in range(a.warmup):
+        for _, f in stage_fns:
+            f()
+    torch.cuda.synchronize()
+
+    # timed region: K whole forwards; events on the launch stream bracket each stage
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stage_fns) + 1)] for _ in range(a.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for s in range(a.steps):
+        ev[s][0].record(stream)
+        for i, (_, f) in enumerate(stage_fns):
+            f()
+            ev[s][i + 1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end) / a.steps
+
+    stage_us = {}
+    for i, (name, _) in enumerate(stage_fns):
+        stage_us[name] = round(1000.0 * sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(a.steps)) / a.steps, 2)
+    flops = cfg.flops
+    value = flops / (ms / 1e3) / 1e12
+
+    # roofline of the dominant kernel (largest average duration)
+    dom = max(("gemm1_swiglu", "gemm2_down"), key=lambda n: stage_us[n])
+    dom_flops = (4 if dom == "gemm1_swiglu" else 2) * cfg.T * cfg.k * cfg.H * cfg.I
+    achieved = dom_flops / (stage_us[dom] * 1e-6) / 1e12
+    peak = PEAK_TFLOPS[cfg.dtype]
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": _traffic(cfg.name, dom, cfg.dtype),
+                "avg_launch_us": stage_us[dom],
+                "algorithmic": f"{4 if dom == 'gemm1_swiglu' else 2}*T*k*H*I = {dom_flops} FLOP per launch"}
+
+    base = PAGE_BASELINE.get(cfg.name) if not a.tokens else None
+    rec = {
+        "metric": "routed MoE-MLP forward TFLOP/s on 1 MI355X (+% of dtype MFMA peak)",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": round(value / base[0], 4) if base else None,
+        "baseline_ref": f"{base[0]} TFLOP/s, {base[1]} (other hardware, context only)" if base else None,
+        "dtype": "bf16" if cfg.dtype == 0 else ("fp8" if cfg.dtype == 1 else "mxfp4xmxfp8"),
+        "data": "synthetic (seeded N(0,1) tokens, N(0,sigma) bf16 weights, router logits x.Wr)",
+        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k, "I": cfg.I,
+                   "routing": cfg.routing, "score": "softmax" if cfg.score == 0 else "sigmoid",
+                   "numeric_path": DTYPE_NAME[cfg.dtype], "block_m": plan.block_m, "parallelism": "none (1 GPU)"},
+        "pct_of_dtype_peak": round(100 * value / peak, 2),
+        "stages_us": stage_us,
+        "wall_s_timed": round(wall, 4),
+        "roofline": roofline,
+    }
+    if cfg.dtype == 2:
+        rec["pct_of_fp4_peak"] = round(100 * value / PEAK_FP4_TFLOPS, 2)
+    if not a.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(cfg, inp)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def _stage_fns(layer, plan, x, logits):
+    import mixture_experts_routed_top_amd as M
+    d = layer.dtype
+    fns = [("route", lambda: M.moe_route(logits, layer.k, layer.score, plan.ids, plan.w)),
+           ("align_sort", lambda: M.moe_align_sort(plan.ids, layer.E, plan.block_m, out=plan.sort))]
+    if d == M.DTYPE_FP8_BLOCK128:
+        fns.append(("quantize_x", lambda: M.moe_quantize_fp8(x, 1, plan.xq, plan.xs)))
+        a, a_s = plan.xq, plan.xs
+    elif d == M.DTYPE_MXFP4W_MXFP8A:
+        fns.append(("quantize_x", lambda: M.moe_quantize_mxfp8(x, plan.xq, plan.xs)))
+        a, a_s = plan.xq, plan.xs
+    else:
+        a, a_s = x, None
+    fns.append(("gemm1_swiglu", lambda: M.moe_grouped_gemm_swiglu(d, a, a_s, layer.w1, layer.w1_scale, plan.sort,
+                                                                    layer.H, layer.I, plan.h, plan.h_scale)))
+    fns.append(("gemm2_down", lambda: M.moe_grouped_gemm_down(d, plan.h, plan.h_scale, layer.w2, layer.w2_scale,
+                                                                plan.sort, layer.H, layer.I, plan.y)))
+    fns.append(("combine", lambda: M.moe_combine(plan.y, plan.w, plan.out)))
+    return fns
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,271 @@
+/*
+ * moe_mi355x.h -- C ABI of the routed-expert MoE MLP forward for MI355X (gfx950).
+ *
+ * The forward of a routed-expert MoE MLP layer, split into the calls below and
+ * run on one GPU:
+ *
+ *   moe_route -> moe_align_sort -> [moe_quantize_fp8 | moe_quantize_mxfp8 (x)]
+ *     -> moe_grouped_gemm_swiglu -> moe_grouped_gemm_down -> moe_combine
+ *
+ * What is computed follows the pages that describe the method:
+ *   - TileScale PR #70 "SM90 FP8 distributed MegaMoE example", Design section:
+ *     routing, GEMM1 (gate/up) + SwiGLU with a quantised intermediate, GEMM2,
+ *     rows written per (token, top-k slot), reduce over the slots to BF16;
+ *     FP8 E4M3 inputs and weights with FP32 per-128 scales.
+ *   - FlashInfer PR #5129 (expert-sorted I/O for the cuTile BF16 MoE),
+ *     Description: GEMM1 writes into padded expert-sorted rows, GEMM2 reads
+ *     them contiguously and scatters back to assignment order, the combine is
+ *     unchanged; padded rows feed only dropped output rows.
+ *   - FlashInfer PR #6465 (Hopper MXFP4 x FP8 MegaMoE tuning), Benchmark
+ *     configuration: MXFP4 weights with K32 scaling, FP8 activations, BF16 I/O.
+ *   - Liger-Kernel PR #1463, Summary: empty experts or K slices must not stall
+ *     the schedule (empty experts own no tiles here).
+ *
+ * Conventions common to every call
+ *   - All tensors are dense, row-major, the reduction dimension (K) contiguous.
+ *     Weights use the [out, in] convention: W1 is [E, 2I, H] with gate rows
+ *     [0, I) and up rows [I, 2I) of each expert; W2 is [E, H, I].
+ *   - bf16 tensors are passed as uint16_t bit patterns.
+ *   - Assignment a = t * k + j is slot j of token t. A = T * k.
+ *   - Device pointers: every pointer argument except those documented as host
+ *     is a device pointer owned by the caller. The library never allocates or
+ *     frees device memory and never synchronises the stream.
+ *   - stream: a hipStream_t passed as void* (NULL = the default stream). All
+ *     work of a call is enqueued on it; ordering between calls is the caller's.
+ *   - Errors: every argument check runs on the host before anything is
+ *     enqueued; a rejected call enqueues nothing. A call with T == 0 (or
+ *     rows == 0) returns MOE_OK and enqueues nothing. Faults inside kernels
+ *     surface at the caller's next synchronisation, not as a return value.
+ *   - Calls are reentrant; the library keeps no mutable state beyond a cached
+ *     per-device property record (architecture check and CU count).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status_t;
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG 1       /* null / misaligned pointer, bad size, k > E, bad block_m */
+#define MOE_ERR_UNSUPPORTED_SHAPE 2 /* shape outside what the dtype's kernels support */
+#define MOE_ERR_WORKSPACE 3         /* workspace too small */
+#define MOE_ERR_DEVICE 4            /* no gfx950 device current, or a launch failed */
+
+/* Numeric path of the grouped GEMMs. */
+#define MOE_DTYPE_BF16 0            /* bf16 x, W; fp32 accumulate; bf16 h */
+#define MOE_DTYPE_FP8_BLOCK128 1    /* E4M3 x (1x128 fp32 scales), E4M3 W (128x128 fp32 scales); E4M3 h (1x128) */
+#define MOE_DTYPE_MXFP4W_MXFP8A 2   /* E4M3 x + E8M0/32, E2M1 W + E8M0/32 along K; E4M3 h + E8M0/32 */
+
+/* Router score function. */
+#define MOE_SCORE_SOFTMAX 0         /* softmax over the k selected logits (top-k renormalised) */
+#define MOE_SCORE_SIGMOID 1         /* sigmoid(logit) of each selected expert, not renormalised */
+
+/* Limits of this build. */
+#define MOE_MAX_EXPERTS 1024
+#define MOE_MAX_TOPK 32
+
+/*
+ * moe_route -- top-k selection and gate weights per token.
+ * TileScale PR #70, Design ("Kernel 1": routing happens before dispatch);
+ * the weights are the softmax over the selected logits, which equals a
+ * softmax over all experts renormalised over the top k.
+ *
+ *   logits   [T, E] fp32, device.
+ *   topk_ids [T, k] int32, device, out: the k largest logits in descending
+ *            order; equal logits -> the lower expert index first.
+ *   topk_w   [T, k] fp32, device, out: SOFTMAX: exp(l_j - l_0) / sum_i exp(l_i - l_0);
+ *            SIGMOID: 1 / (1 + exp(-l_j)).
+ * Requires 1 <= E <= MOE_MAX_EXPERTS, 1 <= k <= min(E, MOE_MAX_TOPK), T >= 0,
+ * finite logits. Errors: MOE_ERR_INVALID_ARG, MOE_ERR_DEVICE.
+ */
+moe_status_t moe_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t score,
+                       int32_t* topk_ids, float* topk_w, void* stream);
+
+/*
+ * moe_pick_block_m -- host only. The tile height (rows per tile of the
+ * expert-sorted layout) this library's kernels use for a problem, from the
+ * mean number of rows per expert (the adaptive token-tile geometry named in
+ * the Abstract of "GC-MoE on SM120"). Returns a value in {16, 32, 64, 128,
+ * 256}, or -1 for invalid arguments.
+ */
+int32_t moe_pick_block_m(int32_t dtype, int64_t T, int32_t k, int32_t E, int32_t H, int32_t I);
+
+/*
+ * moe_sorted_capacity -- host only. Rows to allocate for the padded sorted
+ * layout: ceil((A + min(E, A) * (block_m - 1)) / block_m) * block_m, an upper
+ * bound on the padded row count whatever the routing. Returns -1 for invalid
+ * arguments.
+ */
+int64_t moe_sorted_capacity(int64_t T, int32_t k, int32_t E, int32_t block_m);
+
+/*
+ * moe_align_sort_workspace_bytes -- host only. Device workspace bytes
+ * moe_align_sort needs (0 when T == 0). Returns 0 for invalid arguments.
+ */
+size_t moe_align_sort_workspace_bytes(int64_t T, int32_t k, int32_t E);
+
+/*
+ * moe_align_sort -- expert-sorted, tile-padded permutation of the assignments
+ * and the flat tile queue.
+ * FlashInfer PR #5129, Description (padded expert-sorted rows); TileScale
+ * PR #70, first commit note in the conversation (a flat m-task queue replaces
+ * the per-tile expert rescan); Liger-Kernel PR #1463, Summary (empty experts).
+ *
+ *   topk_ids    [T, k] int32, device, values in [0, E).
+ *   counts      [E] int32, out: rows routed to each expert.
+ *   offsets     [E + 1] int32, out: exclusive prefix sum of the padded counts
+ *               ceil(counts[e] / block_m) * block_m; offsets[E] = padded rows.
+ *   sorted_ids  [cap] int32, out, cap = moe_sorted_capacity(T, k, E, block_m):
+ *               rows offsets[e] .. offsets[e] + counts[e] - 1 hold the
+ *               assignments routed to expert e in increasing a; every other
+ *               entry (padding, and the tail past offsets[E]) holds A.
+ *   tile_expert [cap / block_m] int32, out: expert of tile i (rows
+ *               [i * block_m, (i + 1) * block_m)), -1 for i >= num_tiles.
+ *   num_tiles   [1] int32, out (device): offsets[E] / block_m.
+ *   ws          device workspace of at least
+ *               moe_align_sort_workspace_bytes(T, k, E) bytes (contents
+ *               undefined on entry and exit).
+ * The result is deterministic (no dependence on atomic ordering).
+ * Errors: MOE_ERR_INVALID_ARG (block_m not in {16, 32, 64, 128, 256}),
+ * MOE_ERR_WORKSPACE, MOE_ERR_DEVICE. Expert ids outside [0, E) are not
+ * detected on the device: the caller guarantees them (moe_route does).
+ */
+moe_status_t moe_align_sort(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, int32_t block_m,
+                            int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
+                            int32_t* tile_expert, int32_t* num_tiles,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_quantize_fp8 -- bf16 -> FP8 E4M3 (OCP "E4M3FN", max 448) with one fp32
+ * scale per block_rows x 128 block. TileScale PR #70, Design (FP8 E4M3 with
+ * FP32 per-128 scales). Per block: amax = max|v|; s = fp32(amax / 448)
+ * (correctly rounded), s = 1 when amax = 0; code = E4M3_RN(clamp(fp32(v / s),
+ * -448, 448)), ties to even, sign of zero kept.
+ *
+ *   in    [rows, cols] bf16, device.
+ *   q     [rows, cols] uint8 codes, out.
+ *   scale [rows / block_rows, cols / 128] fp32, out.
+ * block_rows is 1 (activations) or 128 (weights); rows % block_rows == 0 and
+ * cols % 128 == 0, else MOE_ERR_UNSUPPORTED_SHAPE.
+ */
+moe_status_t moe_quantize_fp8(const uint16_t* in, int64_t rows, int64_t cols, int32_t block_rows,
+                              uint8_t* q, float* scale, void* stream);
+
+/*
+ * moe_quantize_mxfp8 -- bf16 -> MXFP8 along each row: E4M3 codes with one
+ * E8M0 scale per 32 consecutive columns (OCP MX v1.0 rule: X = 2^(floor(log2
+ * amax) - 8), exponent clamped to [-127, 127]; byte = exponent + 127; an
+ * all-zero block gets byte 0; code = E4M3_RN_SAT(v / X)). FlashInfer PR
+ * #6465, Benchmark configuration (FP8 activations against K32-scaled MXFP4).
+ *
+ *   in [rows, cols] bf16; q [rows, cols] uint8; e8m0 [rows, cols / 32] uint8.
+ * cols % 32 == 0, else MOE_ERR_UNSUPPORTED_SHAPE.
+ */
+moe_status_t moe_quantize_mxfp8(const uint16_t* in, int64_t rows, int64_t cols,
+                                uint8_t* q, uint8_t* e8m0, void* stream);
+
+/*
+ * moe_quantize_mxfp4 -- bf16 -> MXFP4 along each row: E2M1 codes (values
+ * 0, 0.5, 1, 1.5, 2, 3, 4, 6), one E8M0 scale per 32 columns (OCP MX v1.0,
+ * X = 2^(floor(log2 amax) - 2)); RN ties to even, saturating at 6. FlashInfer
+ * PR #6465, Benchmark configuration (MXFP4 weights with K32 scaling).
+ *
+ *   in [rows, cols] bf16; q [rows, cols / 2] uint8, two codes per byte, the
+ *   even column in the low nibble; e8m0 [rows, cols / 32] uint8.
+ * cols % 32 == 0, else MOE_ERR_UNSUPPORTED_SHAPE.
+ */
+moe_status_t moe_quantize_mxfp4(const uint16_t* in, int64_t rows, int64_t cols,
+                                uint8_t* q, uint8_t* e8m0, void* stream);
+
+/*
+ * moe_grouped_gemm_swiglu -- GEMM1 (gate and up projections) of every routed
+ * row and the SwiGLU, written into the padded expert-sorted row space.
+ * TileScale PR #70, Design ("Kernel 1": L1 GEMM + SwiGLU, quantised
+ * intermediate); FlashInfer PR #5129, Description (GEMM1 scatters into the
+ * padded sorted rows).
+ *
+ * For each sorted row r < num_tiles * block_m with a = sorted_ids[r]:
+ *   e = tile_expert[r / block_m]; x_row = x[a / k] if a < A else 0;
+ *   g_n = x_row . W1[e, n, :], u_n = x_row . W1[e, I + n, :]  (fp32 accumulate)
+ *   h[r, n] = silu(g_n) * u_n, stored per dtype:
+ *     BF16:           h [cap, I] bf16 (RN); h_scale unused (may be NULL).
+ *     FP8_BLOCK128:   h [cap, I] E4M3 codes; h_scale [cap, I / 128] fp32 (the
+ *                     moe_quantize_fp8 rule, 1 x 128, applied to the fp32 h).
+ *     MXFP4W_MXFP8A:  h [cap, I] E4M3 codes; h_scale [cap, I / 32] E8M0 (the
+ *                     moe_quantize_mxfp8 rule applied to the fp32 h).
+ *   Pad rows are written too (their h is 0). Rows past num_tiles * block_m are
+ *   not touched.
+ * Operands per dtype:
+ *   BF16:          x [T, H] bf16; W1 [E, 2I, H] bf16; scales unused.
+ *   FP8_BLOCK128:  x [T, H] E4M3 + x_scale [T, H / 128] fp32;
+ *                  W1 [E*2I, H] E4M3 + w1_scale [E*2I/128, H/128] fp32.
+ *   MXFP4W_MXFP8A: x [T, H] E4M3 + x_scale [T, H / 32] E8M0;
+ *                  W1 [E*2I, H/2] packed E2M1 + w1_scale [E*2I, H/32] E8M0.
+ * sorted_ids / tile_expert / num_tiles come from moe_align_sort with the same
+ * T, k, E, block_m; cap = moe_sorted_capacity(T, k, E, block_m).
+ * Shapes: BF16 needs H % 8 == 0 and I % 8 == 0; FP8 needs H % 128 == 0 and
+ * I % 128 == 0; MX needs H % 128 == 0 and I % 128 == 0
+ * (else MOE_ERR_UNSUPPORTED_SHAPE). block_m must be one this dtype's kernels
+ * support (moe_pick_block_m returns one), else MOE_ERR_UNSUPPORTED_SHAPE.
+ */
+moe_status_t moe_grouped_gemm_swiglu(int32_t dtype, const void* x, const void* x_scale,
+                                     const void* w1, const void* w1_scale,
+                                     const int32_t* sorted_ids, const int32_t* tile_expert,
+                                     const int32_t* num_tiles,
+                                     int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                                     int32_t block_m, int64_t cap,
+                                     void* h, void* h_scale, void* stream);
+
+/*
+ * moe_grouped_gemm_down -- GEMM2 (down projection) over the sorted rows; the
+ * epilogue writes each real row to assignment order and drops pad rows.
+ * FlashInfer PR #5129, Description (GEMM2 loads its A tiles contiguously and
+ * scatters to assignment order); TileScale PR #70, Design ("Kernel 2": rows
+ * land in a (token, top-k slot) workspace).
+ *
+ * For each sorted row r < num_tiles * block_m with a = sorted_ids[r] < A:
+ *   y[a, c] = bf16( sum_i h_hat[r, i] * W2_hat[e, c, i] ), fp32 accumulate,
+ * where h_hat / W2_hat are the dequantised operands:
+ *   BF16:          h [cap, I] bf16; W2 [E, H, I] bf16.
+ *   FP8_BLOCK128:  h [cap, I] E4M3 + h_scale [cap, I/128] fp32;
+ *                  W2 [E*H, I] E4M3 + w2_scale [E*H/128, I/128] fp32.
+ *   MXFP4W_MXFP8A: h [cap, I] E4M3 + h_scale [cap, I/32] E8M0;
+ *                  W2 [E*H, I/2] packed E2M1 + w2_scale [E*H, I/32] E8M0.
+ *   y [A, H] bf16, out: every row a < A is written exactly once.
+ * Shape rules as for moe_grouped_gemm_swiglu.
+ */
+moe_status_t moe_grouped_gemm_down(int32_t dtype, const void* h, const void* h_scale,
+                                   const void* w2, const void* w2_scale,
+                                   const int32_t* sorted_ids, const int32_t* tile_expert,
+                                   const int32_t* num_tiles,
+                                   int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                                   int32_t block_m, int64_t cap,
+                                   uint16_t* y, void* stream);
+
+/*
+ * moe_combine -- top-k weighted sum of each token's expert rows.
+ * TileScale PR #70, review thread on the reduce tail (sum over the top-k
+ * slots into the BF16 output); FlashInfer PR #5129, Description (the combine
+ * after the sorted GEMM2 is unchanged).
+ *
+ *   out[t, c] = bf16( sum_{j = 0..k-1} topk_w[t, j] * y[t*k + j, c] ), summed in
+ *   fp32 in slot order, rounded to nearest even.
+ *   y [T*k, H] bf16; topk_w [T, k] fp32; out [T, H] bf16.
+ * Requires H % 8 == 0 (MOE_ERR_UNSUPPORTED_SHAPE otherwise).
+ */
+moe_status_t moe_combine(const uint16_t* y, const float* topk_w, int64_t T, int32_t k, int32_t H,
+                         uint16_t* out, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* moe_status_string(moe_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,225 @@
+"""ctypes binding of libmoe_mi355x.so (include/moe_mi355x.h).
+
+Argument marshalling only: every step of the routed forward runs in the HIP
+kernels behind the C ABI. torch supplies device memory (tensor.data_ptr())
+and streams (torch.cuda.current_stream().cuda_stream). If the library is not
+built, or no gfx950 GPU is current, every compute call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_mi355x.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = 1
+MOE_ERR_UNSUPPORTED_SHAPE = 2
+MOE_ERR_WORKSPACE = 3
+MOE_ERR_DEVICE = 4
+
+DTYPE_BF16 = 0
+DTYPE_FP8_BLOCK128 = 1
+DTYPE_MXFP4W_MXFP8A = 2
+SCORE_SOFTMAX = 0
+SCORE_SIGMOID = 1
+
+# name -> (restype, argtypes); mirrors include/moe_mi355x.h
+_P, _I32, _I64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+SIGNATURES = {
+    "moe_route": (_I32, [_P, _I64, _I32, _I32, _I32, _P, _P, _P]),
+    "moe_pick_block_m": (_I32, [_I32, _I64, _I32, _I32, _I32, _I32]),
+    "moe_sorted_capacity": (_I64, [_I64, _I32, _I32, _I32]),
+    "moe_align_sort_workspace_bytes": (_SZ, [_I64, _I32, _I32]),
+    "moe_align_sort": (_I32, [_P, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_quantize_fp8": (_I32, [_P, _I64, _I64, _I32, _P, _P, _P]),
+    "moe_quantize_mxfp8": (_I32, [_P, _I64, _I64, _P, _P, _P]),
+    "moe_quantize_mxfp4": (_I32, [_P, _I64, _I64, _P, _P, _P]),
+    "moe_grouped_gemm_swiglu": (_I32, [_I32, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32,
+                                       _I32, _I64, _P, _P, _P]),
+    "moe_grouped_gemm_down": (_I32, [_I32, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32,
+                                     _I32, _I64, _P, _P]),
+    "moe_combine": (_I32, [_P, _P, _I64, _I32, _I32, _P, _P]),
+    "moe_status_string": (ctypes.c_char_p, [_I32]),
+}
+
+_lib = None
+
+
+class MoeError(RuntimeError):
+    def __init__(self, call: str, status: int):
+        super().__init__(f"{call} failed: {moe_status_string(status)} ({status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load the library once; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python mixture_experts_routed_top_amd/build.py`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def moe_status_string(status: int) -> str:
+    return lib().moe_status_string(int(status)).decode()
+
+
+def _check(name: str, status: int) -> None:
+    if status != MOE_OK:
+        raise MoeError(name, status)
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _s(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _need(t: torch.Tensor, dtype, name: str):
+    if not t.is_cuda or t.dtype != dtype or not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous CUDA {dtype} tensor, got {t.dtype} on {t.device}")
+
+
+# ---------------------------------------------------------------- host-only queries
+def moe_pick_block_m(dtype: int, T: int, k: int, E: int, H: int, I: int) -> int:
+    return lib().moe_pick_block_m(dtype, T, k, E, H, I)
+
+
+def moe_sorted_capacity(T: int, k: int, E: int, block_m: int) -> int:
+    return lib().moe_sorted_capacity(T, k, E, block_m)
+
+
+def moe_align_sort_workspace_bytes(T: int, k: int, E: int) -> int:
+    return lib().moe_align_sort_workspace_bytes(T, k, E)
+
+
+# ---------------------------------------------------------------- compute calls
+def moe_route(logits: torch.Tensor, k: int, score: int = SCORE_SOFTMAX, topk_ids=None, topk_w=None,
+              stream=None):
+    _need(logits, torch.float32, "logits")
+    T, E = logits.shape
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _check("moe_route", lib().moe_route(_p(logits), T, E, k, score, _p(topk_ids), _p(topk_w), _s(stream)))
+    return topk_ids, topk_w
+
+
+class SortResult:
+    """Outputs of moe_align_sort (device tensors)."""
+
+    def __init__(self, T, k, E, block_m, device):
+        self.T, self.k, self.E, self.block_m = T, k, E, block_m
+        self.cap = moe_sorted_capacity(T, k, E, block_m)
+        self.counts = torch.empty(E, dtype=torch.int32, device=device)
+        self.offsets = torch.empty(E + 1, dtype=torch.int32, device=device)
+        self.sorted_ids = torch.empty(max(self.cap, 1), dtype=torch.int32, device=device)
+        self.tile_expert = torch.empty(max(self.cap // block_m, 1), dtype=torch.int32, device=device)
+        self.num_tiles = torch.zeros(1, dtype=torch.int32, device=device)
+        nbytes = moe_align_sort_workspace_bytes(T, k, E)
+        self.ws = torch.empty(max(nbytes, 4), dtype=torch.uint8, device=device)
+        self.ws_bytes = nbytes
+
+
+def moe_align_sort(topk_ids: torch.Tensor, E: int, block_m: int, out: Optional[SortResult] = None,
+                   stream=None) -> SortResult:
+    _need(topk_ids, torch.int32, "topk_ids")
+    T, k = topk_ids.shape
+    if out is None:
+        out = SortResult(T, k, E, block_m, topk_ids.device)
+    _check("moe_align_sort", lib().moe_align_sort(
+        _p(topk_ids), T, k, E, block_m, _p(out.counts), _p(out.offsets), _p(out.sorted_ids),
+        _p(out.tile_expert), _p(out.num_tiles), _p(out.ws), out.ws_bytes, _s(stream)))
+    return out
+
+
+def moe_quantize_fp8(x: torch.Tensor, block_rows: int = 1, q=None, scale=None, stream=None):
+    _need(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty((rows // block_rows, cols // 128), dtype=torch.float32, device=x.device)
+    _check("moe_quantize_fp8", lib().moe_quantize_fp8(_p(x), rows, cols, block_rows, _p(q), _p(scale),
+                                                      _s(stream)))
+    return q, scale
+
+
+def moe_quantize_mxfp8(x: torch.Tensor, q=None, e8m0=None, stream=None):
+    _need(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if e8m0 is None:
+        e8m0 = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
+    _check("moe_quantize_mxfp8", lib().moe_quantize_mxfp8(_p(x), rows, cols, _p(q), _p(e8m0), _s(stream)))
+    return q, e8m0
+
+
+def moe_quantize_mxfp4(x: torch.Tensor, q=None, e8m0=None, stream=None):
+    _need(x, torch.bfloat16, "x")
+    rows, cols = x.shape
+    if q is None:
+        q = torch.empty((rows, cols // 2), dtype=torch.uint8, device=x.device)
+    if e8m0 is None:
+        e8m0 = torch.empty((rows, cols // 32), dtype=torch.uint8, device=x.device)
+    _check("moe_quantize_mxfp4", lib().moe_quantize_mxfp4(_p(x), rows, cols, _p(q), _p(e8m0), _s(stream)))
+    return q, e8m0
+
+
+def _h_alloc(dtype, cap, I, device):
+    if dtype == DTYPE_BF16:
+        return torch.empty((cap, I), dtype=torch.bfloat16, device=device), None
+    h = torch.empty((cap, I), dtype=torch.uint8, device=device)
+    if dtype == DTYPE_FP8_BLOCK128:
+        return h, torch.empty((cap, I // 128), dtype=torch.float32, device=device)
+    return h, torch.empty((cap, I // 32), dtype=torch.uint8, device=device)
+
+
+def moe_grouped_gemm_swiglu(dtype: int, x, x_scale, w1, w1_scale, sort: SortResult, H: int, I: int,
+                            h=None, h_scale=None, stream=None):
+    if h is None:
+        h, h_scale = _h_alloc(dtype, max(sort.cap, 1), I, x.device)
+    _check("moe_grouped_gemm_swiglu", lib().moe_grouped_gemm_swiglu(
+        dtype, _p(x), _p(x_scale), _p(w1), _p(w1_scale), _p(sort.sorted_ids), _p(sort.tile_expert),
+        _p(sort.num_tiles), sort.T, H, I, sort.E, sort.k, sort.block_m, sort.cap, _p(h), _p(h_scale),
+        _s(stream)))
+    return h, h_scale
+
+
+def moe_grouped_gemm_down(dtype: int, h, h_scale, w2, w2_scale, sort: SortResult, H: int, I: int, y=None,
+                          stream=None):
+    if y is None:
+        y = torch.empty((max(sort.T * sort.k, 1), H), dtype=torch.bfloat16, device=h.device)
+    _check("moe_grouped_gemm_down", lib().moe_grouped_gemm_down(
+        dtype, _p(h), _p(h_scale), _p(w2), _p(w2_scale), _p(sort.sorted_ids), _p(sort.tile_expert),
+        _p(sort.num_tiles), sort.T, H, I, sort.E, sort.k, sort.block_m, sort.cap, _p(y), _s(stream)))
+    return y
+
+
+def moe_combine(y: torch.Tensor, topk_w: torch.Tensor, out=None, stream=None):
+    _need(y, torch.bfloat16, "y")
+    _need(topk_w, torch.float32, "topk_w")
+    T, k = topk_w.shape
+    H = y.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    _check("moe_combine", lib().moe_combine(_p(y), _p(topk_w), T, k, H, _p(out), _s(stream)))
+    return out

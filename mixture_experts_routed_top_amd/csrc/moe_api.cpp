@@ -1,0 +1,258 @@
+// C ABI front end: argument validation (host only, before anything is
+// enqueued), workspace / capacity queries, tile selection and dispatch to the
+// gfx950 kernels. See include/moe_mi355x.h for the contract of every call.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <mutex>
+
+#include "../../include/moe_mi355x.h"
+#include "moe_launch.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct DevCache {
+  std::once_flag once;
+  bool ok = false;
+  moe::DeviceInfo info{};
+};
+DevCache g_dev[kMaxDevices];
+
+// Architecture check and CU count of the current device, cached per device.
+moe_status_t current_device(moe::DeviceInfo* out) {
+  int d = -1;
+  if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= kMaxDevices) return MOE_ERR_DEVICE;
+  DevCache& c = g_dev[d];
+  std::call_once(c.once, [&c, d] {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, d) != hipSuccess) return;
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return;
+    c.info.num_cus = prop.multiProcessorCount;
+    c.ok = c.info.num_cus > 0;
+  });
+  if (!c.ok) return MOE_ERR_DEVICE;
+  *out = c.info;
+  return MOE_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool valid_block_m(int32_t bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128 || bm == 256; }
+
+bool valid_dtype(int32_t dt) {
+  return dt == MOE_DTYPE_BF16 || dt == MOE_DTYPE_FP8_BLOCK128 || dt == MOE_DTYPE_MXFP4W_MXFP8A;
+}
+
+int64_t capacity(int64_t T, int32_t k, int32_t E, int32_t bm) {
+  const int64_t A = T * k;
+  const int64_t ne = A < E ? A : E;
+  const int64_t bound = A + ne * (bm - 1);
+  return (bound + bm - 1) / bm * bm;
+}
+
+moe_status_t launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
+
+// Shape and pointer checks shared by both grouped GEMMs.
+moe_status_t check_gemm(int32_t dtype, const void* act, const void* act_scale, const void* w,
+                        const void* w_scale, const int32_t* sorted_ids, const int32_t* tile_expert,
+                        const int32_t* num_tiles, int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                        int32_t block_m, int64_t cap, const void* out, const void* out_scale,
+                        bool gemm1) {
+  if (!valid_dtype(dtype)) return MOE_ERR_INVALID_ARG;
+  if (T < 0 || H <= 0 || I <= 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > E || k > MOE_MAX_TOPK)
+    return MOE_ERR_INVALID_ARG;
+  if (!valid_block_m(block_m)) return MOE_ERR_INVALID_ARG;
+  if (T > (int64_t{1} << 31) / k) return MOE_ERR_INVALID_ARG;
+  if (cap != capacity(T, k, E, block_m) || cap >= (int64_t{1} << 31)) return MOE_ERR_INVALID_ARG;
+  switch (dtype) {
+    case MOE_DTYPE_BF16:
+      if (H % 8 || I % 8) return MOE_ERR_UNSUPPORTED_SHAPE;
+      if (!moe::gemm_bf16_supports(block_m)) return MOE_ERR_UNSUPPORTED_SHAPE;
+      break;
+    case MOE_DTYPE_FP8_BLOCK128:
+      if (H % 128 || I % 128) return MOE_ERR_UNSUPPORTED_SHAPE;
+      if (!moe::gemm_fp8_supports(block_m)) return MOE_ERR_UNSUPPORTED_SHAPE;
+      break;
+    default:
+      if (H % 128 || I % 128) return MOE_ERR_UNSUPPORTED_SHAPE;
+      if (!moe::gemm_mx_supports(block_m)) return MOE_ERR_UNSUPPORTED_SHAPE;
+      break;
+  }
+  if (T == 0) return MOE_OK;
+  if (!act || !w || !sorted_ids || !tile_expert || !num_tiles || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned(act, 16) || !aligned(w, 16) || !aligned(out, 16)) return MOE_ERR_INVALID_ARG;
+  if (!aligned(sorted_ids, 4) || !aligned(tile_expert, 4) || !aligned(num_tiles, 4))
+    return MOE_ERR_INVALID_ARG;
+  if (dtype != MOE_DTYPE_BF16) {
+    if (!act_scale || !w_scale) return MOE_ERR_INVALID_ARG;
+    if (!aligned(act_scale, 4) || !aligned(w_scale, 4)) return MOE_ERR_INVALID_ARG;
+    if (gemm1 && (!out_scale || !aligned(out_scale, 4))) return MOE_ERR_INVALID_ARG;
+  }
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED_SHAPE: return "MOE_ERR_UNSUPPORTED_SHAPE";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_DEVICE: return "MOE_ERR_DEVICE";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+moe_status_t moe_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t score,
+                       int32_t* topk_ids, float* topk_w, void* stream) {
+  if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > E || k > MOE_MAX_TOPK)
+    return MOE_ERR_INVALID_ARG;
+  if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if (T > (int64_t{1} << 31) / k) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!logits || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+  if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4)) return MOE_ERR_INVALID_ARG;
+  moe::DeviceInfo dev;
+  if (moe_status_t st = current_device(&dev)) return st;
+  return launched(moe::launch_route(logits, T, E, k, score, topk_ids, topk_w,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+int32_t moe_pick_block_m(int32_t dtype, int64_t T, int32_t k, int32_t E, int32_t H, int32_t I) {
+  if (!valid_dtype(dtype) || T < 0 || k < 1 || E < 1 || k > E || H <= 0 || I <= 0) return -1;
+  const int64_t A = T * k;
+  const int64_t mean = A / E;  // mean rows per expert
+  if (mean >= 256) return 128;
+  if (mean >= 48) return 64;
+  return 32;
+}
+
+int64_t moe_sorted_capacity(int64_t T, int32_t k, int32_t E, int32_t block_m) {
+  if (T < 0 || k < 1 || E < 1 || !valid_block_m(block_m)) return -1;
+  return capacity(T, k, E, block_m);
+}
+
+size_t moe_align_sort_workspace_bytes(int64_t T, int32_t k, int32_t E) {
+  if (T < 0 || k < 1 || E < 1 || E > MOE_MAX_EXPERTS) return 0;
+  return moe::align_sort_ws_bytes(T, k, E);
+}
+
+moe_status_t moe_align_sort(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, int32_t block_m,
+                            int32_t* counts, int32_t* offsets, int32_t* sorted_ids, int32_t* tile_expert,
+                            int32_t* num_tiles, void* ws, size_t ws_bytes, void* stream) {
+  if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > E || k > MOE_MAX_TOPK)
+    return MOE_ERR_INVALID_ARG;
+  if (!valid_block_m(block_m)) return MOE_ERR_INVALID_ARG;
+  if (T > (int64_t{1} << 31) / k) return MOE_ERR_INVALID_ARG;
+  const int64_t cap = capacity(T, k, E, block_m);
+  if (cap >= (int64_t{1} << 31)) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!topk_ids || !counts || !offsets || !sorted_ids || !tile_expert || !num_tiles)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned(topk_ids, 4) || !aligned(counts, 4) || !aligned(offsets, 4) || !aligned(sorted_ids, 4) ||
+      !aligned(tile_expert, 4) || !aligned(num_tiles, 4))
+    return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < moe::align_sort_ws_bytes(T, k, E) || !ws || !aligned(ws, 4)) return MOE_ERR_WORKSPACE;
+  moe::DeviceInfo dev;
+  if (moe_status_t st = current_device(&dev)) return st;
+  return launched(moe::launch_align_sort(topk_ids, T, k, E, block_m, counts, offsets, sorted_ids,
+                                         tile_expert, num_tiles, cap, ws,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_quantize_fp8(const uint16_t* in, int64_t rows, int64_t cols, int32_t block_rows,
+                              uint8_t* q, float* scale, void* stream) {
+  if (rows < 0 || cols < 0 || (block_rows != 1 && block_rows != 128)) return MOE_ERR_INVALID_ARG;
+  if (rows % block_rows || cols % 128) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (rows == 0 || cols == 0) return MOE_OK;
+  if (!in || !q || !scale) return MOE_ERR_INVALID_ARG;
+  if (!aligned(in, 16) || !aligned(q, 8) || !aligned(scale, 4)) return MOE_ERR_INVALID_ARG;
+  moe::DeviceInfo dev;
+  if (moe_status_t st = current_device(&dev)) return st;
+  return launched(moe::launch_quantize_fp8(in, rows, cols, block_rows, q, scale,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_quantize_mxfp8(const uint16_t* in, int64_t rows, int64_t cols, uint8_t* q, uint8_t* e8m0,
+                                void* stream) {
+  if (rows < 0 || cols < 0) return MOE_ERR_INVALID_ARG;
+  if (cols % 32) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (rows == 0 || cols == 0) return MOE_OK;
+  if (!in || !q || !e8m0) return MOE_ERR_INVALID_ARG;
+  if (!aligned(in, 16) || !aligned(q, 8)) return MOE_ERR_INVALID_ARG;
+  moe::DeviceInfo dev;
+  if (moe_status_t st = current_device(&dev)) return st;
+  return launched(moe::launch_quantize_mx(in, rows, cols, false, q, e8m0, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_quantize_mxfp4(const uint16_t* in, int64_t rows, int64_t cols, uint8_t* q, uint8_t* e8m0,
+                                void* stream) {
+  if (rows < 0 || cols < 0) return MOE_ERR_INVALID_ARG;
+  if (cols % 32) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (rows == 0 || cols == 0) return MOE_OK;
+  if (!in || !q || !e8m0) return MOE_ERR_INVALID_ARG;
+  if (!aligned(in, 16) || !aligned(q, 4)) return MOE_ERR_INVALID_ARG;
+  moe::DeviceInfo dev;
+  if (moe_status_t st = current_device(&dev)) return st;
+  return launched(moe::launch_quantize_mx(in, rows, cols, true, q, e8m0, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_grouped_gemm_swiglu(int32_t dtype, const void* x, const void* x_scale, const void* w1,
+                                     const void* w1_scale, const int32_t* sorted_ids,
+                                     const int32_t* tile_expert, const int32_t* num_tiles, int64_t T,
+                                     int32_t H, int32_t I, int32_t E, int32_t k, int32_t block_m, int64_t cap,
+                                     void* h, void* h_scale, void* stream) {
+  if (moe_status_t st = check_gemm(dtype, x, x_scale, w1, w1_scale, sorted_ids, tile_expert, num_tiles, T, H,
+                                   I, E, k, block_m, cap, h, h_scale, true))
+    return st;
+  if (T == 0) return MOE_OK;
+  moe::DeviceInfo dev;
+  if (moe_status_t st = current_device(&dev)) return st;
+  moe::GemmArgs g{x, x_scale, w1, w1_scale, sorted_ids, tile_expert, num_tiles, h, h_scale,
+                  T, H, I, E, k, block_m, cap};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (dtype) {
+    case MOE_DTYPE_BF16: return launched(moe::launch_gemm1_bf16(g, dev, s));
+    case MOE_DTYPE_FP8_BLOCK128: return launched(moe::launch_gemm1_fp8(g, dev, s));
+    default: return launched(moe::launch_gemm1_mx(g, dev, s));
+  }
+}
+
+moe_status_t moe_grouped_gemm_down(int32_t dtype, const void* h, const void* h_scale, const void* w2,
+                                   const void* w2_scale, const int32_t* sorted_ids, const int32_t* tile_expert,
+                                   const int32_t* num_tiles, int64_t T, int32_t H, int32_t I, int32_t E,
+                                   int32_t k, int32_t block_m, int64_t cap, uint16_t* y, void* stream) {
+  if (moe_status_t st = check_gemm(dtype, h, h_scale, w2, w2_scale, sorted_ids, tile_expert, num_tiles, T, H, I,
+                                   E, k, block_m, cap, y, nullptr, false))
+    return st;
+  if (T == 0) return MOE_OK;
+  moe::DeviceInfo dev;
+  if (moe_status_t st = current_device(&dev)) return st;
+  moe::GemmArgs g{h, h_scale, w2, w2_scale, sorted_ids, tile_expert, num_tiles, y, nullptr,
+                  T, H, I, E, k, block_m, cap};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (dtype) {
+    case MOE_DTYPE_BF16: return launched(moe::launch_gemm2_bf16(g, dev, s));
+    case MOE_DTYPE_FP8_BLOCK128: return launched(moe::launch_gemm2_fp8(g, dev, s));
+    default: return launched(moe::launch_gemm2_mx(g, dev, s));
+  }
+}
+
+moe_status_t moe_combine(const uint16_t* y, const float* topk_w, int64_t T, int32_t k, int32_t H,
+                         uint16_t* out, void* stream) {
+  if (T < 0 || k < 1 || k > MOE_MAX_TOPK || H <= 0) return MOE_ERR_INVALID_ARG;
+  if (H % 8) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!y || !topk_w || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned(y, 16) || !aligned(out, 16) || !aligned(topk_w, 4)) return MOE_ERR_INVALID_ARG;
+  moe::DeviceInfo dev;
+  if (moe_status_t st = current_device(&dev)) return st;
+  return launched(moe::launch_combine(y, topk_w, T, k, H, out, dev, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,111 @@
+// Device helpers shared by the gfx950 kernels: vector types, bf16 / E4M3 /
+// E2M1 / E8M0 conversions, wave-level reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(2))) int i32x2;
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------------ bf16
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even of a finite fp32 value to bf16 (bit pattern).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// ------------------------------------------------------------------ E4M3 (OCP E4M3FN)
+// Hardware conversion of two fp32 values to E4M3 (round to nearest even) into
+// the low (WORD_HI = false) or high 16 bits of `old`. Inputs are clamped to
+// [-448, 448] first, which is the saturating conversion: every magnitude
+// above 448 would round to 448 or to the (absent) 480.
+template <bool WORD_HI>
+__device__ __forceinline__ uint32_t cvt_e4m3x2(float a, float b, uint32_t old) {
+  a = __builtin_fminf(__builtin_fmaxf(a, -448.0f), 448.0f);
+  b = __builtin_fminf(__builtin_fmaxf(b, -448.0f), 448.0f);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(a, b, static_cast<int>(old), WORD_HI));
+}
+
+__device__ __forceinline__ uint32_t pack_e4m3x4(float v0, float v1, float v2, float v3) {
+  const uint32_t r = cvt_e4m3x2<false>(v0, v1, 0u);
+  return cvt_e4m3x2<true>(v2, v3, r);
+}
+
+// ------------------------------------------------------------------ E2M1
+// Round-to-nearest-even of a finite fp32 value to a 4-bit E2M1 code
+// (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), saturating at 6. Decision
+// thresholds are the midpoints of the grid; at a midpoint the code with an
+// even mantissa bit wins (0.25->0, 0.75->1, 1.25->1, 1.75->2, 2.5->2,
+// 3.5->4, 5->4).
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float a = __builtin_fabsf(v);
+  uint32_t c;
+  if (a <= 0.25f) c = 0;
+  else if (a < 0.75f) c = 1;
+  else if (a <= 1.25f) c = 2;
+  else if (a < 1.75f) c = 3;
+  else if (a <= 2.5f) c = 4;
+  else if (a < 3.5f) c = 5;
+  else if (a <= 5.0f) c = 6;
+  else c = 7;
+  return c | ((__float_as_uint(v) >> 28) & 0x8u);
+}
+
+// ------------------------------------------------------------------ E8M0 (OCP MX shared scale)
+// floor(log2(a)) of a finite a > 0 (normal or subnormal fp32), exactly.
+__device__ __forceinline__ int floor_log2(float a) {
+  const uint32_t u = __float_as_uint(a);
+  const int ex = static_cast<int>((u >> 23) & 0xFF);
+  if (ex != 0) return ex - 127;
+  return (31 - static_cast<int>(__builtin_clz(u & 0x7FFFFFu))) - 149;  // subnormal: m * 2^-149
+}
+
+// E8M0 byte of a block with maximum magnitude amax for an element format whose
+// largest power of two is 2^emax (E4M3: 8, E2M1: 2). Byte 0 when amax == 0.
+__device__ __forceinline__ int mx_scale_exponent(float amax, int emax) {
+  if (!(amax > 0.0f)) return -127;
+  int x = floor_log2(amax) - emax;
+  return x < -127 ? -127 : (x > 127 ? 127 : x);
+}
+
+// 2^-x as fp32 for x in [-127, 127] (the reciprocal of the MX scale); v * it
+// is exact whenever the product is a normal fp32 number.
+__device__ __forceinline__ float mx_inv_scale(int x) { return __builtin_ldexpf(1.0f, -x); }
+
+// ------------------------------------------------------------------ wave reductions
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+template <int WIDTH>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int o = WIDTH / 2; o > 0; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o, WIDTH));
+  return v;
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+__device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
+
+}  // namespace moe

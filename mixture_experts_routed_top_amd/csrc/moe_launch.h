@@ -1,0 +1,64 @@
+// Host-side launchers of the gfx950 kernels. Each launcher assumes its
+// arguments were validated by the C ABI front end (moe_api.cpp) and only
+// enqueues work on `stream`; it returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct DeviceInfo {
+  int num_cus;   // compute units of the current device
+};
+
+hipError_t launch_route(const float* logits, int64_t T, int E, int k, int score,
+                        int32_t* ids, float* w, hipStream_t s);
+
+// align_sort: chunked, deterministic counting sort (see align_sort.hip).
+constexpr int kAlignChunk = 1024;          // assignments per chunk of the counting pass
+size_t align_sort_ws_bytes(int64_t T, int k, int E);
+hipError_t launch_align_sort(const int32_t* ids, int64_t T, int k, int E, int block_m,
+                             int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
+                             int32_t* tile_expert, int32_t* num_tiles, int64_t cap,
+                             void* ws, hipStream_t s);
+
+hipError_t launch_quantize_fp8(const uint16_t* in, int64_t rows, int64_t cols, int block_rows,
+                               uint8_t* q, float* scale, hipStream_t s);
+hipError_t launch_quantize_mx(const uint16_t* in, int64_t rows, int64_t cols, bool fp4,
+                              uint8_t* q, uint8_t* e8m0, hipStream_t s);
+
+hipError_t launch_combine(const uint16_t* y, const float* w, int64_t T, int k, int H,
+                          uint16_t* out, const DeviceInfo& dev, hipStream_t s);
+
+// Grouped GEMMs. `gemm1` selects GEMM1 + SwiGLU (x gathered by token) versus
+// GEMM2 (h rows contiguous, output scattered to assignment order).
+struct GemmArgs {
+  const void* a;          // GEMM1: x [T, H]; GEMM2: h [cap, I]
+  const void* a_scale;
+  const void* w;          // GEMM1: W1; GEMM2: W2
+  const void* w_scale;
+  const int32_t* sorted_ids;
+  const int32_t* tile_expert;
+  const int32_t* num_tiles;
+  void* out;              // GEMM1: h [cap, I]; GEMM2: y [A, H]
+  void* out_scale;        // GEMM1 quantised h scales
+  int64_t T;
+  int H, I, E, k, block_m;
+  int64_t cap;
+};
+
+bool gemm_bf16_supports(int block_m);
+hipError_t launch_gemm1_bf16(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s);
+hipError_t launch_gemm2_bf16(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s);
+
+bool gemm_fp8_supports(int block_m);
+hipError_t launch_gemm1_fp8(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s);
+hipError_t launch_gemm2_fp8(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s);
+
+bool gemm_mx_supports(int block_m);
+hipError_t launch_gemm1_mx(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s);
+hipError_t launch_gemm2_mx(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s);
+
+}  // namespace moe

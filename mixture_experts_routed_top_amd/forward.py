@@ -1,0 +1,96 @@
+"""The routed forward as one object: weights prepared once, buffers planned
+per token count, then route -> align_sort -> [quantise x] -> GEMM1+SwiGLU ->
+GEMM2 -> combine on one stream with no allocation and no host sync.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import _binding as B
+
+
+@dataclass
+class Plan:
+    T: int
+    block_m: int
+    ids: torch.Tensor
+    w: torch.Tensor
+    sort: B.SortResult
+    xq: Optional[torch.Tensor]
+    xs: Optional[torch.Tensor]
+    h: torch.Tensor
+    h_scale: Optional[torch.Tensor]
+    y: torch.Tensor
+    out: torch.Tensor
+
+
+class MoeLayer:
+    """Routed-expert MoE MLP forward on one GPU.
+
+    w1: [E, 2I, H] bf16 (gate rows [0, I), up rows [I, 2I)); w2: [E, H, I] bf16.
+    For the FP8 path the weights are quantised here to E4M3 with 128x128 fp32
+    block scales, for the MX path to E2M1 with E8M0 per 32 along K (weight
+    preparation, outside the timed forward).
+    """
+
+    def __init__(self, dtype: int, w1: torch.Tensor, w2: torch.Tensor, k: int, score: int = B.SCORE_SOFTMAX):
+        E, twoI, H = w1.shape
+        self.dtype, self.k, self.score = dtype, k, score
+        self.E, self.H, self.I = E, H, twoI // 2
+        if w2.shape != (E, H, self.I):
+            raise ValueError("w2 must be [E, H, I]")
+        self.w1_scale = self.w2_scale = None
+        if dtype == B.DTYPE_BF16:
+            self.w1, self.w2 = w1.contiguous(), w2.contiguous()
+        elif dtype == B.DTYPE_FP8_BLOCK128:
+            self.w1, self.w1_scale = B.moe_quantize_fp8(w1.reshape(E * twoI, H).contiguous(), 128)
+            self.w2, self.w2_scale = B.moe_quantize_fp8(w2.reshape(E * H, self.I).contiguous(), 128)
+        elif dtype == B.DTYPE_MXFP4W_MXFP8A:
+            self.w1, self.w1_scale = B.moe_quantize_mxfp4(w1.reshape(E * twoI, H).contiguous())
+            self.w2, self.w2_scale = B.moe_quantize_mxfp4(w2.reshape(E * H, self.I).contiguous())
+        else:
+            raise ValueError("unknown dtype")
+
+    def plan(self, T: int, block_m: Optional[int] = None, device=None) -> Plan:
+        device = device or self.w1.device
+        bm = block_m or B.moe_pick_block_m(self.dtype, T, self.k, self.E, self.H, self.I)
+        sort = B.SortResult(T, self.k, self.E, bm, device)
+        xq = xs = None
+        if self.dtype == B.DTYPE_FP8_BLOCK128:
+            xq = torch.empty((T, self.H), dtype=torch.uint8, device=device)
+            xs = torch.empty((T, self.H // 128), dtype=torch.float32, device=device)
+        elif self.dtype == B.DTYPE_MXFP4W_MXFP8A:
+            xq = torch.empty((T, self.H), dtype=torch.uint8, device=device)
+            xs = torch.empty((T, self.H // 32), dtype=torch.uint8, device=device)
+        h, h_scale = B._h_alloc(self.dtype, max(sort.cap, 1), self.I, device)
+        return Plan(T, bm,
+                    torch.empty((T, self.k), dtype=torch.int32, device=device),
+                    torch.empty((T, self.k), dtype=torch.float32, device=device),
+                    sort, xq, xs, h, h_scale,
+                    torch.empty((max(T * self.k, 1), self.H), dtype=torch.bfloat16, device=device),
+                    torch.empty((T, self.H), dtype=torch.bfloat16, device=device))
+
+    def forward(self, x: torch.Tensor, logits: torch.Tensor, plan: Optional[Plan] = None,
+                stream=None) -> torch.Tensor:
+        T = x.shape[0]
+        p = plan if plan is not None else self.plan(T, device=x.device)
+        if p.T != T:
+            raise ValueError("plan was made for another token count")
+        B.moe_route(logits, self.k, self.score, p.ids, p.w, stream=stream)
+        B.moe_align_sort(p.ids, self.E, p.block_m, out=p.sort, stream=stream)
+        if self.dtype == B.DTYPE_BF16:
+            a, a_scale = x, None
+        elif self.dtype == B.DTYPE_FP8_BLOCK128:
+            a, a_scale = B.moe_quantize_fp8(x, 1, p.xq, p.xs, stream=stream)
+        else:
+            a, a_scale = B.moe_quantize_mxfp8(x, p.xq, p.xs, stream=stream)
+        B.moe_grouped_gemm_swiglu(self.dtype, a, a_scale, self.w1, self.w1_scale, p.sort, self.H, self.I,
+                                  p.h, p.h_scale, stream=stream)
+        B.moe_grouped_gemm_down(self.dtype, p.h, p.h_scale, self.w2, self.w2_scale, p.sort, self.H, self.I,
+                                p.y, stream=stream)
+        return B.moe_combine(p.y, p.w, p.out, stream=stream)
+
+    __call__ = forward

@@ -1,0 +1,67 @@
+"""Helpers for the GPU parity tests (comparison metrics, device transfer)."""
+import sys
+
+import numpy as np
+import torch
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    """Name the case before each GPU step (flushed, so it survives a crash)."""
+    print("[gpu-case]", *a, file=sys.stderr, flush=True)
+
+
+def cuda(t):
+    return t.to(DEV).contiguous()
+
+
+def f64(t):
+    return t.detach().to("cpu", torch.float32).numpy().astype(np.float64)
+
+
+def rel_fro(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    nb = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / (nb if nb > 0 else 1.0))
+
+
+def min_row_cos(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    na, nb = np.linalg.norm(a, axis=1), np.linalg.norm(b, axis=1)
+    ok = (na > 0) & (nb > 0)
+    if not ok.any():
+        return 1.0
+    cos = (a[ok] * b[ok]).sum(1) / (na[ok] * nb[ok])
+    return float(cos.min())
+
+
+def bf16_ulp(v):
+    """Spacing of bf16 values at |v| (normal range)."""
+    a = np.maximum(np.abs(np.asarray(v, np.float64)), 2.0 ** -126)
+    return np.ldexp(1.0, np.frexp(a)[1] - 8)
+
+
+U32 = 2.0 ** -24   # unit roundoff of fp32
+
+
+def assert_within_rounding(got, ref, delta, min_exact=None):
+    """got was rounded to bf16 from a value within `delta` of the exact value
+    whose bf16 rounding is ref: |got - ref| <= delta + one bf16 step.
+
+    delta is the caller's bound on the fp32 arithmetic error of the kernel
+    (e.g. n * 2^-24 * sum|terms| for an n-term fp32 sum)."""
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    lim = bf16_ulp(np.abs(ref) + delta) + delta + 1e-38
+    bad = np.abs(got - ref) > lim
+    assert not bad.any(), (f"{bad.sum()} of {bad.size} beyond the rounding bound; worst "
+                           f"{np.max(np.abs(got - ref) - lim):.3e}")
+    if min_exact is not None:
+        frac = float(np.mean(got == ref))
+        assert frac >= min_exact, f"only {frac:.4f} identical"
+
+
+# pass criteria for the routed forward output: relative Frobenius error of
+# the whole [T, H] output per numeric path, and the worst per-token cosine
+TOL_FRO = {0: 1e-2, 1: 2e-2, 2: 2e-2}
+TOL_COS = 0.9995

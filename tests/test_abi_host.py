@@ -1,0 +1,150 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/moe_mi355x.h declares, and rejects bad arguments on the host before
+touching a device. No call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from oracle import moe as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mi355x.h")
+
+M = pytest.importorskip("mixture_experts_routed_top_amd")
+
+
+def _lib():
+    try:
+        return M.lib()
+    except RuntimeError as e:  # not built
+        pytest.fail(str(e))
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(moe_[a-z_0-9]+)\s*\(", text, flags=re.M)
+
+
+def test_header_declares_the_boundary():
+    names = set(declared_functions())
+    for n in ["moe_route", "moe_align_sort", "moe_grouped_gemm_swiglu", "moe_grouped_gemm_down",
+              "moe_combine", "moe_quantize_fp8", "moe_quantize_mxfp8", "moe_quantize_mxfp4",
+              "moe_sorted_capacity", "moe_align_sort_workspace_bytes", "moe_pick_block_m",
+              "moe_status_string"]:
+        assert n in names, n
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    # the binding declares the same set with signatures
+    assert set(declared_functions()) == set(M._binding.SIGNATURES)
+
+
+def test_status_strings():
+    assert M.moe_status_string(0) == "MOE_OK"
+    assert M.moe_status_string(3) == "MOE_ERR_WORKSPACE"
+    assert M.moe_status_string(99) == "MOE_ERR_UNKNOWN"
+
+
+@pytest.mark.parametrize("T,k,E,bm", [(0, 2, 8, 16), (1, 1, 1, 16), (64, 2, 8, 32), (8192, 8, 128, 128),
+                                      (16384, 10, 512, 16), (129, 10, 512, 64)])
+def test_capacity_matches_oracle(T, k, E, bm):
+    assert M.moe_sorted_capacity(T, k, E, bm) == O.sorted_capacity(T, k, E, bm)
+
+
+def test_capacity_and_block_m_rejections():
+    assert M.moe_sorted_capacity(10, 2, 8, 48) == -1
+    assert M.moe_sorted_capacity(-1, 2, 8, 16) == -1
+    assert M.moe_pick_block_m(0, 10, 9, 8, 256, 128) == -1          # k > E
+    for dt in (0, 1, 2):
+        for T in (1, 64, 1024, 8192, 16384):
+            assert M.moe_pick_block_m(dt, T, 8, 128, 2048, 768) in (16, 32, 64, 128, 256)
+
+
+def test_workspace_bytes():
+    assert M.moe_align_sort_workspace_bytes(0, 8, 128) == 0
+    assert M.moe_align_sort_workspace_bytes(64, 2, 8) == 4 * (1 * 8 + 128)
+    assert M.moe_align_sort_workspace_bytes(8192, 8, 128) == 4 * (64 * 128 + 65536)
+
+
+NULL = None
+FAKE = 0x10000  # 16-byte aligned non-null address; never dereferenced by these calls
+MIS = 0x10002   # misaligned
+
+
+def test_route_host_validation():
+    L = _lib()
+    assert L.moe_route(FAKE, 4, 8, 9, 0, FAKE, FAKE, NULL) == M._binding.MOE_ERR_INVALID_ARG  # k > E
+    assert L.moe_route(FAKE, 4, 8, 0, 0, FAKE, FAKE, NULL) == 1
+    assert L.moe_route(FAKE, 4, 2000, 2, 0, FAKE, FAKE, NULL) == 1                           # E too large
+    assert L.moe_route(FAKE, 4, 8, 2, 7, FAKE, FAKE, NULL) == 1                              # score
+    assert L.moe_route(NULL, 4, 8, 2, 0, FAKE, FAKE, NULL) == 1
+    assert L.moe_route(MIS, 4, 8, 2, 0, FAKE, FAKE, NULL) == 1
+    assert L.moe_route(NULL, 0, 8, 2, 0, NULL, NULL, NULL) == 0                              # T = 0
+    assert L.moe_route(FAKE, -1, 8, 2, 0, FAKE, FAKE, NULL) == 1
+
+
+def test_align_sort_host_validation():
+    L = _lib()
+    ws = M.moe_align_sort_workspace_bytes(64, 2, 8)
+    args = lambda bm, wsb, ids=FAKE: (ids, 64, 2, 8, bm, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wsb, NULL)
+    assert L.moe_align_sort(*args(48, ws)) == 1
+    assert L.moe_align_sort(*args(16, ws - 4)) == M._binding.MOE_ERR_WORKSPACE
+    assert L.moe_align_sort(*args(16, ws, NULL)) == 1
+    assert L.moe_align_sort(NULL, 0, 2, 8, 16, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL) == 0
+
+
+def test_quantize_host_validation():
+    L = _lib()
+    assert L.moe_quantize_fp8(FAKE, 128, 100, 1, FAKE, FAKE, NULL) == M._binding.MOE_ERR_UNSUPPORTED_SHAPE
+    assert L.moe_quantize_fp8(FAKE, 100, 128, 128, FAKE, FAKE, NULL) == 2
+    assert L.moe_quantize_fp8(FAKE, 128, 128, 64, FAKE, FAKE, NULL) == 1
+    assert L.moe_quantize_fp8(MIS, 128, 128, 1, FAKE, FAKE, NULL) == 1
+    assert L.moe_quantize_mxfp8(FAKE, 4, 40, FAKE, FAKE, NULL) == 2
+    assert L.moe_quantize_mxfp4(FAKE, 4, 40, FAKE, FAKE, NULL) == 2
+    assert L.moe_quantize_mxfp4(NULL, 0, 64, NULL, NULL, NULL) == 0
+
+
+def _gemm_args(dtype=0, T=64, H=256, I=128, E=8, k=2, bm=32, cap=None, x=FAKE, w=FAKE, out=FAKE):
+    cap = O.sorted_capacity(T, k, E, bm) if cap is None else cap
+    return (dtype, x, FAKE, w, FAKE, FAKE, FAKE, FAKE, T, H, I, E, k, bm, cap)
+
+
+def test_gemm_host_validation():
+    L = _lib()
+    sw = lambda *a, **kw: L.moe_grouped_gemm_swiglu(*_gemm_args(*a, **kw), FAKE, FAKE, NULL)
+    dn = lambda *a, **kw: L.moe_grouped_gemm_down(*_gemm_args(*a, **kw), FAKE, NULL)
+    for f in (sw, dn):
+        assert f(dtype=5) == 1
+        assert f(H=100) == 2                    # bf16 needs H % 8 == 0
+        assert f(dtype=1, H=192) == 2           # fp8 needs H % 128 == 0
+        assert f(dtype=2, I=96) == 2            # mx needs I % 128 == 0
+        assert f(bm=48) == 1
+        assert f(cap=12345) == 1                # capacity must be the queried one
+        assert f(k=9) == 1
+        assert f(x=NULL) == 1
+        assert f(w=MIS) == 1
+        assert f(T=0, x=NULL, w=NULL) == 0
+
+
+def test_combine_host_validation():
+    L = _lib()
+    assert L.moe_combine(FAKE, FAKE, 4, 2, 100, FAKE, NULL) == 2
+    assert L.moe_combine(FAKE, FAKE, 4, 0, 128, FAKE, NULL) == 1
+    assert L.moe_combine(MIS, FAKE, 4, 2, 128, FAKE, NULL) == 1
+    assert L.moe_combine(NULL, NULL, 0, 2, 128, NULL, NULL) == 0
+
+
+def test_device_check_without_gpu():
+    # valid arguments reach the device check; without a gfx950 device current
+    # the call must fail with MOE_ERR_DEVICE and launch nothing
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: fake pointers would be dereferenced")
+    L = _lib()
+    assert L.moe_route(FAKE, 4, 8, 2, 0, FAKE, FAKE, NULL) == M._binding.MOE_ERR_DEVICE

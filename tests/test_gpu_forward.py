@@ -1,0 +1,100 @@
+"""End-to-end GPU forward (route -> align_sort -> GEMM1+SwiGLU -> GEMM2 ->
+combine, all through the C ABI) against the oracle.
+
+Small problems are compared on every output element; the full-size
+workloads, in the launch configuration the benchmark times, are compared on
+all routing / layout outputs and on a sample of tokens that the oracle
+evaluates one by one."""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_routed_top_amd as M
+from oracle import moe as O
+from workloads import get_config, make_inputs, to_f64
+from tests.gpu_util import TOL_COS, TOL_FRO, cuda, f64, min_row_cos, rel_fro, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(cfg, inp, block_m=None):
+    layer = M.MoeLayer(cfg.dtype, cuda(inp.w1), cuda(inp.w2), cfg.k, cfg.score)
+    plan = layer.plan(cfg.T, block_m=block_m)
+    out = layer(cuda(inp.x), cuda(inp.logits), plan)
+    torch.cuda.synchronize()
+    return layer, plan, out
+
+
+def _full_compare(cfg, inp, block_m=None):
+    say("forward full", cfg.name, cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, block_m)
+    layer, plan, out = _run(cfg, inp, block_m)
+    ref = O.moe_forward(inp.logits.numpy(), to_f64(inp.x), to_f64(inp.w1), to_f64(inp.w2), cfg.k, cfg.score,
+                        cfg.dtype, block_m=plan.block_m)
+    np.testing.assert_array_equal(plan.ids.cpu().numpy(), ref["ids"])
+    np.testing.assert_array_equal(plan.sort.sorted_ids.cpu().numpy()[:len(ref["sorted_ids"])], ref["sorted_ids"])
+    got = f64(out)
+    assert rel_fro(got, ref["out"]) <= TOL_FRO[cfg.dtype]
+    assert min_row_cos(got, ref["out"]) >= TOL_COS
+    return got, ref
+
+
+def test_tiny_bf16_forward():
+    cfg = get_config("tiny_bf16")
+    got, ref = _full_compare(cfg, make_inputs(cfg))
+    assert rel_fro(got, ref["out"]) < 4e-3
+
+
+@pytest.mark.parametrize("T,H,E,k,I", [(1, 256, 8, 2, 128), (7, 256, 8, 2, 128), (129, 384, 16, 4, 256),
+                                       (64, 192, 4, 2, 96), (8191 // 16, 2048, 128, 8, 768),
+                                       (100, 1024, 1, 1, 512)])
+def test_bf16_forward_edge_shapes(T, H, E, k, I):
+    cfg = get_config("tiny_bf16").with_(T=T, H=H, E=E, k=k, I=I, w_std=0.05)
+    _full_compare(cfg, make_inputs(cfg, seed=T))
+
+
+def test_bf16_forward_one_expert_takes_all():
+    cfg = get_config("tiny_bf16").with_(T=300, E=8, k=1)
+    inp = make_inputs(cfg, seed=3)
+    inp.logits[:] = -1.0
+    inp.logits[:, 5] = 2.0        # every token -> expert 5; the others stay empty
+    _full_compare(cfg, inp)
+
+
+def test_bf16_forward_deterministic():
+    cfg = get_config("tiny_bf16").with_(T=513, E=16, k=4)
+    inp = make_inputs(cfg, seed=9)
+    say("forward determinism")
+    _, _, a = _run(cfg, inp)
+    _, _, b = _run(cfg, inp)
+    assert torch.equal(a, b)
+
+
+def _sampled_compare(name, n_sample=24):
+    cfg = get_config(name)
+    inp = make_inputs(cfg)
+    say("forward full-size sampled", name)
+    layer, plan, out = _run(cfg, inp)
+    # every routing and layout output is compared in full
+    rid, rw = O.route(inp.logits.numpy(), cfg.k, cfg.score)
+    np.testing.assert_array_equal(plan.ids.cpu().numpy(), rid)
+    np.testing.assert_allclose(plan.w.cpu().numpy(), rw, rtol=0, atol=4e-6)
+    counts, offsets, sorted_ids, tile_expert, num_tiles = O.align_sort(rid, cfg.E, plan.block_m)
+    np.testing.assert_array_equal(plan.sort.sorted_ids.cpu().numpy()[:len(sorted_ids)], sorted_ids)
+    np.testing.assert_array_equal(plan.sort.tile_expert.cpu().numpy()[:len(tile_expert)], tile_expert)
+    # sampled tokens, evaluated one by one
+    rng = np.random.default_rng(0)
+    toks = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, n_sample, replace=False)]))
+    experts = sorted({int(e) for t in toks for e in rid[t]})
+    w1 = {e: to_f64(inp.w1[e]) for e in experts}
+    w2 = {e: to_f64(inp.w2[e]) for e in experts}
+    x = to_f64(inp.x[torch.from_numpy(toks)])
+    ref = np.stack([O.token_forward(x[i], w1, w2, rid[t], rw[t], cfg.dtype) for i, t in enumerate(toks)])
+    got = f64(out[torch.from_numpy(toks).to(out.device)])
+    assert rel_fro(got, ref) <= TOL_FRO[cfg.dtype]
+    assert min_row_cos(got, ref) >= TOL_COS
+    assert torch.isfinite(out.float()).all()
+
+
+@pytest.mark.parametrize("name", ["qwen3_30b_a3b_bf16", "qwen3_30b_a3b_bf16_zipf", "llama4_scout_bf16"])
+def test_full_size_bf16_sampled(name):
+    _sampled_compare(name)
