@@ -30,8 +30,8 @@ DTYPE_NAME = {0: "bf16", 1: "fp8_e4m3 (128-block scales)", 2: "mxfp4 weights x m
 PAGE_BASELINE = {"qwen3_30b_a3b_bf16": (354.38, "H200 1-GPU BF16 forward, Liger-Kernel PR #1463 MoEBenchmark"),
                  "llama4_scout_bf16": (511.36, "H200 1-GPU BF16 forward, Liger-Kernel PR #1463 MoEBenchmark")}
 STAGES = ["route", "align_sort", "quantize_x", "gemm1_swiglu", "gemm2_down", "combine"]
-KERNEL_SRC = {"gemm1_swiglu": {0: "gemm_bf16.hip", 1: "gemm_fp8.hip", 2: "gemm_mx.hip"},
-              "gemm2_down": {0: "gemm_bf16.hip", 1: "gemm_fp8.hip", 2: "gemm_mx.hip"}}
+KERNEL_SRC = {"gemm1_swiglu": {0: "gemm_bf16.hip", 1: "gemm_scaled.hip", 2: "gemm_scaled.hip"},
+              "gemm2_down": {0: "gemm_bf16.hip", 1: "gemm_scaled.hip", 2: "gemm_scaled.hip"}}
 
 
 def _src_hash(fname: str) -> str:

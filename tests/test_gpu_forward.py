@@ -88,6 +88,8 @@ def _sampled_compare(name, n_sample=24):
     w1 = {e: to_f64(inp.w1[e]) for e in experts}
     w2 = {e: to_f64(inp.w2[e]) for e in experts}
     x = to_f64(inp.x[torch.from_numpy(toks)])
+    if cfg.dtype != O.DTYPE_BF16:
+        x, w1, w2 = _dequantised(cfg, layer, x, w1, w2)
     ref = np.stack([O.token_forward(x[i], w1, w2, rid[t], rw[t], cfg.dtype) for i, t in enumerate(toks)])
     got = f64(out[torch.from_numpy(toks).to(out.device)])
     assert rel_fro(got, ref) <= TOL_FRO[cfg.dtype]
@@ -95,6 +97,53 @@ def _sampled_compare(name, n_sample=24):
     assert torch.isfinite(out.float()).all()
 
 
+def _dequantised(cfg, layer, x, w1, w2):
+    """Oracle-quantised operands of the sampled tokens / experts; the GPU's
+    own weight codes for those experts must equal the oracle's bit for bit."""
+    twoI, H, I = 2 * cfg.I, cfg.H, cfg.I
+    d1, d2 = {}, {}
+    for e in w1:
+        gw1 = {e: layer.w1[e * twoI:(e + 1) * twoI].cpu().numpy()}
+        gw2 = {e: layer.w2[e * H:(e + 1) * H].cpu().numpy()}
+        if cfg.dtype == O.DTYPE_FP8_BLOCK128:
+            q1, s1 = O.quantize_fp8_block(w1[e], 128, 128)
+            q2, s2 = O.quantize_fp8_block(w2[e], 128, 128)
+            np.testing.assert_array_equal(gw1[e], q1)
+            np.testing.assert_array_equal(layer.w1_scale[e * twoI // 128:(e + 1) * twoI // 128].cpu().numpy(), s1)
+            np.testing.assert_array_equal(gw2[e], q2)
+            np.testing.assert_array_equal(layer.w2_scale[e * H // 128:(e + 1) * H // 128].cpu().numpy(), s2)
+            d1[e] = O.dequantize_fp8_block(q1, s1, 128, 128)
+            d2[e] = O.dequantize_fp8_block(q2, s2, 128, 128)
+        else:
+            q1, s1 = O.quantize_mxfp4(w1[e])
+            q2, s2 = O.quantize_mxfp4(w2[e])
+            np.testing.assert_array_equal(gw1[e], q1)
+            np.testing.assert_array_equal(layer.w1_scale[e * twoI:(e + 1) * twoI].cpu().numpy(), s1)
+            np.testing.assert_array_equal(gw2[e], q2)
+            np.testing.assert_array_equal(layer.w2_scale[e * H:(e + 1) * H].cpu().numpy(), s2)
+            d1[e] = O.dequantize_mxfp4(q1, s1)
+            d2[e] = O.dequantize_mxfp4(q2, s2)
+    if cfg.dtype == O.DTYPE_FP8_BLOCK128:
+        xh = O.dequantize_fp8_block(*O.quantize_fp8_block(x, 1, 128), 1, 128)
+    else:
+        xh = O.dequantize_mxfp8(*O.quantize_mxfp8(x))
+    return xh, d1, d2
+
+
 @pytest.mark.parametrize("name", ["qwen3_30b_a3b_bf16", "qwen3_30b_a3b_bf16_zipf", "llama4_scout_bf16"])
 def test_full_size_bf16_sampled(name):
     _sampled_compare(name)
+
+
+@pytest.mark.parametrize("name", ["fp8_block128_share", "mxfp4_moe_t128", "mxfp4_moe_t1024", "mxfp4_moe_t8192",
+                                  "mxfp4_moe_t16384"])
+def test_full_size_scaled_sampled(name):
+    _sampled_compare(name)
+
+
+@pytest.mark.parametrize("dtype", [O.DTYPE_FP8_BLOCK128, O.DTYPE_MXFP4W_MXFP8A])
+@pytest.mark.parametrize("T,H,E,k,I", [(64, 256, 8, 2, 128), (129, 384, 16, 4, 256), (1, 256, 4, 2, 128),
+                                       (300, 1024, 32, 8, 512), (257, 2560, 64, 10, 640)])
+def test_scaled_forward_small(dtype, T, H, E, k, I):
+    cfg = get_config("tiny_bf16").with_(T=T, H=H, E=E, k=k, I=I, dtype=dtype, w_std=0.05)
+    _full_compare(cfg, make_inputs(cfg, seed=T + dtype))

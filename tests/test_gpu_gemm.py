@@ -146,3 +146,175 @@ def test_gemm_bitwise_invariant_to_block_m_layout():
         torch.cuda.synchronize()
         ys.append(y.cpu())
     assert torch.equal(ys[0], ys[1]) and torch.equal(ys[0], ys[2])
+
+
+# ============================================================ FP8 128-block and MX paths
+def _fp8_operands(x, w1, w2, integer):
+    """Oracle-quantised operands (codes, scales) for the FP8 path.
+
+    integer: small-integer values encoded exactly with unit scales, so every
+    product and every fp32 partial sum is exact."""
+    from oracle import formats as F
+    E, twoI, H = w1.shape
+    I = twoI // 2
+    if integer:
+        xq, xs = F.e4m3_encode(x), np.ones((x.shape[0], H // 128), np.float32)
+        w1q, w1s = F.e4m3_encode(w1.reshape(E * twoI, H)), np.ones((E * twoI // 128, H // 128), np.float32)
+        w2q, w2s = F.e4m3_encode(w2.reshape(E * H, I)), np.ones((E * H // 128, I // 128), np.float32)
+    else:
+        xq, xs = O.quantize_fp8_block(x, 1, 128)
+        w1q, w1s = O.quantize_fp8_block(w1.reshape(E * twoI, H), 128, 128)
+        w2q, w2s = O.quantize_fp8_block(w2.reshape(E * H, I), 128, 128)
+    deq = (O.dequantize_fp8_block(xq, xs, 1, 128),
+           O.dequantize_fp8_block(w1q, w1s, 128, 128).reshape(w1.shape),
+           O.dequantize_fp8_block(w2q, w2s, 128, 128).reshape(w2.shape))
+    return (xq, xs), (w1q, w1s), (w2q, w2s), deq
+
+
+def _mx_operands(x, w1, w2, integer):
+    from oracle import formats as F
+    E, twoI, H = w1.shape
+    I = twoI // 2
+    if integer:
+        xq, xs = F.e4m3_encode(x), np.full((x.shape[0], H // 32), 127, np.uint8)
+        w1q = F.pack_e2m1(F.e2m1_encode(w1.reshape(E * twoI, H)))
+        w1s = np.full((E * twoI, H // 32), 127, np.uint8)
+        w2q = F.pack_e2m1(F.e2m1_encode(w2.reshape(E * H, I)))
+        w2s = np.full((E * H, I // 32), 127, np.uint8)
+    else:
+        xq, xs = O.quantize_mxfp8(x)
+        w1q, w1s = O.quantize_mxfp4(w1.reshape(E * twoI, H))
+        w2q, w2s = O.quantize_mxfp4(w2.reshape(E * H, I))
+    deq = (O.dequantize_mxfp8(xq, xs), O.dequantize_mxfp4(w1q, w1s).reshape(w1.shape),
+           O.dequantize_mxfp4(w2q, w2s).reshape(w2.shape))
+    return (xq, xs), (w1q, w1s), (w2q, w2s), deq
+
+
+def _t(a):
+    return cuda(torch.from_numpy(np.ascontiguousarray(a)))
+
+
+SCALED_SHAPES = [  # T, H, E, k, I, block_m
+    (64, 256, 8, 2, 128, 32),
+    (129, 384, 16, 4, 256, 64),
+    (300, 1024, 32, 8, 512, 128),
+    (1, 256, 4, 2, 128, 32),
+]
+
+
+def _int_problem(T, H, E, k, I, seed, dtype):
+    rng = np.random.default_rng(seed)
+    vals = np.array([-3, -2, -1.5, -1, -0.5, 0, 0.5, 1, 1.5, 2, 3]) if dtype == M.DTYPE_MXFP4W_MXFP8A \
+        else np.arange(-4, 5).astype(np.float64)
+    x = rng.integers(-3, 4, (T, H)).astype(np.float64)
+    w1 = rng.choice(vals, (E, 2 * I, H))
+    w2 = rng.choice(vals, (E, H, I))
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    ids, _ = O.route(logits, k)
+    return x, w1, w2, ids
+
+
+@pytest.mark.parametrize("dtype", [M.DTYPE_FP8_BLOCK128, M.DTYPE_MXFP4W_MXFP8A])
+@pytest.mark.parametrize("integer", [True, False])
+@pytest.mark.parametrize("T,H,E,k,I,bm", SCALED_SHAPES)
+def test_gemm2_down_scaled(T, H, E, k, I, bm, integer, dtype):
+    if integer:
+        x, w1, w2, ids = _int_problem(T, H, E, k, I, T + H, dtype)
+    else:
+        x, w1, w2, ids = _problem(T, H, E, k, I, T + 3 * H + I, False)
+    sort, (sorted_ids, tile_expert, num_tiles) = _sort_from_oracle(ids, E, bm)
+    rows = num_tiles * bm
+    rng = np.random.default_rng(11)
+    # h operand: codes and scales straight from the oracle's quantiser of a random h
+    hraw = rng.integers(-4, 5, (sort.cap, I)).astype(np.float64) if integer else \
+        f64(_bf16(rng.standard_normal((sort.cap, I))))
+    ops = _fp8_operands if dtype == M.DTYPE_FP8_BLOCK128 else _mx_operands
+    _, _, (w2q, w2s), (_, _, w2h) = ops(x, w1, w2, integer)
+    if dtype == M.DTYPE_FP8_BLOCK128:
+        from oracle import formats as F
+        hq, hs = (F.e4m3_encode(hraw), np.ones((sort.cap, I // 128), np.float32)) if integer else \
+            O.quantize_fp8_block(hraw, 1, 128)
+        hhat = O.dequantize_fp8_block(hq, hs, 1, 128)
+    else:
+        from oracle import formats as F
+        hq, hs = (F.e4m3_encode(hraw), np.full((sort.cap, I // 32), 127, np.uint8)) if integer else \
+            O.quantize_mxfp8(hraw)
+        hhat = O.dequantize_mxfp8(hq, hs)
+    say("gemm2 scaled", dtype, T, H, E, k, I, bm, integer)
+    y = torch.full((T * k, H), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    M.moe_grouped_gemm_down(dtype, _t(hq), _t(hs), _t(w2q), _t(w2s), sort, H, I, y=y)
+    torch.cuda.synchronize()
+    ref = O.grouped_gemm_down(hhat[:rows], w2h, sorted_ids, tile_expert, num_tiles, bm, T * k)
+    got = f64(y)
+    assert not np.isnan(got).any()
+    if integer:
+        np.testing.assert_array_equal(got, ref)
+    else:
+        absref = O.grouped_gemm_down(np.abs(hhat[:rows]), np.abs(w2h), sorted_ids, tile_expert, num_tiles, bm,
+                                     T * k)
+        # fp32 accumulation, plus (FP8) one scale product and one fused add per 128-group
+        assert_within_rounding(got, ref, 1.05 * (I + 3 * I // 128) * U32 * absref, min_exact=0.98)
+
+
+def _check_h_quant(dtype, hq_gpu, hs_gpu, href, rows, I, delta):
+    """Requantised h from the kernel versus the float64 h of the same operands.
+
+    delta bounds |h_fp32 - h| elementwise (fp32 accumulation in the kernel)."""
+    from oracle import formats as F
+    hq_gpu, hs_gpu = hq_gpu[:rows], hs_gpu[:rows]
+    if dtype == M.DTYPE_FP8_BLOCK128:
+        deq = O.dequantize_fp8_block(hq_gpu, hs_gpu, 1, 128)
+        # every non-zero 1x128 block has its maximum on the top code (+-448)
+        mag = (hq_gpu & 0x7F).reshape(rows, I // 128, 128).max(-1)
+        nz = np.abs(href).reshape(rows, I // 128, 128).max(-1) > 0
+        assert np.all(mag[nz] == 0x7E)
+        scale = np.repeat(hs_gpu.astype(np.float64), 128, axis=1)
+    else:
+        deq = O.dequantize_mxfp8(hq_gpu, hs_gpu)
+        mag = np.abs(F.e4m3_decode(hq_gpu)).reshape(rows, I // 32, 32).max(-1)
+        nz = hs_gpu != 0
+        assert np.all((mag[nz] >= 256) & (mag[nz] <= 448))
+        scale = np.repeat(F.e8m0_decode(hs_gpu), 32, axis=1)
+    # E4M3 rounding: half an ulp is 2^-4 of |v| for normal codes and 2^-10 of
+    # the scale for subnormal ones, applied to the kernel's fp32 h (within
+    # delta of h). MX blocks may clip: magnitudes above 448 X become 448 X.
+    target = np.clip(href, -448 * scale, 448 * scale)
+    lim = (1.01 / 16) * (np.abs(target) + delta) + delta + scale / 512 + 1e-30
+    bad = np.abs(deq - target) > lim
+    if bad.any():
+        r, c = np.argwhere(bad)[0]
+        blk = 128 if dtype == M.DTYPE_FP8_BLOCK128 else 32
+        b0 = (c // blk) * blk
+        raise AssertionError(f"{bad.sum()} of {bad.size} elements off; first at row {r} col {c}: h={href[r, c]:.6g} "
+                             f"deq={deq[r, c]:.6g} scale={scale[r, c]:.6g} block amax(h)="
+                             f"{np.abs(href[r, b0:b0 + blk]).max():.6g} code={hq_gpu[r, c]:#x}")
+    return deq
+
+
+@pytest.mark.parametrize("dtype", [M.DTYPE_FP8_BLOCK128, M.DTYPE_MXFP4W_MXFP8A])
+@pytest.mark.parametrize("T,H,E,k,I,bm", SCALED_SHAPES)
+def test_gemm1_swiglu_scaled(T, H, E, k, I, bm, dtype):
+    x, w1, w2, ids = _problem(T, H, E, k, I, T + 5 * H + I, False)
+    sort, (sorted_ids, tile_expert, num_tiles) = _sort_from_oracle(ids, E, bm)
+    rows = num_tiles * bm
+    ops = _fp8_operands if dtype == M.DTYPE_FP8_BLOCK128 else _mx_operands
+    (xq, xs), (w1q, w1s), _, (xh, w1h, _) = ops(x, w1, w2, False)
+    say("gemm1 scaled", dtype, T, H, E, k, I, bm)
+    hq, hs = M.moe_grouped_gemm_swiglu(dtype, _t(xq), _t(xs), _t(w1q), _t(w1s), sort, H, I)
+    torch.cuda.synchronize()
+    # float64 h from the same dequantised operands, before its storage point
+    g, u = _values(xh, w1h, sorted_ids, tile_expert, num_tiles, bm, k, rows)
+    sig = 1.0 / (1.0 + np.exp(-np.clip(g, -700, 700)))
+    href = g * sig * u
+    # fp32 accumulation of H products, plus (FP8) one scale product and one
+    # fused add per 128-group, for g and for u
+    ga, ua = _abs_sums(xh, w1h, sorted_ids, tile_expert, num_tiles, bm, k, rows)
+    dg, du = (H + 3 * H // 128) * U32 * ga, (H + 3 * H // 128) * U32 * ua
+    delta = 1.1 * dg * (np.abs(u) + du) + np.abs(g * sig) * du + 8 * U32 * np.abs(href)
+    deq = _check_h_quant(dtype, hq.cpu().numpy(), hs.cpu().numpy(), href, rows, I, delta)
+    (ref_codes, _ref_scales), ref_val = O.grouped_gemm_swiglu(xh, w1h, sorted_ids, tile_expert, num_tiles, bm, k,
+                                                              dtype)
+    assert np.linalg.norm(deq - ref_val) <= 0.02 * np.linalg.norm(ref_val) + 1e-30
+    # codes agree with the oracle's requantisation of its own float64 h except
+    # where the fp32 and float64 h straddle a rounding boundary
+    assert np.mean(hq.cpu().numpy()[:rows] == ref_codes) > 0.97
