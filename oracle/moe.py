@@ -362,22 +362,29 @@ def routed_flops(T: int, k: int, H: int, I: int) -> int:
     return 6 * T * k * H * I
 
 
+def assignment_forward(x_row, w1e, w2e, dtype: int = DTYPE_BF16):
+    """One (token, expert) row of Y computed on its own: the same arithmetic as
+    grouped_gemm_swiglu + grouped_gemm_down restricted to one assignment.
+
+    x_row [H] dequantised token, w1e [2I, H] and w2e [H, I] the expert's
+    dequantised weights. Returns float64 bf16 values [H]."""
+    w1e = np.asarray(w1e, np.float64)
+    I = w1e.shape[0] // 2
+    g = w1e[:I] @ x_row
+    u = w1e[I:] @ x_row
+    _, hv = _store_h((silu(g) * u)[None, :], dtype)
+    return F.round_bf16(np.asarray(w2e, np.float64) @ hv[0])
+
+
 def token_forward(x_row, w1_hat, w2_hat, ids_row, w_row, dtype: int = DTYPE_BF16):
     """One token's output computed on its own (used for sampled checks at
     full size: same arithmetic as moe_forward restricted to one token).
 
     x_row [H] dequantised input, ids_row/w_row [k]. Returns float64 bf16 values [H].
     """
-    e0 = int(ids_row[0])
-    I = np.asarray(w1_hat[e0]).shape[0] // 2
-    acc = np.zeros(np.asarray(w2_hat[e0]).shape[0], dtype=np.float64)
-    for j, e in enumerate(ids_row):
-        w1e = np.asarray(w1_hat[e], np.float64)      # array [E,...] or a dict of experts
-        g = w1e[:I] @ x_row
-        u = w1e[I:] @ x_row
-        _, hv = _store_h((silu(g) * u)[None, :], dtype)
-        y = F.round_bf16(np.asarray(w2_hat[e], np.float64) @ hv[0])
-        acc += float(w_row[j]) * y
+    acc = np.zeros(np.asarray(w2_hat[int(ids_row[0])]).shape[0], dtype=np.float64)
+    for j, e in enumerate(ids_row):   # w1_hat / w2_hat: arrays [E, ...] or dicts of experts
+        acc += float(w_row[j]) * assignment_forward(x_row, w1_hat[e], w2_hat[e], dtype)
     return F.round_bf16(acc)
 
 
