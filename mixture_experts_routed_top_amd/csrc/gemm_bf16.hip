@@ -6,17 +6,25 @@
 // Design for gfx950:
 //   * persistent workgroups walk one flat task list: task = (m-tile of the
 //     sorted rows, n-tile of the output columns); the m-tile count is read
-//     from device memory, so the host never waits for the router;
+//     from device memory, so the host never waits for the router. The list is
+//     cut into one contiguous slice per XCD (workgroup b runs on XCD b % 8), so
+//     the workgroups that run together on one XCD work on neighbouring tasks of
+//     the same expert and share its weight slices in that XCD's L2;
 //   * MFMA v_mfma_f32_32x32x16_bf16 with the weight rows as the MFMA "A"
-//     operand and the token rows as "B" (output transposed in registers:
-//     each lane ends up with four consecutive output columns of one token,
-//     which become one 8-byte store);
-//   * 4 waves per workgroup, LDS double buffered (global -> registers for
-//     k-step s+1 while the MFMAs consume k-step s); 128-byte LDS rows with
-//     the 16-byte chunk index XOR-swizzled by (row & 7) so that the MFMA
-//     fragment reads of 8 consecutive rows hit distinct banks;
-//   * GEMM1 keeps the gate rows n and up rows I + n of the same output
-//     column in one workgroup, so SwiGLU runs in registers in the epilogue.
+//     operand and the token rows as "B" (output transposed in registers: each
+//     lane ends up with four consecutive output columns of one token, which
+//     become one 8-byte store);
+//   * 8 waves per workgroup (two per SIMD, so one wave's MFMAs cover the other's
+//     waits); a workgroup tile is 128 sorted rows x 512 weight rows and each
+//     wave owns 8 32x32 accumulator tiles (64 tokens x 128 weight rows), which
+//     keeps both the L2->LDS traffic and the LDS reads per MFMA low;
+//   * software pipeline of depth two: the global loads for k-step s+2 are in
+//     flight in one register set while k-step s+1 waits in the other and the
+//     MFMAs consume k-step s from LDS (double buffered); one barrier per step;
+//   * LDS rows of BK bf16 with the 16-byte chunk index XOR-swizzled by row, so
+//     the fragment reads of 8 consecutive rows fall on distinct banks;
+//   * GEMM1 keeps the gate rows n and up rows I + n of the same output column
+//     in one workgroup, so SwiGLU runs in registers in the epilogue.
 #include "moe_common.cuh"
 #include "moe_launch.h"
 
@@ -24,33 +32,51 @@ namespace moe {
 
 namespace {
 
-constexpr int kBK = 64;        // bf16 elements per k-step (128 bytes per LDS row)
-constexpr int kThreads = 256;
+constexpr int kXcds = 8;
 
 template <int BM, int BN, int WM, int WN, bool GEMM1>
 struct Cfg {
+  static constexpr int BK = 64;                       // bf16 per k-step: 128-byte LDS rows
   static constexpr int B_ROWS = GEMM1 ? 2 * BN : BN;  // weight rows staged per k-step
   static constexpr int TM = BM / WM;                  // token rows per wave
   static constexpr int TN = BN / WN;                  // output columns per wave
   static constexpr int FM = TM / 32;
   static constexpr int FN = TN / 32;
   static constexpr int HALVES = GEMM1 ? 2 : 1;
-  static constexpr int A_LOADS = BM * 8 / kThreads;   // 16-byte chunks per thread
-  static constexpr int B_LOADS = B_ROWS * 8 / kThreads;
-  static constexpr int STAGE = (BM + B_ROWS) * 128;   // bytes per LDS stage
-  static_assert(WM * WN == 4, "4 waves");
+  static constexpr int WAVES = WM * WN;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int ROWS = BM + B_ROWS;            // LDS rows per stage
+  static constexpr int GROUPS = ROWS / 8;             // 8 rows = one 1 KB direct-to-LDS load
+  static constexpr int GPW = (GROUPS + WAVES - 1) / WAVES;   // loads per wave per k-step
+  static constexpr int STAGE = ROWS * 128;
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile is a multiple of 32");
-  static_assert(BM * 8 % kThreads == 0 && B_ROWS * 8 % kThreads == 0, "whole loads");
+  static_assert(BM % 8 == 0, "token rows fill whole 8-row groups");
+  static_assert(2 * STAGE <= 160 * 1024, "two stages fit in LDS");
 };
 
-__device__ __forceinline__ uint32_t lds_off(int row, int chunk) {
-  return static_cast<uint32_t>(row * 128 + ((chunk ^ (row & 7)) << 4));
+// Byte offset of 16-byte chunk c of LDS row `row`: the XOR swizzle spreads 8
+// consecutive rows reading the same logical chunk over distinct banks.
+__device__ __forceinline__ uint32_t lds_off(int row, int c) {
+  return static_cast<uint32_t>(row * 128 + ((c ^ (row & 7)) << 4));
 }
 
 __device__ __forceinline__ bf16x8 lds_frag(const char* base, int row, int chunk) {
   const uint4 v = *reinterpret_cast<const uint4*>(base + lds_off(row, chunk));
   return __builtin_bit_cast(bf16x8, v);
 }
+
+// Raw buffer accesses: a 32-bit byte offset against a descriptor whose range
+// is one operand (or one expert's weights). An offset at or beyond the range
+// reads as zeros, which is how pad rows, rows past N and the K tail become
+// zeros without branches.
+constexpr uint32_t kOob = 0x7FFFFFF0u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 struct Params {
   const uint16_t* a;       // GEMM1: x [T, H]; GEMM2: h [cap, I]
@@ -60,13 +86,18 @@ struct Params {
   const int32_t* num_tiles;
   uint16_t* out;           // GEMM1: h [cap, I]; GEMM2: y [A, H]
   int64_t A;
+  uint32_t a_bytes;        // bytes of the token operand (below 2^31)
   int H, I, k;
 };
 
 template <int BM, int BN, int WM, int WN, bool GEMM1>
-__global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(Params p) {
+__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
   using C = Cfg<BM, BN, WM, WN, GEMM1>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
+  constexpr int BK = C::BK;
+  // two separate LDS arrays, so the compiler can tell the stage being filled
+  // by the direct-to-LDS loads from the stage being read
+  __shared__ __attribute__((aligned(1024))) char stage0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage1[C::STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -74,69 +105,77 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(Params p) {
   const int K = GEMM1 ? p.H : p.I;      // reduction length
   const int ntn = (N + BN - 1) / BN;
   const int total = *p.num_tiles * ntn;
-  const int nk = (K + kBK - 1) / kBK;
-  const int chunk = tid & 7;
-  const int lrow = tid >> 3;            // 0..31: row within a 32-row load slab
+  const int nk = (K + BK - 1) / BK;
+  // this lane's place in a direct-to-LDS load: the load writes 64 x 16 bytes
+  // contiguously, i.e. 8 LDS rows; lane l fills physical chunk l % 8 of row l / 8
+  const int g_row = lane >> 3, g_pc = lane & 7;
 
-  for (int task = blockIdx.x; task < total; task += gridDim.x) {
-    const int mt = task / ntn, nt = task - mt * ntn;
+  // XCD-aware slice of the flat task list
+  const int G = gridDim.x;
+  const int xcd = blockIdx.x % kXcds, local = blockIdx.x / kXcds;
+  const int per_xcd = (G + kXcds - 1 - xcd) / kXcds;        // workgroups on this XCD
+  // contiguous slice [t0, t1) of the task list for this XCD, proportional to its workgroups
+  const int64_t t0 = static_cast<int64_t>(total) * (xcd * (G / kXcds) + (xcd < G % kXcds ? xcd : G % kXcds)) / G;
+  const int64_t t1 = static_cast<int64_t>(total) *
+                     ((xcd + 1) * (G / kXcds) + (xcd + 1 < G % kXcds ? xcd + 1 : G % kXcds)) / G;
+
+  for (int64_t task = t0 + local; task < t1; task += per_xcd) {
+    const int mt = static_cast<int>(task / ntn), nt = static_cast<int>(task - static_cast<int64_t>(mt) * ntn);
     const int e = p.tile_expert[mt];
     const int64_t row0 = static_cast<int64_t>(mt) * BM;
     const int n0 = nt * BN;
 
-    // sources of the rows this thread stages
-    const uint16_t* a_src[C::A_LOADS];
-    bool a_ok[C::A_LOADS];
+    // source of every LDS row this lane fills: a byte offset into the token
+    // operand (rows < BM) or into expert e's weights (kOob: zeros)
+    const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(p.a, p.a_bytes);
+    const int wrows = GEMM1 ? 2 * p.I : p.H;           // weight rows of one expert
+    const __amdgpu_buffer_rsrc_t b_rsrc =
+        make_rsrc(p.w + static_cast<int64_t>(e) * wrows * K, static_cast<uint32_t>(wrows) * K * 2);
+    uint32_t off[C::GPW];
+    int kcol[C::GPW];                                   // first K column of this lane's chunk
 #pragma unroll
-    for (int q = 0; q < C::A_LOADS; ++q) {
-      const int r = lrow + 32 * q;
-      if (GEMM1) {
-        const int sid = p.sorted_ids[row0 + r];
-        a_ok[q] = sid < p.A;
-        a_src[q] = p.a + static_cast<int64_t>(a_ok[q] ? sid / p.k : 0) * K;
+    for (int q = 0; q < C::GPW; ++q) {
+      const int row = (wave * C::GPW + q) * 8 + g_row;
+      const int lc = g_pc ^ (row & 7);                  // logical chunk stored at this place
+      kcol[q] = lc * 8;
+      if (row >= C::ROWS) {
+        off[q] = kOob;
+      } else if (row < BM) {
+        int64_t src_row = -1;
+        if (GEMM1) {
+          const int sid = p.sorted_ids[row0 + row];
+          if (sid < p.A) src_row = sid / p.k;
+        } else {
+          src_row = row0 + row;
+        }
+        off[q] = src_row < 0 ? kOob : static_cast<uint32_t>(src_row * K * 2 + lc * 16);
       } else {
-        a_ok[q] = true;
-        a_src[q] = p.a + (row0 + r) * K;
+        const int br = row - BM;
+        int n, wrow;
+        if (GEMM1) {
+          const int half = br >= BN ? 1 : 0;
+          n = n0 + br - half * BN;
+          wrow = half * p.I + n;
+        } else {
+          n = n0 + br;
+          wrow = n;
+        }
+        off[q] = n < N ? static_cast<uint32_t>(wrow) * K * 2 + lc * 16 : kOob;
       }
     }
-    const uint16_t* b_src[C::B_LOADS];
-    bool b_ok[C::B_LOADS];
+    // issue the direct-to-LDS loads of k-step kt into `stage`
+    auto load = [&](char* stage, int kt) {
+      const uint32_t soff = static_cast<uint32_t>(kt) * BK * 2;
 #pragma unroll
-    for (int q = 0; q < C::B_LOADS; ++q) {
-      const int br = lrow + 32 * q;
-      int64_t wrow;
-      int n;
-      if (GEMM1) {
-        const int half = br >= BN ? 1 : 0;
-        n = n0 + br - half * BN;
-        wrow = static_cast<int64_t>(e) * 2 * p.I + half * p.I + n;
-      } else {
-        n = n0 + br;
-        wrow = static_cast<int64_t>(e) * p.H + n;
+      for (int q = 0; q < C::GPW; ++q) {
+        const int grp = wave * C::GPW + q;
+        // chunks past K (the K tail, and the k-steps past the end that the
+        // branch-free pipeline still issues) read as zeros
+        const uint32_t o = kt * BK + kcol[q] < K ? off[q] : kOob;
+        if (C::GROUPS % C::WAVES == 0 || grp < C::GROUPS)   // wave-uniform
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(grp * 8 < BM ? a_rsrc : b_rsrc, (lds_ptr_t)(stage + grp * 1024), 16, o,
+                                                   soff, 0, 0);
       }
-      b_ok[q] = n < N;
-      b_src[q] = p.w + (b_ok[q] ? wrow : 0) * K;
-    }
-
-    uint4 ra[C::A_LOADS], rb[C::B_LOADS];
-    auto load = [&](int kt) {
-      const int col = kt * kBK + chunk * 8;
-      const bool kin = col < K;
-#pragma unroll
-      for (int q = 0; q < C::A_LOADS; ++q)
-        ra[q] = (a_ok[q] && kin) ? *reinterpret_cast<const uint4*>(a_src[q] + col) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-      for (int q = 0; q < C::B_LOADS; ++q)
-        rb[q] = (b_ok[q] && kin) ? *reinterpret_cast<const uint4*>(b_src[q] + col) : make_uint4(0, 0, 0, 0);
-    };
-    auto store = [&](int stage) {
-      char* base = smem + stage * C::STAGE;
-#pragma unroll
-      for (int q = 0; q < C::A_LOADS; ++q)
-        *reinterpret_cast<uint4*>(base + lds_off(lrow + 32 * q, chunk)) = ra[q];
-#pragma unroll
-      for (int q = 0; q < C::B_LOADS; ++q)
-        *reinterpret_cast<uint4*>(base + lds_off(BM + lrow + 32 * q, chunk)) = rb[q];
     };
 
     f32x16 acc[C::HALVES][C::FM][C::FN];
@@ -147,14 +186,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(Params p) {
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) acc[h][i][j] = f32x16{};
 
-    load(0);
-    store(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      if (kt + 1 < nk) load(kt + 1);
-      const char* base = smem + (kt & 1) * C::STAGE;
+    auto compute = [&](const char* base) {
 #pragma unroll
-      for (int kk = 0; kk < kBK / 16; ++kk) {
+      for (int kk = 0; kk < BK / 16; ++kk) {
         const int ch = kk * 2 + (lane >> 5);
         bf16x8 xf[C::FM];
 #pragma unroll
@@ -170,7 +204,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(Params p) {
           }
         }
       }
-      if (kt + 1 < nk) store((kt + 1) & 1);
+    };
+
+    // k-step s+1 streams into one stage while the MFMAs consume k-step s from
+    // the other; the loads are issued first (the scheduling barrier keeps them
+    // there) and must have landed at the barrier that ends the step
+    load(stage0, 0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt += 2) {
+      load(stage1, kt + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(stage0);
+      __syncthreads();
+      load(stage0, kt + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(stage1);
       __syncthreads();
     }
 
@@ -199,7 +247,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(Params p) {
             const float gv = acc[0][i][j][g * 4 + r];
             if (GEMM1) {
               const float uv = acc[C::HALVES - 1][i][j][g * 4 + r];
-              o[r] = gv / (1.0f + expf(-gv)) * uv;
+              o[r] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
             } else {
               o[r] = gv;
             }
@@ -218,6 +266,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(Params p) {
 
 template <int BM, int BN, int WM, int WN, bool GEMM1>
 hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
+  using C = Cfg<BM, BN, WM, WN, GEMM1>;
   Params p;
   p.a = static_cast<const uint16_t*>(g.a);
   p.w = static_cast<const uint16_t*>(g.w);
@@ -226,6 +275,7 @@ hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   p.num_tiles = g.num_tiles;
   p.out = static_cast<uint16_t*>(g.out);
   p.A = g.T * g.k;
+  p.a_bytes = static_cast<uint32_t>((GEMM1 ? g.T * g.H : g.cap * g.I) * 2);
   p.H = g.H;
   p.I = g.I;
   p.k = g.k;
@@ -234,7 +284,7 @@ hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   int64_t grid = dev.num_cus;
   if (grid > max_tasks) grid = max_tasks;
   if (grid < 1) grid = 1;
-  gemm_bf16_kernel<BM, BN, WM, WN, GEMM1><<<static_cast<unsigned>(grid), kThreads, 0, s>>>(p);
+  gemm_bf16_kernel<BM, BN, WM, WN, GEMM1><<<static_cast<unsigned>(grid), C::THREADS, 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -244,18 +294,18 @@ bool gemm_bf16_supports(int block_m) { return block_m == 32 || block_m == 64 || 
 
 hipError_t launch_gemm1_bf16(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   switch (g.block_m) {
-    case 128: return launch<128, 128, 2, 2, true>(g, dev, s);
-    case 64: return launch<64, 128, 2, 2, true>(g, dev, s);
-    case 32: return launch<32, 128, 1, 4, true>(g, dev, s);
+    case 128: return launch<128, 256, 2, 4, true>(g, dev, s);
+    case 64: return launch<64, 256, 1, 8, true>(g, dev, s);
+    case 32: return launch<32, 256, 1, 8, true>(g, dev, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_gemm2_bf16(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   switch (g.block_m) {
-    case 128: return launch<128, 256, 2, 2, false>(g, dev, s);
-    case 64: return launch<64, 256, 2, 2, false>(g, dev, s);
-    case 32: return launch<32, 256, 1, 4, false>(g, dev, s);
+    case 128: return launch<128, 512, 2, 4, false>(g, dev, s);
+    case 64: return launch<64, 512, 1, 8, false>(g, dev, s);
+    case 32: return launch<32, 512, 1, 8, false>(g, dev, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -80,6 +80,12 @@ moe_status_t check_gemm(int32_t dtype, const void* act, const void* act_scale, c
       if (!moe::gemm_mx_supports(block_m)) return MOE_ERR_UNSUPPORTED_SHAPE;
       break;
   }
+  // the kernels address the token operand and one expert's weights with 32-bit
+  // byte offsets
+  const int64_t elt = dtype == MOE_DTYPE_BF16 ? 2 : 1;
+  const int64_t act_bytes = gemm1 ? T * H * elt : cap * I * elt;
+  const int64_t wexp_bytes = (gemm1 ? int64_t{2} * I * H : int64_t{H} * I) * elt;
+  if (act_bytes >= (int64_t{1} << 31) || wexp_bytes >= (int64_t{1} << 31)) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (T == 0) return MOE_OK;
   if (!act || !w || !sorted_ids || !tile_expert || !num_tiles || !out) return MOE_ERR_INVALID_ARG;
   if (!aligned(act, 16) || !aligned(w, 16) || !aligned(out, 16)) return MOE_ERR_INVALID_ARG;
