@@ -99,7 +99,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
   __shared__ __attribute__((aligned(1024))) char stage0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) char stage1[C::STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform across the wave: keep it in a scalar register so
+  // that the LDS destinations and descriptors of the loads are scalar too
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int N = GEMM1 ? p.I : p.H;      // output columns
   const int K = GEMM1 ? p.H : p.I;      // reduction length

@@ -43,7 +43,7 @@ namespace moe {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kXcds = 8;
 constexpr int kFp8Block = 1;
 constexpr int kMx = 2;
 
@@ -54,16 +54,25 @@ struct Cfg {
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / 32, FN = TN / 32;
   static constexpr int HALVES = GEMM1 ? 2 : 1;
-  static constexpr int A_LOADS = BM * 8 / kThreads;         // 16-byte chunks per thread
-  static constexpr int W_CPR = W_BYTES / 16;                // chunks per weight row
-  static constexpr int W_LOADS = B_ROWS * W_CPR / kThreads;
+  static constexpr int WAVES = WM * WN;
+  static constexpr int THREADS = 64 * WAVES;
   static constexpr int A_REGION = BM * 128;
   static constexpr int W_REGION = B_ROWS * W_BYTES;
-  static constexpr int STAGE = A_REGION + W_REGION + (BM + B_ROWS) * 4;
-  static_assert(WM * WN == 4, "4 waves");
+  static constexpr int A_GROUPS = BM / 8;                     // 1 KB direct-to-LDS loads of token rows
+  static constexpr int W_GROUPS = W_REGION / 1024;            // ... of weight rows
+  static constexpr int GROUPS = A_GROUPS + W_GROUPS;
+  static constexpr int GPW = (GROUPS + WAVES - 1) / WAVES;    // data loads per wave per k-step
+  // scale words per k-step: token rows (padded to whole 64-row groups, so that
+  // one load never mixes the two operands), then (MX) weight rows
+  static constexpr int S_TOK = (BM + 63) / 64 * 64;
+  static constexpr int S_ROWS = S_TOK + (MODE == kMx ? B_ROWS : 0);
+  static constexpr int S_GROUPS = (S_ROWS + 63) / 64;         // 256 B direct-to-LDS loads of scale words
+  static constexpr int SPW = (S_GROUPS + WAVES - 1) / WAVES;
+  static constexpr int STAGE = A_REGION + W_REGION + S_GROUPS * 256;
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile is a multiple of 32");
-  static_assert(A_LOADS * kThreads == BM * 8 && W_LOADS * kThreads == B_ROWS * W_CPR, "whole loads");
+  static_assert(BM % 8 == 0 && W_REGION % 1024 == 0, "whole 1 KB load groups");
   static_assert(MODE != kFp8Block || TN <= 128, "a wave's weight rows share one 128x128 scale block");
+  static_assert(2 * STAGE <= 160 * 1024, "two stages fit in LDS");
 };
 
 __device__ __forceinline__ uint32_t a_off(int row, int c) {
@@ -89,6 +98,44 @@ __device__ __forceinline__ i32x8 frag16(const char* p) {
                0, 0, 0, 0};
 }
 
+// Raw buffer accesses: a 32-bit byte offset against a descriptor covering one
+// operand (or one expert's weights); offsets at or past the range read zeros.
+constexpr uint32_t kOob = 0x7FFFFFF0u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Issue the direct-to-LDS loads of k-step kt into `stage`: the token and
+// weight tiles in 1 KB groups (16 bytes a lane), then the k-step's scale words
+// in 256 B groups (4 bytes a lane). k-steps past the end read zeros.
+template <class C>
+__device__ __forceinline__ void issue_loads(char* stage, int kt, int nk, int wave, __amdgpu_buffer_rsrc_t a_rsrc,
+                                            __amdgpu_buffer_rsrc_t w_rsrc, __amdgpu_buffer_rsrc_t as_rsrc,
+                                            __amdgpu_buffer_rsrc_t ws_rsrc, const uint32_t (&doff)[C::GPW],
+                                            const uint32_t (&soff)[C::SPW]) {
+  const bool live = kt < nk;
+#pragma unroll
+  for (int q = 0; q < C::GPW; ++q) {
+    const int g = wave * C::GPW + q;
+    if (C::GROUPS % C::WAVES == 0 || g < C::GROUPS)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(g < C::A_GROUPS ? a_rsrc : w_rsrc, (lds_ptr_t)(stage + g * 1024), 16,
+                                               live ? doff[q] : kOob,
+                                               static_cast<uint32_t>(kt) * (g < C::A_GROUPS ? 128 : C::W_BYTES), 0, 0);
+  }
+#pragma unroll
+  for (int q = 0; q < C::SPW; ++q) {
+    const int g = wave + q * C::WAVES;
+    if (g < C::S_GROUPS)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(g * 64 < C::S_TOK ? as_rsrc : ws_rsrc,
+                                               (lds_ptr_t)(stage + C::A_REGION + C::W_REGION + g * 256), 4,
+                                               live ? soff[q] : kOob, static_cast<uint32_t>(kt) * 4, 0, 0);
+  }
+}
+
 struct Params {
   const uint8_t* a;          // GEMM1: x codes [T, H]; GEMM2: h codes [cap, I]
   const void* a_scale;       // fp32 [rows, K/128] or E8M0 [rows, K/32]
@@ -100,133 +147,121 @@ struct Params {
   void* out;                 // GEMM1: h codes [cap, I]; GEMM2: y bf16 [A, H]
   void* out_scale;           // GEMM1: fp32 [cap, I/128] or E8M0 [cap, I/32]
   int64_t A;
-  int H, I, k;
+  uint32_t a_rows;           // rows of the token operand (T for GEMM1, cap for GEMM2)
+  int E, H, I, k;
 };
 
 template <int BM, int BN, int WM, int WN, bool GEMM1, int MODE>
-__global__ __launch_bounds__(kThreads, 1) void gemm_scaled_kernel(Params p) {
+__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_scaled_kernel(Params p) {
   using C = Cfg<BM, BN, WM, WN, GEMM1, MODE>;
   constexpr int WB = C::W_BYTES;
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
+  // two separate LDS arrays, so the compiler can tell the stage being filled
+  // by the direct-to-LDS loads from the stage being read
+  __shared__ __attribute__((aligned(1024))) char stage0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage1[C::STAGE];
   __shared__ float red[WN][BM];   // per-row partial amax of each n-wave (FP8 requantisation)
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform across the wave: keep it in a scalar register so
+  // that the LDS destinations and descriptors of the loads are scalar too
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const int N = GEMM1 ? p.I : p.H;
   const int K = GEMM1 ? p.H : p.I;
   const int ntn = (N + BN - 1) / BN;
   const int total = *p.num_tiles * ntn;
   const int nk = K / 128;
-  const int wrows_per_expert = GEMM1 ? 2 * p.I : p.H;
-  const int a_chunk = tid & 7, a_lrow = tid >> 3;                    // 32 token rows per slab
-  const int w_chunk = tid % C::W_CPR, w_lrow = tid / C::W_CPR;       // weight rows per slab
-  constexpr int W_SLAB = kThreads / C::W_CPR;
+  const int wrows = GEMM1 ? 2 * p.I : p.H;           // weight rows of one expert
+  const int wrow_bytes = MODE == kMx ? K / 2 : K;
+  const int srow_bytes = MODE == kMx ? K / 32 : (K / 128) * 4;   // scale bytes per token row
 
-  for (int task = blockIdx.x; task < total; task += gridDim.x) {
-    const int mt = task / ntn, nt = task - mt * ntn;
+  // XCD-aware slice of the flat task list
+  const int G = gridDim.x;
+  const int xcd = blockIdx.x % kXcds, local = blockIdx.x / kXcds;
+  const int per_xcd = (G + kXcds - 1 - xcd) / kXcds;
+  const int64_t t0 = static_cast<int64_t>(total) * (xcd * (G / kXcds) + (xcd < G % kXcds ? xcd : G % kXcds)) / G;
+  const int64_t t1 = static_cast<int64_t>(total) *
+                     ((xcd + 1) * (G / kXcds) + (xcd + 1 < G % kXcds ? xcd + 1 : G % kXcds)) / G;
+
+  const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(p.a, p.a_rows * static_cast<uint32_t>(K));
+  const __amdgpu_buffer_rsrc_t as_rsrc = make_rsrc(p.a_scale, p.a_rows * static_cast<uint32_t>(srow_bytes));
+
+  for (int64_t task = t0 + local; task < t1; task += per_xcd) {
+    const int mt = static_cast<int>(task / ntn), nt = static_cast<int>(task - static_cast<int64_t>(mt) * ntn);
     const int e = p.tile_expert[mt];
     const int64_t row0 = static_cast<int64_t>(mt) * BM;
     const int n0 = nt * BN;
+    const __amdgpu_buffer_rsrc_t w_rsrc =
+        make_rsrc(p.w + static_cast<int64_t>(e) * wrows * wrow_bytes, static_cast<uint32_t>(wrows) * wrow_bytes);
+    const __amdgpu_buffer_rsrc_t ws_rsrc =
+        MODE == kMx ? make_rsrc(static_cast<const uint8_t*>(p.w_scale) + static_cast<int64_t>(e) * wrows * (K / 32),
+                                static_cast<uint32_t>(wrows) * (K / 32))
+                    : as_rsrc;
 
-    // token rows staged by this thread
-    const uint8_t* a_src[C::A_LOADS];
-    bool a_ok[C::A_LOADS];
-#pragma unroll
-    for (int q = 0; q < C::A_LOADS; ++q) {
-      const int r = a_lrow + 32 * q;
-      int64_t src_row;
+    // token row r of the tile -> source row of the token operand (-1: pad)
+    auto token_row = [&](int r) -> int64_t {
       if (GEMM1) {
         const int sid = p.sorted_ids[row0 + r];
-        a_ok[q] = sid < p.A;
-        src_row = a_ok[q] ? sid / p.k : 0;
-      } else {
-        a_ok[q] = true;
-        src_row = row0 + r;
+        return sid < p.A ? sid / p.k : -1;
       }
-      a_src[q] = p.a + src_row * K;
-    }
-    // weight rows staged by this thread
-    const uint8_t* w_src[C::W_LOADS];
-    bool w_ok[C::W_LOADS];
-#pragma unroll
-    for (int q = 0; q < C::W_LOADS; ++q) {
-      const int br = w_lrow + W_SLAB * q;
-      int n, off;
+      return row0 + r;
+    };
+    // weight row br of the tile -> row within expert e's weights (-1: past N)
+    auto weight_row = [&](int br) -> int {
       if (GEMM1) {
         const int half = br >= BN ? 1 : 0;
-        n = n0 + br - half * BN;
-        off = half * p.I + n;
-      } else {
-        n = n0 + br;
-        off = n;
+        const int n = n0 + br - half * BN;
+        return n < N ? half * p.I + n : -1;
       }
-      w_ok[q] = n < N;
-      const int64_t wrow = static_cast<int64_t>(e) * wrows_per_expert + (w_ok[q] ? off : 0);
-      w_src[q] = p.w + wrow * (MODE == kMx ? K / 2 : K);
+      const int n = n0 + br;
+      return n < N ? n : -1;
+    };
+
+    // data loads: group g (1 KB) fills 8 token rows (g < A_GROUPS) or 1 KB of
+    // weight rows; lane l writes the 16 bytes at l * 16 of the group
+    uint32_t doff[C::GPW];
+#pragma unroll
+    for (int q = 0; q < C::GPW; ++q) {
+      const int g = wave * C::GPW + q;
+      doff[q] = kOob;
+      if (g < C::A_GROUPS) {
+        const int row = g * 8 + (lane >> 3), pc = lane & 7;
+        const int64_t src = token_row(row);
+        if (src >= 0) doff[q] = static_cast<uint32_t>(src * K + ((pc ^ (row & 7)) << 4));
+      } else if (g < C::GROUPS) {
+        const int byte = (g - C::A_GROUPS) * 1024 + lane * 16;
+        const int br = byte / WB, pc = (byte % WB) / 16;
+        const int lc = WB == 128 ? (pc ^ (br & 7)) : (pc ^ ((br >> 2) & 3));
+        const int wr = weight_row(br);
+        if (wr >= 0) doff[q] = static_cast<uint32_t>(wr) * wrow_bytes + (lc << 4);
+      }
     }
-    // scale words: thread tid < BM stages token row tid; tid < B_ROWS stages weight row tid (MX)
-    int64_t sa_row = -1;
-    if (tid < BM) {
-      if (GEMM1) {
-        const int sid = p.sorted_ids[row0 + tid];
-        sa_row = sid < p.A ? sid / p.k : -1;
-      } else {
-        sa_row = row0 + tid;
+    // scale-word loads: group g (256 B) holds the k-step's scale word of 64
+    // rows: token rows first, then (MX) weight rows
+    uint32_t soff_[C::SPW];
+#pragma unroll
+    for (int q = 0; q < C::SPW; ++q) {
+      const int r = (wave + q * C::WAVES) * 64 + lane;
+      soff_[q] = kOob;
+      if (r < BM) {
+        const int64_t src = token_row(r);
+        if (src >= 0) soff_[q] = static_cast<uint32_t>(src * srow_bytes);
+      } else if (r >= C::S_TOK && r < C::S_ROWS) {
+        const int wr = weight_row(r - C::S_TOK);
+        if (wr >= 0) soff_[q] = static_cast<uint32_t>(wr) * (K / 32);
       }
-    }
-    int64_t sw_row = -1;
-    if (MODE == kMx && tid < C::B_ROWS) {
-      int n, off;
-      if (GEMM1) {
-        const int half = tid >= BN ? 1 : 0;
-        n = n0 + tid - half * BN;
-        off = half * p.I + n;
-      } else {
-        n = n0 + tid;
-        off = n;
-      }
-      if (n < N) sw_row = static_cast<int64_t>(e) * wrows_per_expert + off;
     }
     // FP8: the 128x128 weight-scale block row of each half of this wave's tile
+    // (clamped to the expert's last block where the wave's columns lie past N:
+    // their weight rows read as zeros)
     int64_t wsb[C::HALVES];
 #pragma unroll
     for (int h = 0; h < C::HALVES; ++h) {
-      const int off = (GEMM1 ? h * p.I : 0) + n0 + wn * C::TN;
-      wsb[h] = (static_cast<int64_t>(e) * wrows_per_expert + off) / 128;
+      const int n = n0 + wn * C::TN < N ? n0 + wn * C::TN : N - 1;
+      wsb[h] = (static_cast<int64_t>(e) * wrows + (GEMM1 ? h * p.I : 0) + n) / 128;
     }
 
-    uint4 ra[C::A_LOADS], rw[C::W_LOADS];
-    uint32_t rsa = 0, rsw = 0;
-    auto load = [&](int kt) {
-#pragma unroll
-      for (int q = 0; q < C::A_LOADS; ++q)
-        ra[q] = a_ok[q] ? *reinterpret_cast<const uint4*>(a_src[q] + kt * 128 + a_chunk * 16)
-                        : make_uint4(0, 0, 0, 0);
-#pragma unroll
-      for (int q = 0; q < C::W_LOADS; ++q)
-        rw[q] = w_ok[q] ? *reinterpret_cast<const uint4*>(w_src[q] + kt * WB + w_chunk * 16)
-                        : make_uint4(0, 0, 0, 0);
-      if (MODE == kMx) {
-        rsa = sa_row >= 0 ? reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(p.a_scale) +
-                                                              sa_row * (K / 32))[kt]
-                          : 0x7F7F7F7Fu;
-        rsw = sw_row >= 0 ? reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(p.w_scale) +
-                                                              sw_row * (K / 32))[kt]
-                          : 0x7F7F7F7Fu;
-      } else {
-        rsa = sa_row >= 0 ? __float_as_uint(static_cast<const float*>(p.a_scale)[sa_row * (K / 128) + kt]) : 0u;
-      }
-    };
-    auto store = [&](int stage) {
-      char* base = smem + stage * C::STAGE;
-#pragma unroll
-      for (int q = 0; q < C::A_LOADS; ++q) *reinterpret_cast<uint4*>(base + a_off(a_lrow + 32 * q, a_chunk)) = ra[q];
-#pragma unroll
-      for (int q = 0; q < C::W_LOADS; ++q)
-        *reinterpret_cast<uint4*>(base + C::A_REGION + w_off<WB>(w_lrow + W_SLAB * q, w_chunk)) = rw[q];
-      uint32_t* sc = reinterpret_cast<uint32_t*>(base + C::A_REGION + C::W_REGION);
-      if (tid < BM) sc[tid] = rsa;
-      if (MODE == kMx && tid < C::B_ROWS) sc[BM + tid] = rsw;
+    auto load = [&](char* stage, int kt) {
+      issue_loads<C>(stage, kt, nk, wave, a_rsrc, w_rsrc, as_rsrc, ws_rsrc, doff, soff_);
     };
 
     f32x16 acc[C::HALVES][C::FM][C::FN];
@@ -237,30 +272,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_scaled_kernel(Params p) {
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) acc[h][i][j] = f32x16{};
 
-    load(0);
-    store(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      if (kt + 1 < nk) load(kt + 1);
-      const char* base = smem + (kt & 1) * C::STAGE;
+    auto compute = [&](const char* base, int kt) {
       const uint32_t* sc = reinterpret_cast<const uint32_t*>(base + C::A_REGION + C::W_REGION);
       const int hl = lane >> 5;   // which 32-deep half of a 64-deep MFMA step this lane holds
-
-      // per-lane token scale (FP8: fp32 value; MX: 4 E8M0 bytes)
       uint32_t tsc[C::FM];
 #pragma unroll
       for (int i = 0; i < C::FM; ++i) tsc[i] = sc[wm * C::TM + i * 32 + (lane & 31)];
-      float wsc[C::HALVES];
-      if (MODE == kFp8Block) {
-#pragma unroll
-        for (int h = 0; h < C::HALVES; ++h)
-          wsc[h] = static_cast<const float*>(p.w_scale)[wsb[h] * (K / 128) + kt];
-      }
-
       if (MODE == kMx) {
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          const int blk = 2 * s + hl;                 // 32-element K block of this lane
+          const int blk = 2 * s + hl;                 // 32-element K block of this lane's scales
           i32x8 xf[C::FM];
           int xs[C::FM];
 #pragma unroll
@@ -275,7 +296,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_scaled_kernel(Params p) {
             for (int j = 0; j < C::FN; ++j) {
               const int r = h * BN + wn * C::TN + j * 32 + (lane & 31);
               const i32x8 wf = frag16(base + C::A_REGION + w_off<WB>(r, s * 2 + hl));
-              const int ws = static_cast<int>((sc[BM + r] >> (8 * blk)) & 0xFF);
+              const int ws = static_cast<int>((sc[C::S_TOK + r] >> (8 * blk)) & 0xFF);
 #pragma unroll
               for (int i = 0; i < C::FM; ++i)
                 acc[h][i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf, xf[i], acc[h][i][j], 4, 0, 0, ws,
@@ -284,6 +305,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_scaled_kernel(Params p) {
           }
         }
       } else {
+        float wsc[C::HALVES];
+#pragma unroll
+        for (int h = 0; h < C::HALVES; ++h)
+          wsc[h] = static_cast<const float*>(p.w_scale)[wsb[h] * (K / 128) + kt];
         f32x16 part[C::HALVES][C::FM][C::FN];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
@@ -318,14 +343,28 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_scaled_kernel(Params p) {
               for (int v = 0; v < 16; ++v) acc[h][i][j][v] = __builtin_fmaf(f, part[h][i][j][v], acc[h][i][j][v]);
           }
       }
-      if (kt + 1 < nk) store((kt + 1) & 1);
+    };
+
+    // k-step s+1 streams into one stage while the MFMAs consume k-step s
+    load(stage0, 0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt += 2) {
+      load(stage1, kt + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(stage0, kt);
+      __syncthreads();
+      if (kt + 1 >= nk) break;
+      load(stage0, kt + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(stage1, kt + 1);
       __syncthreads();
     }
 
     // ------------------------------------------------------------ epilogue
     if (GEMM1) {
       // h = silu(g) * u for every accumulator element, then requantise along I
-      float hv[C::FM][C::FN][16];
+      // (h overwrites the gate accumulators in place)
+      f32x16 hv[C::FM][C::FN];
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
@@ -385,6 +424,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_scaled_kernel(Params p) {
             const int x = mx_scale_exponent(am, 8);
             const float inv = mx_inv_scale(x);
             const int nb = n0 + wn * C::TN + j * 32;
+            if (nb >= N) continue;   // a ragged last column tile: whole 32-column fragments past I
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
               const int n = nb + g * 8 + (lane >> 5) * 4;
@@ -422,6 +462,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_scaled_kernel(Params p) {
 
 template <int BM, int BN, int WM, int WN, bool GEMM1, int MODE>
 hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
+  using C = Cfg<BM, BN, WM, WN, GEMM1, MODE>;
   Params p;
   p.a = static_cast<const uint8_t*>(g.a);
   p.a_scale = g.a_scale;
@@ -433,6 +474,8 @@ hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   p.out = g.out;
   p.out_scale = g.out_scale;
   p.A = g.T * g.k;
+  p.a_rows = static_cast<uint32_t>(GEMM1 ? g.T : g.cap);
+  p.E = g.E;
   p.H = g.H;
   p.I = g.I;
   p.k = g.k;
@@ -441,26 +484,43 @@ hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   int64_t grid = dev.num_cus;
   if (grid > max_tasks) grid = max_tasks;
   if (grid < 1) grid = 1;
-  gemm_scaled_kernel<BM, BN, WM, WN, GEMM1, MODE><<<static_cast<unsigned>(grid), kThreads, 0, s>>>(p);
+  gemm_scaled_kernel<BM, BN, WM, WN, GEMM1, MODE><<<static_cast<unsigned>(grid), C::THREADS, 0, s>>>(p);
   return hipGetLastError();
 }
 
-template <int MODE>
-hipError_t launch_gemm1(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
+hipError_t launch_gemm1_mx_tiles(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   switch (g.block_m) {
-    case 128: return launch<128, 128, 2, 2, true, MODE>(g, dev, s);
-    case 64: return launch<64, 128, 2, 2, true, MODE>(g, dev, s);
-    case 32: return launch<32, 128, 1, 4, true, MODE>(g, dev, s);
+    case 128: return launch<128, 256, 4, 2, true, kMx>(g, dev, s);
+    case 64: return launch<64, 256, 1, 8, true, kMx>(g, dev, s);
+    case 32: return launch<32, 256, 1, 8, true, kMx>(g, dev, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <int MODE>
-hipError_t launch_gemm2(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
+hipError_t launch_gemm2_mx_tiles(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   switch (g.block_m) {
-    case 128: return launch<128, 256, 2, 2, false, MODE>(g, dev, s);
-    case 64: return launch<64, 256, 2, 2, false, MODE>(g, dev, s);
-    case 32: return launch<32, 256, 1, 4, false, MODE>(g, dev, s);
+    case 128: return launch<128, 512, 2, 4, false, kMx>(g, dev, s);
+    case 64: return launch<64, 512, 1, 8, false, kMx>(g, dev, s);
+    case 32: return launch<32, 512, 1, 8, false, kMx>(g, dev, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// FP8 keeps four waves: its per-128 promotion holds a second accumulator set
+hipError_t launch_gemm1_fp8_tiles(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
+  switch (g.block_m) {
+    case 128: return launch<128, 128, 2, 2, true, kFp8Block>(g, dev, s);
+    case 64: return launch<64, 128, 2, 2, true, kFp8Block>(g, dev, s);
+    case 32: return launch<32, 128, 1, 4, true, kFp8Block>(g, dev, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_gemm2_fp8_tiles(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
+  switch (g.block_m) {
+    case 128: return launch<128, 256, 2, 2, false, kFp8Block>(g, dev, s);
+    case 64: return launch<64, 256, 2, 2, false, kFp8Block>(g, dev, s);
+    case 32: return launch<32, 256, 1, 4, false, kFp8Block>(g, dev, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -471,16 +531,16 @@ bool gemm_fp8_supports(int block_m) { return block_m == 32 || block_m == 64 || b
 bool gemm_mx_supports(int block_m) { return block_m == 32 || block_m == 64 || block_m == 128; }
 
 hipError_t launch_gemm1_fp8(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
-  return launch_gemm1<kFp8Block>(g, dev, s);
+  return launch_gemm1_fp8_tiles(g, dev, s);
 }
 hipError_t launch_gemm2_fp8(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
-  return launch_gemm2<kFp8Block>(g, dev, s);
+  return launch_gemm2_fp8_tiles(g, dev, s);
 }
 hipError_t launch_gemm1_mx(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
-  return launch_gemm1<kMx>(g, dev, s);
+  return launch_gemm1_mx_tiles(g, dev, s);
 }
 hipError_t launch_gemm2_mx(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
-  return launch_gemm2<kMx>(g, dev, s);
+  return launch_gemm2_mx_tiles(g, dev, s);
 }
 
 }  // namespace moe
