@@ -292,10 +292,11 @@ hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
 
 }  // namespace
 
-bool gemm_bf16_supports(int block_m) { return block_m == 32 || block_m == 64 || block_m == 128; }
+bool gemm_bf16_supports(int block_m) { return block_m == 32 || block_m == 64 || block_m == 128 || block_m == 256; }
 
 hipError_t launch_gemm1_bf16(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   switch (g.block_m) {
+    case 256: return launch<256, 128, 4, 2, true>(g, dev, s);
     case 128: return launch<128, 256, 2, 4, true>(g, dev, s);
     case 64: return launch<64, 256, 1, 8, true>(g, dev, s);
     case 32: return launch<32, 256, 1, 8, true>(g, dev, s);
@@ -305,6 +306,7 @@ hipError_t launch_gemm1_bf16(const GemmArgs& g, const DeviceInfo& dev, hipStream
 
 hipError_t launch_gemm2_bf16(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   switch (g.block_m) {
+    case 256: return launch<256, 256, 4, 2, false>(g, dev, s);
     case 128: return launch<128, 512, 2, 4, false>(g, dev, s);
     case 64: return launch<64, 512, 1, 8, false>(g, dev, s);
     case 32: return launch<32, 512, 1, 8, false>(g, dev, s);

@@ -133,6 +133,9 @@ int32_t moe_pick_block_m(int32_t dtype, int64_t T, int32_t k, int32_t E, int32_t
   if (!valid_dtype(dtype) || T < 0 || k < 1 || E < 1 || k > E || H <= 0 || I <= 0) return -1;
   const int64_t A = T * k;
   const int64_t mean = A / E;  // mean rows per expert
+  // BF16: 256 x 256 workgroup tiles stage the fewest bytes per MFMA once the
+  // experts hold enough rows that the extra padding stays small
+  if (dtype == MOE_DTYPE_BF16 && mean >= 384) return 256;
   if (mean >= 256) return 128;
   if (mean >= 48) return 64;
   return 32;

@@ -79,6 +79,8 @@ SHAPES = [  # T, H, E, k, I, block_m
     (1, 256, 8, 2, 128, 32),
     (300, 2048, 128, 8, 768, 128), # the Qwen3-30B-A3B expert shape at small T
     (200, 200, 8, 3, 40, 64),      # K tails of one 8-column chunk
+    (700, 2048, 8, 4, 768, 256),   # 256-row tiles: several full tiles per expert, ragged last tiles
+    (300, 384, 16, 4, 136, 256),   # 256-row tiles with partial column tiles and a K tail
 ]
 
 
