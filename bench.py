@@ -54,6 +54,97 @@ def _traffic(workload: str, kernel: str, dtype: int):
     return rec.get("bytes_per_launch")
 
 
+# ----------------------------------------------------------------- HBM traffic
+# rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE give KiB per dispatch; each is scaled
+# by what the same counter reads for a plain streaming copy of known size (a
+# torch negation: reads N bytes, writes N bytes), run in the same process.
+COPY_KERNEL_KEY = "neg"
+
+
+def _kernel_role(name: str):
+    """Which GEMM of the path a profiled kernel name is, or None."""
+    if "gemm_bf16_kernel<" not in name and "gemm_scaled_kernel<" not in name:
+        return None
+    args = name.split("<", 1)[1].split(">", 1)[0]
+    return "gemm1_swiglu" if "true" in args else "gemm2_down"
+
+
+def _read_counter(csv_path: str, counter: str):
+    import csv
+    per_kernel = {}
+    for r in csv.DictReader(open(csv_path)):
+        if r["Counter_Name"] != counter:
+            continue
+        per_kernel.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return per_kernel
+
+
+def write_traffic(workload: str, fetch_csv: str, write_csv: str, copy_mib: int, command: str):
+    """Turn two counter passes of `bench.py --copy-probe-mib N` into the
+    per-launch HBM byte records that the roofline object reports."""
+    from workloads import get_config
+    cfg = get_config(workload)
+    fetch, write = _read_counter(fetch_csv, "FETCH_SIZE"), _read_counter(write_csv, "WRITE_SIZE")
+    nbytes = copy_mib << 20
+    copy_f = [v for k, vs in fetch.items() if COPY_KERNEL_KEY in k for v in vs]
+    copy_w = [v for k, vs in write.items() if COPY_KERNEL_KEY in k for v in vs]
+    if not copy_f or not copy_w:
+        raise SystemExit("no copy-probe dispatch in the counter files")
+    f_fac = nbytes / (1024.0 * sum(copy_f) / len(copy_f))
+    w_fac = nbytes / (1024.0 * sum(copy_w) / len(copy_w))
+    out = []
+    for role in ("gemm1_swiglu", "gemm2_down"):
+        fk = [v for k, vs in fetch.items() if _kernel_role(k) == role for v in vs]
+        wk = [v for k, vs in write.items() if _kernel_role(k) == role for v in vs]
+        if not fk or not wk:
+            continue
+        f_kib, w_kib = sum(fk) / len(fk), sum(wk) / len(wk)
+        rec = {"kernel": role, "workload": workload, "src_hash": _src_hash(KERNEL_SRC[role][cfg.dtype]),
+               "fetch_kib_per_launch": round(f_kib, 1), "write_kib_per_launch": round(w_kib, 1),
+               "copy_probe_bytes": nbytes, "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4),
+               "bytes_per_launch": int(f_kib * 1024 * f_fac + w_kib * 1024 * w_fac),
+               "launches": [len(fk), len(wk)], "command": command}
+        path = os.path.join(ROOT, "profiles", f"{role}_{workload}_hbm_traffic.json")
+        with open(path, "w") as fh:
+            json.dump(rec, fh, indent=1)
+        out.append(rec)
+    print(json.dumps(out))
+
+
+def stats_markdown(csv_path: str, title: str, command: str, out_path: str):
+    """A short markdown table of a rocprofv3 --stats kernel summary."""
+    import csv
+
+    def short(n):
+        n = n.replace("moe::(anonymous namespace)::", "").replace("void ", "")
+        depth, out = 0, ""
+        for ch in n:
+            if ch == "(" and depth == 0:
+                break
+            depth += (ch == "<") - (ch == ">")
+            out += ch
+        return out.strip()
+
+    lines = [f"# {title}", "", "Command (run from /tmp on one MI355X, repository at $R):", "", "```", command, "```", "",
+             "Times in microseconds over every dispatch of the run (warm-up steps included).", "",
+             "| kernel | calls | average us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+    for r in csv.DictReader(open(csv_path)):
+        lines.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
+def copy_probe(mib: int):
+    import torch
+    src = torch.ones((mib << 20) // 4, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def cpu_baseline(cfg, inp, budget_s: float = 15.0):
     """The oracle as it stands, timed on this host on a bounded prefix of the
     same batch (same weights, the first T' tokens), scaled to TFLOP/s."""
@@ -97,7 +188,22 @@ def main(argv=None):
     ap.add_argument("--tokens", type=int, default=None, help="override T (parity-size runs)")
     ap.add_argument("--block-m", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="first run a plain streaming copy of this many MiB (HBM counter calibration)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the HBM traffic records from two rocprofv3 counter passes and exit")
+    ap.add_argument("--traffic-command", default="", help="the command that made the profile")
+    ap.add_argument("--stats-md", nargs=3, metavar=("STATS_CSV", "TITLE", "OUT_MD"),
+                    help="write a markdown summary of a rocprofv3 --stats kernel table and exit")
     a = ap.parse_args(argv)
+
+    if a.stats_md:
+        stats_markdown(a.stats_md[0], a.stats_md[1], a.traffic_command, a.stats_md[2])
+        return 0
+    if a.write_traffic:
+        write_traffic(a.workload, a.write_traffic[0], a.write_traffic[1], a.copy_probe_mib or 1024,
+                      a.traffic_command)
+        return 0
 
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the routed forward here is the "
@@ -113,6 +219,8 @@ def main(argv=None):
         cfg = cfg.with_(T=a.tokens)
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if a.copy_probe_mib:
+        copy_probe(a.copy_probe_mib)
     inp = make_inputs(cfg)
     layer = M.MoeLayer(cfg.dtype, inp.w1.to(dev), inp.w2.to(dev), cfg.k, cfg.score)
     x, logits = inp.x.to(dev), inp.logits.to(dev)

@@ -47,8 +47,9 @@ constexpr int kXcds = 8;
 constexpr int kFp8Block = 1;
 constexpr int kMx = 2;
 
-template <int BM, int BN, int WM, int WN, bool GEMM1, int MODE>
+template <int BM, int BN, int WM, int WN, bool GEMM1, int MODE, int NST_ = 2>
 struct Cfg {
+  static constexpr int NST = NST_;                          // LDS stages (2 or 4)
   static constexpr int W_BYTES = MODE == kMx ? 64 : 128;   // weight row bytes per k-step
   static constexpr int B_ROWS = GEMM1 ? 2 * BN : BN;
   static constexpr int TM = BM / WM, TN = BN / WN;
@@ -72,7 +73,9 @@ struct Cfg {
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile is a multiple of 32");
   static_assert(BM % 8 == 0 && W_REGION % 1024 == 0, "whole 1 KB load groups");
   static_assert(MODE != kFp8Block || TN <= 128, "a wave's weight rows share one 128x128 scale block");
-  static_assert(2 * STAGE <= 160 * 1024, "two stages fit in LDS");
+  static_assert(NST == 2 || NST == 4, "double or quadruple buffering");
+  static_assert(NST * STAGE + WN * BM * 4 + (NST > 2 ? 1024 : 0) <= 160 * 1024, "the stages fit in LDS");
+  static_assert((NST - 2) * (GPW + SPW) < 64, "outstanding loads fit the counter");
 };
 
 __device__ __forceinline__ uint32_t a_off(int row, int c) {
@@ -108,31 +111,43 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(4))) const float* const_f32_ptr;   // read-only global memory
 
 // Issue the direct-to-LDS loads of k-step kt into `stage`: the token and
 // weight tiles in 1 KB groups (16 bytes a lane), then the k-step's scale words
-// in 256 B groups (4 bytes a lane). k-steps past the end read zeros.
+// in 256 B groups (4 bytes a lane). k-steps past the end read zeros. With more
+// than two stages every wave issues the same number of loads, GPW + SPW, so
+// that one wait count fits all: a slot without a group loads zeros into
+// `sink`, an LDS area nobody reads.
 template <class C>
-__device__ __forceinline__ void issue_loads(char* stage, int kt, int nk, int wave, __amdgpu_buffer_rsrc_t a_rsrc,
-                                            __amdgpu_buffer_rsrc_t w_rsrc, __amdgpu_buffer_rsrc_t as_rsrc,
-                                            __amdgpu_buffer_rsrc_t ws_rsrc, const uint32_t (&doff)[C::GPW],
-                                            const uint32_t (&soff)[C::SPW]) {
+__device__ __forceinline__ void issue_loads(char* stage, char* sink, int kt, int nk, int wave,
+                                            __amdgpu_buffer_rsrc_t a_rsrc, __amdgpu_buffer_rsrc_t w_rsrc,
+                                            __amdgpu_buffer_rsrc_t as_rsrc, __amdgpu_buffer_rsrc_t ws_rsrc,
+                                            const uint32_t (&doff)[C::GPW], const uint32_t (&soff)[C::SPW]) {
+  constexpr bool kUniform = C::NST > 2;
   const bool live = kt < nk;
 #pragma unroll
   for (int q = 0; q < C::GPW; ++q) {
     const int g = wave * C::GPW + q;
-    if (C::GROUPS % C::WAVES == 0 || g < C::GROUPS)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(g < C::A_GROUPS ? a_rsrc : w_rsrc, (lds_ptr_t)(stage + g * 1024), 16,
-                                               live ? doff[q] : kOob,
-                                               static_cast<uint32_t>(kt) * (g < C::A_GROUPS ? 128 : C::W_BYTES), 0, 0);
+    const bool real = C::GROUPS % C::WAVES == 0 || g < C::GROUPS;
+    if (real || kUniform) {
+      const __amdgpu_buffer_rsrc_t rsrc = g < C::A_GROUPS ? a_rsrc : w_rsrc;
+      char* const dst = real ? stage + g * 1024 : sink;
+      const uint32_t voff = live && real ? doff[q] : kOob;
+      const uint32_t soffset = static_cast<uint32_t>(kt) * (g < C::A_GROUPS ? 128 : C::W_BYTES);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)dst, 16, voff, soffset, 0, 0);
+    }
   }
 #pragma unroll
   for (int q = 0; q < C::SPW; ++q) {
     const int g = wave + q * C::WAVES;
-    if (g < C::S_GROUPS)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(g * 64 < C::S_TOK ? as_rsrc : ws_rsrc,
-                                               (lds_ptr_t)(stage + C::A_REGION + C::W_REGION + g * 256), 4,
-                                               live ? soff[q] : kOob, static_cast<uint32_t>(kt) * 4, 0, 0);
+    const bool real = g < C::S_GROUPS;
+    if (real || kUniform) {
+      const __amdgpu_buffer_rsrc_t rsrc = g * 64 < C::S_TOK ? as_rsrc : ws_rsrc;
+      char* const dst = real ? stage + C::A_REGION + C::W_REGION + g * 256 : sink;
+      const uint32_t voff = live && real ? soff[q] : kOob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)dst, 4, voff, static_cast<uint32_t>(kt) * 4, 0, 0);
+    }
   }
 }
 
@@ -151,14 +166,17 @@ struct Params {
   int E, H, I, k;
 };
 
-template <int BM, int BN, int WM, int WN, bool GEMM1, int MODE>
+template <int BM, int BN, int WM, int WN, bool GEMM1, int MODE, int NST>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_scaled_kernel(Params p) {
-  using C = Cfg<BM, BN, WM, WN, GEMM1, MODE>;
+  using C = Cfg<BM, BN, WM, WN, GEMM1, MODE, NST>;
   constexpr int WB = C::W_BYTES;
-  // two separate LDS arrays, so the compiler can tell the stage being filled
-  // by the direct-to-LDS loads from the stage being read
+  // one LDS array per stage, so that the compiler can tell the stages being
+  // filled by direct-to-LDS loads from the one being read
   __shared__ __attribute__((aligned(1024))) char stage0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) char stage1[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage2[NST > 2 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) char stage3[NST > 2 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) char sink[NST > 2 ? 1024 : 16];   // target of the padding loads
   __shared__ float red[WN][BM];   // per-row partial amax of each n-wave (FP8 requantisation)
 
   // the wave index is uniform across the wave: keep it in a scalar register so
@@ -261,7 +279,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_scaled_kernel(Params p) 
     }
 
     auto load = [&](char* stage, int kt) {
-      issue_loads<C>(stage, kt, nk, wave, a_rsrc, w_rsrc, as_rsrc, ws_rsrc, doff, soff_);
+      issue_loads<C>(stage, sink, kt, nk, wave, a_rsrc, w_rsrc, as_rsrc, ws_rsrc, doff, soff_);
     };
 
     f32x16 acc[C::HALVES][C::FM][C::FN];
@@ -308,7 +326,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_scaled_kernel(Params p) 
         float wsc[C::HALVES];
 #pragma unroll
         for (int h = 0; h < C::HALVES; ++h)
-          wsc[h] = static_cast<const float*>(p.w_scale)[wsb[h] * (K / 128) + kt];
+          // a scalar load (the index is uniform and the scales are read-only
+          // here): it waits on its own counter, not behind the stage loads
+          wsc[h] = ((const_f32_ptr)p.w_scale)[__builtin_amdgcn_readfirstlane(
+              static_cast<int>(wsb[h] * (K / 128) + kt))];
         f32x16 part[C::HALVES][C::FM][C::FN];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
@@ -345,19 +366,59 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_scaled_kernel(Params p) 
       }
     };
 
-    // k-step s+1 streams into one stage while the MFMAs consume k-step s
-    load(stage0, 0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; kt += 2) {
-      load(stage1, kt + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(stage0, kt);
+    if (NST == 2) {
+      // k-step s+1 streams into one stage while the MFMAs consume k-step s
+      load(stage0, 0);
       __syncthreads();
-      if (kt + 1 >= nk) break;
-      load(stage0, kt + 2);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(stage1, kt + 1);
-      __syncthreads();
+      for (int kt = 0; kt < nk; kt += 2) {
+        load(stage1, kt + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(stage0, kt);
+        __syncthreads();
+        if (kt + 1 >= nk) break;
+        load(stage0, kt + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(stage1, kt + 1);
+        __syncthreads();
+      }
+    } else {
+      // four stages (tiles this small are bound by the weight stream, which
+      // wants more bytes in flight): k-step s is read from one stage while
+      // k-steps s+1 .. s+3 stream into the others. Each step waits for its
+      // own stage (the two younger k-steps stay in flight), meets the other
+      // waves, and refills the stage read in the step before with k-step s+3.
+      load(stage0, 0);
+      load(stage1, 1);
+      load(stage2, 2);
+      for (int kt = 0; kt < nk; kt += 4) {
+        wait_vmcnt<2 * (C::GPW + C::SPW)>();
+        barrier_no_fence();
+        load(stage3, kt + 3);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(stage0, kt);
+        if (kt + 1 >= nk) break;
+        wait_vmcnt<2 * (C::GPW + C::SPW)>();
+        barrier_no_fence();
+        load(stage0, kt + 4);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(stage1, kt + 1);
+        if (kt + 2 >= nk) break;
+        wait_vmcnt<2 * (C::GPW + C::SPW)>();
+        barrier_no_fence();
+        load(stage1, kt + 5);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(stage2, kt + 2);
+        if (kt + 3 >= nk) break;
+        wait_vmcnt<2 * (C::GPW + C::SPW)>();
+        barrier_no_fence();
+        load(stage2, kt + 6);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(stage3, kt + 3);
+      }
+      // drain the loads issued past the end (zeros) and meet, before the
+      // epilogue and the next task's loads
+      wait_vmcnt<0>();
+      barrier_no_fence();
     }
 
     // ------------------------------------------------------------ epilogue
@@ -460,9 +521,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_scaled_kernel(Params p) 
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool GEMM1, int MODE>
+template <int BM, int BN, int WM, int WN, bool GEMM1, int MODE, int NST = 2>
 hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
-  using C = Cfg<BM, BN, WM, WN, GEMM1, MODE>;
+  using C = Cfg<BM, BN, WM, WN, GEMM1, MODE, NST>;
   Params p;
   p.a = static_cast<const uint8_t*>(g.a);
   p.a_scale = g.a_scale;
@@ -484,7 +545,7 @@ hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   int64_t grid = dev.num_cus;
   if (grid > max_tasks) grid = max_tasks;
   if (grid < 1) grid = 1;
-  gemm_scaled_kernel<BM, BN, WM, WN, GEMM1, MODE><<<static_cast<unsigned>(grid), C::THREADS, 0, s>>>(p);
+  gemm_scaled_kernel<BM, BN, WM, WN, GEMM1, MODE, NST><<<static_cast<unsigned>(grid), C::THREADS, 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -492,7 +553,7 @@ hipError_t launch_gemm1_mx_tiles(const GemmArgs& g, const DeviceInfo& dev, hipSt
   switch (g.block_m) {
     case 128: return launch<128, 256, 4, 2, true, kMx>(g, dev, s);
     case 64: return launch<64, 256, 1, 8, true, kMx>(g, dev, s);
-    case 32: return launch<32, 256, 1, 8, true, kMx>(g, dev, s);
+    case 32: return launch<32, 256, 1, 8, true, kMx, 4>(g, dev, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -501,26 +562,25 @@ hipError_t launch_gemm2_mx_tiles(const GemmArgs& g, const DeviceInfo& dev, hipSt
   switch (g.block_m) {
     case 128: return launch<128, 512, 2, 4, false, kMx>(g, dev, s);
     case 64: return launch<64, 512, 1, 8, false, kMx>(g, dev, s);
-    case 32: return launch<32, 512, 1, 8, false, kMx>(g, dev, s);
+    case 32: return launch<32, 512, 1, 8, false, kMx, 4>(g, dev, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-// FP8 keeps four waves: its per-128 promotion holds a second accumulator set
 hipError_t launch_gemm1_fp8_tiles(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   switch (g.block_m) {
-    case 128: return launch<128, 128, 2, 2, true, kFp8Block>(g, dev, s);
-    case 64: return launch<64, 128, 2, 2, true, kFp8Block>(g, dev, s);
-    case 32: return launch<32, 128, 1, 4, true, kFp8Block>(g, dev, s);
+    case 128: return launch<128, 128, 2, 4, true, kFp8Block>(g, dev, s);
+    case 64: return launch<64, 128, 2, 4, true, kFp8Block>(g, dev, s);
+    case 32: return launch<32, 128, 1, 4, true, kFp8Block, 4>(g, dev, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_gemm2_fp8_tiles(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   switch (g.block_m) {
-    case 128: return launch<128, 256, 2, 2, false, kFp8Block>(g, dev, s);
-    case 64: return launch<64, 256, 2, 2, false, kFp8Block>(g, dev, s);
-    case 32: return launch<32, 256, 1, 4, false, kFp8Block>(g, dev, s);
+    case 128: return launch<128, 256, 2, 4, false, kFp8Block>(g, dev, s);
+    case 64: return launch<64, 256, 2, 4, false, kFp8Block>(g, dev, s);
+    case 32: return launch<32, 256, 1, 4, false, kFp8Block, 4>(g, dev, s);
     default: return hipErrorInvalidValue;
   }
 }

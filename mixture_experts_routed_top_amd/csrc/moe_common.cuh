@@ -108,4 +108,22 @@ __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
 __device__ __forceinline__ uint32_t lane_id() { return __lane_id(); }
 
+
+// ------------------------------------------------------------------ LDS pipelines
+// Wait until at most N of this wave's vector memory operations are outstanding
+// (loads complete in issue order, so: all but the N most recent loads have
+// landed, in LDS for the direct-to-LDS form) and every LDS read it issued has
+// returned, so that a stage it read may be refilled after the next barrier.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+}
+
+// Workgroup barrier that orders the compiler's memory accesses around it (the
+// clobber) without the release/acquire fences of __syncthreads, whose wait for
+// every outstanding load would also wait for the later pipeline stages.
+__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
+
+
 }  // namespace moe
