@@ -255,6 +255,12 @@ def main(argv=None):
         stage_us[name] = round(1000.0 * sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(a.steps)) / a.steps, 2)
     flops = cfg.flops
     value = flops / (ms / 1e3) / 1e12
+    # per-step distribution, and the compute-only rate (x already quantised:
+    # every stage but quantize_x) next to the end-to-end one
+    steps_ms = sorted(ev[s][0].elapsed_time(ev[s][-1]) for s in range(a.steps))
+    step_stats = {"median": round(steps_ms[len(steps_ms) // 2], 4), "min": round(steps_ms[0], 4),
+                  "p90": round(steps_ms[min(len(steps_ms) - 1, int(0.9 * len(steps_ms)))], 4)}
+    compute_us = sum(v for n, v in stage_us.items() if n != "quantize_x")
 
     # roofline of the dominant kernel (largest average duration)
     dom = max(("gemm1_swiglu", "gemm2_down"), key=lambda n: stage_us[n])
@@ -279,6 +285,8 @@ def main(argv=None):
                    "routing": cfg.routing, "score": "softmax" if cfg.score == 0 else "sigmoid",
                    "numeric_path": DTYPE_NAME[cfg.dtype], "block_m": plan.block_m, "parallelism": "none (1 GPU)"},
         "pct_of_dtype_peak": round(100 * value / peak, 2),
+        "step_ms": step_stats,
+        "compute_tflops": round(flops / (compute_us * 1e-6) / 1e12, 2),
         "stages_us": stage_us,
         "wall_s_timed": round(wall, 4),
         "roofline": roofline,
