@@ -193,6 +193,8 @@ def main(argv=None):
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM traffic records from two rocprofv3 counter passes and exit")
     ap.add_argument("--traffic-command", default="", help="the command that made the profile")
+    ap.add_argument("--sweep", choices=("grid", "tokens"), default=None,
+                    help="throughput sweep, one JSON line per shape: the BF16 parameter grid or the token sweep")
     ap.add_argument("--stats-md", nargs=3, metavar=("STATS_CSV", "TITLE", "OUT_MD"),
                     help="write a markdown summary of a rocprofv3 --stats kernel table and exit")
     a = ap.parse_args(argv)
@@ -211,36 +213,54 @@ def main(argv=None):
         return 2
 
     import torch
-    import mixture_experts_routed_top_amd as M
-    from workloads import get_config, make_inputs
 
-    cfg = get_config(a.workload)
-    if a.tokens:
-        cfg = cfg.with_(T=a.tokens)
-    dev = "cuda:0"
     torch.cuda.set_device(0)
     if a.copy_probe_mib:
         copy_probe(a.copy_probe_mib)
+    if a.sweep:
+        return sweep(a)
+
+    from workloads import get_config, make_inputs
+    cfg = get_config(a.workload)
+    if a.tokens:
+        cfg = cfg.with_(T=a.tokens)
     inp = make_inputs(cfg)
+    rec = measure(cfg, inp, a.steps, a.warmup, a.block_m)
+    base = PAGE_BASELINE.get(cfg.name) if not a.tokens else None
+    rec["vs_baseline"] = round(rec["value"] / base[0], 4) if base else None
+    rec["baseline_ref"] = f"{base[0]} TFLOP/s, {base[1]} (other hardware, context only)" if base else None
+    if not a.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(cfg, inp)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+def measure(cfg, inp, steps: int, warmup: int, block_m=None, data=None) -> dict:
+    """Time `steps` whole forwards of workload cfg on inputs inp (after
+    `warmup` untimed ones) and build the result record."""
+    import torch
+    import mixture_experts_routed_top_amd as M
+
+    dev = "cuda:0"
     layer = M.MoeLayer(cfg.dtype, inp.w1.to(dev), inp.w2.to(dev), cfg.k, cfg.score)
     x, logits = inp.x.to(dev), inp.logits.to(dev)
-    plan = layer.plan(cfg.T, block_m=a.block_m)
+    plan = layer.plan(cfg.T, block_m=block_m)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
     stage_fns = _stage_fns(layer, plan, x, logits)
-    for _ in range(a.warmup):
+    for _ in range(warmup):
         for _, f in stage_fns:
             f()
     torch.cuda.synchronize()
 
     # timed region: K whole forwards; events on the launch stream bracket each stage
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stage_fns) + 1)] for _ in range(a.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stage_fns) + 1)] for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
-    for s in range(a.steps):
+    for s in range(steps):
         ev[s][0].record(stream)
         for i, (_, f) in enumerate(stage_fns):
             f()
@@ -248,16 +268,16 @@ def main(argv=None):
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = start.elapsed_time(end) / a.steps
+    ms = start.elapsed_time(end) / steps
 
     stage_us = {}
     for i, (name, _) in enumerate(stage_fns):
-        stage_us[name] = round(1000.0 * sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(a.steps)) / a.steps, 2)
+        stage_us[name] = round(1000.0 * sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) / steps, 2)
     flops = cfg.flops
     value = flops / (ms / 1e3) / 1e12
     # per-step distribution, and the compute-only rate (x already quantised:
     # every stage but quantize_x) next to the end-to-end one
-    steps_ms = sorted(ev[s][0].elapsed_time(ev[s][-1]) for s in range(a.steps))
+    steps_ms = sorted(ev[s][0].elapsed_time(ev[s][-1]) for s in range(steps))
     step_stats = {"median": round(steps_ms[len(steps_ms) // 2], 4), "min": round(steps_ms[0], 4),
                   "p90": round(steps_ms[min(len(steps_ms) - 1, int(0.9 * len(steps_ms)))], 4)}
     compute_us = sum(v for n, v in stage_us.items() if n != "quantize_x")
@@ -272,15 +292,13 @@ def main(argv=None):
                 "avg_launch_us": stage_us[dom],
                 "algorithmic": f"{4 if dom == 'gemm1_swiglu' else 2}*T*k*H*I = {dom_flops} FLOP per launch"}
 
-    base = PAGE_BASELINE.get(cfg.name) if not a.tokens else None
     rec = {
         "metric": "routed MoE-MLP forward TFLOP/s on 1 MI355X (+% of dtype MFMA peak)",
-        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": round(value / base[0], 4) if base else None,
-        "baseline_ref": f"{base[0]} TFLOP/s, {base[1]} (other hardware, context only)" if base else None,
+        "vs_baseline": None,
         "dtype": "bf16" if cfg.dtype == 0 else ("fp8" if cfg.dtype == 1 else "mxfp4xmxfp8"),
-        "data": "synthetic (seeded N(0,1) tokens, N(0,sigma) bf16 weights, router logits x.Wr)",
+        "data": data or "synthetic (seeded N(0,1) tokens, N(0,sigma) bf16 weights, router logits x.Wr)",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k, "I": cfg.I,
                    "routing": cfg.routing, "score": "softmax" if cfg.score == 0 else "sigmoid",
                    "numeric_path": DTYPE_NAME[cfg.dtype], "block_m": plan.block_m, "parallelism": "none (1 GPU)"},
@@ -293,9 +311,33 @@ def main(argv=None):
     }
     if cfg.dtype == 2:
         rec["pct_of_fp4_peak"] = round(100 * value / PEAK_FP4_TFLOPS, 2)
-    if not a.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(cfg, inp)
-    print(json.dumps(rec), flush=True)
+    return rec
+
+
+def sweep(a) -> int:
+    """One JSON line per shape: the BF16 parameter grid (T=8192, D=I in
+    {2048, 4096}, E in {8..128}, top-K in {1, 2, 4, 8}) or the token sweep of
+    the named BF16 shapes (T = 1024 .. 16384). Inputs drawn on the GPU."""
+    import torch
+    from workloads import P5_GRID, get_config, make_inputs_device
+
+    if a.sweep == "grid":
+        cfgs = [get_config(n) for n in P5_GRID]
+    elif a.sweep == "tokens":
+        cfgs = [get_config(n).with_(T=t) for n in ("qwen3_30b_a3b_bf16", "llama4_scout_bf16")
+                for t in (1024, 2048, 4096, 8192, 16384)]
+    else:
+        raise SystemExit(f"unknown sweep {a.sweep!r}")
+    for cfg in cfgs:
+        inp = make_inputs_device(cfg, "cuda:0")
+        rec = measure(cfg, inp, a.steps, a.warmup,
+                      data="synthetic, drawn on the GPU (seeded torch generator; same distributions)")
+        print(json.dumps({"sweep": a.sweep, "workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k,
+                          "I": cfg.I, "value": rec["value"], "unit": "TFLOP/s", "ms_per_step": rec["ms_per_step"],
+                          "pct_of_dtype_peak": rec["pct_of_dtype_peak"], "block_m": rec["config"]["block_m"],
+                          "stages_us": rec["stages_us"]}), flush=True)
+        del inp, rec
+        torch.cuda.empty_cache()
     return 0
 
 

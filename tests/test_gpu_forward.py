@@ -173,6 +173,13 @@ def test_full_size_bf16_sampled(name):
     _sampled_compare(name, n_experts=4, n_tokens=6)
 
 
+@pytest.mark.parametrize("name", ["grid_d2048_e8_k1", "grid_d2048_e128_k8", "grid_d4096_e16_k4", "grid_d4096_e64_k2"])
+def test_parameter_grid_sampled(name):
+    """Shapes of the BF16 parameter grid (T=8192, D=I, E, top-K), compared
+    like the named workloads."""
+    _sampled_compare(name, n_experts=3, n_tokens=4)
+
+
 @pytest.mark.parametrize("name", ["fp8_block128_share", "mxfp4_moe_t128", "mxfp4_moe_t1024", "mxfp4_moe_t8192",
                                   "mxfp4_moe_t16384"])
 def test_full_size_scaled_sampled(name):

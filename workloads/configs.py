@@ -72,6 +72,22 @@ CONFIGS = {
 }
 
 
+# The parameter grid of Liger-Kernel PR #1463 ("Additional eight-GPU sweeps",
+# H200 parameter grid): T=8192, hidden = intermediate = D in {2048, 4096},
+# E in {8, 16, 32, 64, 128}, top-K in {1, 2, 4, 8} with K < E (38 shapes).
+# BF16, softmax top-K. Run whole on one GPU, each shape has the per-expert
+# GEMM shapes (8192 K / E rows per expert) of one rank's share under expert
+# parallelism.
+P5_GRID = []
+for _d in (2048, 4096):
+    for _e in (8, 16, 32, 64, 128):
+        for _k in (1, 2, 4, 8):
+            if _k < _e:
+                _name = f"grid_d{_d}_e{_e}_k{_k}"
+                CONFIGS[_name] = Config(_name, 10 + len(P5_GRID), 8192, _d, _e, _k, _d, DTYPE_BF16, SCORE_SOFTMAX, 0.02)
+                P5_GRID.append(_name)
+
+
 def get_config(name: str) -> Config:
     try:
         return CONFIGS[name]

@@ -13,6 +13,12 @@ Draws are fp32 and rounded RN to bf16 with torch. Router logits:
   zipf:    fp32( log p_e + G[t, e] ), p_e proportional to (rank_e + 1)^-1.2,
            which makes the top-k a Zipf-weighted draw without replacement
            (Gumbel-top-k).
+
+make_inputs_device draws the same distributions with torch's generator on
+the GPU (seeded from the same SeedSequence) and computes the uniform-routing
+logits in fp32 there: for throughput sweeps over large shapes, where drawing
+gigabytes of weights on the host would dominate. Parity tests use
+make_inputs.
 """
 from __future__ import annotations
 
@@ -101,4 +107,27 @@ def make_inputs(cfg: Config, seed: int = 0, with_weights: bool = True) -> Inputs
     logits = make_logits(cfg, x, seed)
     w1 = _stack_experts(cfg, 2, seed) if with_weights else None
     w2 = _stack_experts(cfg, 3, seed) if with_weights else None
+    return Inputs(cfg, x, logits, w1, w2, seed)
+
+
+def make_inputs_device(cfg: Config, device, seed: int = 0) -> Inputs:
+    """Inputs of the same distributions drawn on `device` (uniform routing;
+    logits = fp32(x . Wr) in fp32 on the device)."""
+    if cfg.routing != "uniform":
+        raise ValueError("make_inputs_device: uniform routing only")
+
+    def gen(tensor_id, index):
+        s = np.random.SeedSequence([cfg.cfg_id, tensor_id, index, seed]).generate_state(1, np.uint64)[0]
+        g = torch.Generator(device=device)
+        g.manual_seed(int(s) & ((1 << 63) - 1))
+        return g
+
+    x = torch.randn((cfg.T, cfg.H), generator=gen(0, cfg.T), device=device).to(torch.bfloat16)
+    wr = (torch.randn((cfg.H, cfg.E), generator=gen(1, 0), device=device) * cfg.wr_std).to(torch.bfloat16)
+    logits = x.float() @ wr.float()
+    w1 = torch.empty((cfg.E, 2 * cfg.I, cfg.H), dtype=torch.bfloat16, device=device)
+    w2 = torch.empty((cfg.E, cfg.H, cfg.I), dtype=torch.bfloat16, device=device)
+    for e in range(cfg.E):
+        w1[e] = (torch.randn((2 * cfg.I, cfg.H), generator=gen(2, e), device=device) * cfg.w_std).to(torch.bfloat16)
+        w2[e] = (torch.randn((cfg.H, cfg.I), generator=gen(3, e), device=device) * cfg.w_std).to(torch.bfloat16)
     return Inputs(cfg, x, logits, w1, w2, seed)
