@@ -22,6 +22,9 @@ Readings where the pages are silent (each listed in the design doc):
   * weights are softmax over the k selected logits (== softmax over all E,
     renormalised over the top k), or sigmoid(logit) without renormalisation;
   * W1 is [E, 2I, H]: gate rows [0, I), up rows [I, 2I); h = silu(gate) * up;
+    with the squared-ReLU activation ([FI5129] Tests run SwiGLU and ReLU2;
+    Measured, the Nemotron shape) the expert is not gated: W1 is [E, I, H]
+    and h = max(g, 0)^2;
   * the top-k weights are applied in the combine, in slot order j = 0..k-1;
   * storage points: h is bf16 (BF16 path), FP8 E4M3 + fp32 1x128 scale along
     I (FP8 path) or E4M3 + E8M0 1x32 along I (MX path); Y and out are bf16.
@@ -41,6 +44,9 @@ SCORE_SIGMOID = 1      # sigmoid(logit), no renormalisation (top-1 gate)
 DTYPE_BF16 = 0
 DTYPE_FP8_BLOCK128 = 1
 DTYPE_MXFP4W_MXFP8A = 2
+
+ACT_SWIGLU = 0         # W1 [E, 2I, H] (gate, up); h = silu(gate) * up
+ACT_RELU2 = 1          # W1 [E, I, H]; h = max(g, 0)^2
 
 
 # ============================================================================ route
@@ -219,6 +225,27 @@ def silu(g: np.ndarray) -> np.ndarray:
     return g / (1.0 + np.exp(-g))
 
 
+def relu2(g: np.ndarray) -> np.ndarray:
+    return np.square(np.maximum(g, 0.0))
+
+
+def _activate(xa: np.ndarray, w1e: np.ndarray, act: int) -> np.ndarray:
+    """The expert's first projection and activation for rows xa.
+
+    SwiGLU: w1e [2I, H], gate rows first. ReLU2: w1e [I, H], no gate."""
+    if act == ACT_SWIGLU:
+        I = w1e.shape[0] // 2
+        return silu(xa @ w1e[:I].T) * (xa @ w1e[I:].T)
+    if act == ACT_RELU2:
+        return relu2(xa @ w1e.T)
+    raise ValueError("unknown activation")
+
+
+def intermediate_size(w1_rows: int, act: int) -> int:
+    """I from the row count of one expert's W1."""
+    return w1_rows // 2 if act == ACT_SWIGLU else w1_rows
+
+
 def _store_h(h: np.ndarray, dtype: int):
     """Storage point of the intermediate (reading listed in the module docstring).
 
@@ -237,18 +264,20 @@ def _store_h(h: np.ndarray, dtype: int):
 
 def grouped_gemm_swiglu(x_hat: np.ndarray, w1_hat: np.ndarray, sorted_ids: np.ndarray,
                         tile_expert: np.ndarray, num_tiles: int, block_m: int, k: int,
-                        dtype: int):
-    """GEMM1 + SwiGLU over the sorted rows, then the h storage point.
+                        dtype: int, act: int = ACT_SWIGLU):
+    """GEMM1 + activation over the sorted rows, then the h storage point.
 
     [TS70] Design, Kernel 1 (L1 GEMM + SwiGLU, quantised intermediate);
-    [FI5129] Description (GEMM1 writes padded expert-sorted rows).
-    x_hat [T, H] and w1_hat [E, 2I, H] are the (dequantised) float64 operands.
-    Sorted row r (r < num_tiles * block_m) holding assignment a < T*k reads
-    token a // k; pad rows read a zero row, so their h is 0.
+    [FI5129] Description (GEMM1 writes padded expert-sorted rows) and Tests
+    (SwiGLU and ReLU2).
+    x_hat [T, H] and w1_hat [E, 2I, H] (SwiGLU) or [E, I, H] (ReLU2) are the
+    (dequantised) float64 operands. Sorted row r (r < num_tiles * block_m)
+    holding assignment a < T*k reads token a // k; pad rows read a zero row,
+    so their h is 0.
     Returns (stored h, float64 value of stored h), both with num_tiles*block_m rows.
     """
-    E, twoI, H = w1_hat.shape
-    I = twoI // 2
+    E, w1_rows, H = w1_hat.shape
+    I = intermediate_size(w1_rows, act)
     A = x_hat.shape[0] * k
     rows = num_tiles * block_m
     h = np.zeros((rows, I), dtype=np.float64)
@@ -259,9 +288,7 @@ def grouped_gemm_swiglu(x_hat: np.ndarray, w1_hat: np.ndarray, sorted_ids: np.nd
         valid = a < A
         xa = np.zeros((block_m, H), dtype=np.float64)
         xa[valid] = x_hat[a[valid] // k]
-        g = xa @ w1_hat[e, :I].T
-        u = xa @ w1_hat[e, I:].T
-        h[r0:r0 + block_m] = silu(g) * u
+        h[r0:r0 + block_m] = _activate(xa, w1_hat[e], act)
     return _store_h(h, dtype)
 
 
@@ -303,19 +330,20 @@ def combine(y: np.ndarray, w: np.ndarray) -> np.ndarray:
 
 # ============================================================================ whole forward
 def moe_forward(logits, x_bf16, w1_bf16, w2_bf16, k: int, score: int, dtype: int,
-                block_m: int = 16, w1_q=None, w2_q=None):
+                block_m: int = 16, w1_q=None, w2_q=None, act: int = ACT_SWIGLU):
     """The whole routed forward for one batch.
 
-    x_bf16 [T, H], w1_bf16 [E, 2I, H], w2_bf16 [E, H, I]: float64 arrays of
-    bf16 values. For the FP8 path x is quantised 1x128 and the weights
-    128x128 (w1_q / w2_q may pass precomputed (codes, scales)); for the MX
-    path x is MXFP8 1x32 and the weights MXFP4 1x32 along K.
+    x_bf16 [T, H], w1_bf16 [E, 2I, H] (SwiGLU) or [E, I, H] (ReLU2),
+    w2_bf16 [E, H, I]: float64 arrays of bf16 values. For the FP8 path x is
+    quantised 1x128 and the weights 128x128 (w1_q / w2_q may pass precomputed
+    (codes, scales)); for the MX path x is MXFP8 1x32 and the weights MXFP4
+    1x32 along K.
     Returns a dict of every intermediate.
     """
     x_bf16 = np.asarray(x_bf16, np.float64)
     T, H = x_bf16.shape
-    E, twoI, _ = w1_bf16.shape
-    I = twoI // 2
+    E, twoI, _ = w1_bf16.shape     # twoI: rows of one expert's W1 (2I, or I for ReLU2)
+    I = intermediate_size(twoI, act)
     ids, w = route(logits, k, score)
     counts, offsets, sorted_ids, tile_expert, num_tiles = align_sort(ids, E, block_m)
     out = {"ids": ids, "w": w, "counts": counts, "offsets": offsets,
@@ -347,36 +375,34 @@ def moe_forward(logits, x_bf16, w1_bf16, w2_bf16, k: int, score: int, dtype: int
     else:
         raise ValueError("unknown dtype")
     (h_store, h_val) = grouped_gemm_swiglu(x_hat, w1_hat, sorted_ids, tile_expert, num_tiles,
-                                           block_m, k, dtype)
+                                           block_m, k, dtype, act)
     y = grouped_gemm_down(h_val, w2_hat, sorted_ids, tile_expert, num_tiles, block_m, T * k)
     out.update(h=h_store, h_val=h_val, y=y, out=combine(y, w))
     return out
 
 
-def routed_flops(T: int, k: int, H: int, I: int) -> int:
-    """Routed FLOPs of one forward: the two grouped GEMMs, 6*T*k*H*I.
+def routed_flops(T: int, k: int, H: int, I: int, act: int = ACT_SWIGLU) -> int:
+    """Routed FLOPs of one forward: the two grouped GEMMs, 6*T*k*H*I for
+    SwiGLU (GEMM1 has 2I outputs per row), 4*T*k*H*I for the ungated ReLU2.
 
     [LIG] MoEBenchmark results: shared experts and attention are not counted;
-    the router projection, SwiGLU and combine are not GEMM work either.
+    the router projection, the activation and combine are not GEMM work either.
     """
-    return 6 * T * k * H * I
+    return (6 if act == ACT_SWIGLU else 4) * T * k * H * I
 
 
-def assignment_forward(x_row, w1e, w2e, dtype: int = DTYPE_BF16):
+def assignment_forward(x_row, w1e, w2e, dtype: int = DTYPE_BF16, act: int = ACT_SWIGLU):
     """One (token, expert) row of Y computed on its own: the same arithmetic as
     grouped_gemm_swiglu + grouped_gemm_down restricted to one assignment.
 
-    x_row [H] dequantised token, w1e [2I, H] and w2e [H, I] the expert's
-    dequantised weights. Returns float64 bf16 values [H]."""
-    w1e = np.asarray(w1e, np.float64)
-    I = w1e.shape[0] // 2
-    g = w1e[:I] @ x_row
-    u = w1e[I:] @ x_row
-    _, hv = _store_h((silu(g) * u)[None, :], dtype)
+    x_row [H] dequantised token, w1e [2I, H] (or [I, H] for ReLU2) and w2e
+    [H, I] the expert's dequantised weights. Returns float64 bf16 values [H]."""
+    hv_raw = _activate(np.asarray(x_row, np.float64)[None, :], np.asarray(w1e, np.float64), act)
+    _, hv = _store_h(hv_raw, dtype)
     return F.round_bf16(np.asarray(w2e, np.float64) @ hv[0])
 
 
-def token_forward(x_row, w1_hat, w2_hat, ids_row, w_row, dtype: int = DTYPE_BF16):
+def token_forward(x_row, w1_hat, w2_hat, ids_row, w_row, dtype: int = DTYPE_BF16, act: int = ACT_SWIGLU):
     """One token's output computed on its own (used for sampled checks at
     full size: same arithmetic as moe_forward restricted to one token).
 
@@ -384,7 +410,7 @@ def token_forward(x_row, w1_hat, w2_hat, ids_row, w_row, dtype: int = DTYPE_BF16
     """
     acc = np.zeros(np.asarray(w2_hat[int(ids_row[0])]).shape[0], dtype=np.float64)
     for j, e in enumerate(ids_row):   # w1_hat / w2_hat: arrays [E, ...] or dicts of experts
-        acc += float(w_row[j]) * assignment_forward(x_row, w1_hat[e], w2_hat[e], dtype)
+        acc += float(w_row[j]) * assignment_forward(x_row, w1_hat[e], w2_hat[e], dtype, act)
     return F.round_bf16(acc)
 
 

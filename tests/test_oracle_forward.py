@@ -193,3 +193,66 @@ def test_token_forward_matches_moe_forward(dtype):
     for t in range(T):
         o = O.token_forward(xh[t], w1h, w2h, r["ids"][t], r["w"][t], dtype)
         np.testing.assert_allclose(o, r["out"][t], rtol=2 ** -7, atol=1e-12)
+
+
+# ------------------------------------------------------------------ squared-ReLU (ungated) experts
+def _relu2_case(T, H, E, k, I, seed, wstd=0.3):
+    rng = np.random.default_rng(seed)
+    x = _bf16(rng.standard_normal((T, H)))
+    w1 = _bf16(rng.standard_normal((E, I, H)) * wstd)
+    w2 = _bf16(rng.standard_normal((E, H, I)) * wstd)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    return x, w1, w2, logits
+
+
+def test_relu2_scalar_brute_force():
+    """Explicit loops: h_n = max(sum_c x_c W1[e, n, c], 0)^2 stored bf16, then
+    y = bf16(sum_n h_n W2[e, :, n]) and the weighted combine."""
+    T, H, E, k, I = 5, 8, 4, 2, 6
+    x, w1, w2, logits = _relu2_case(T, H, E, k, I, seed=21)
+    r = O.moe_forward(logits, x, w1, w2, k, O.SCORE_SOFTMAX, O.DTYPE_BF16, act=O.ACT_RELU2)
+    for t in range(T):
+        order = sorted(range(E), key=lambda e: (-float(logits[t, e]), e))[:k]
+        z = [math.exp(float(logits[t, e]) - float(logits[t, order[0]])) for e in order]
+        w = [float(np.float32(zi / sum(z))) for zi in z]
+        acc = [0.0] * H
+        for j, e in enumerate(order):
+            h = []
+            for n in range(I):
+                g = sum(x[t, c] * w1[e, n, c] for c in range(H))
+                h.append(float(F.round_bf16(np.array([g * g if g > 0 else 0.0]))[0]))
+            for c in range(H):
+                y = float(F.round_bf16(np.array([sum(h[n] * w2[e, c, n] for n in range(I))]))[0])
+                assert abs(r["y"][t * k + j, c] - y) <= 2 ** -7 * abs(y) + 1e-12
+                acc[c] += w[j] * y
+        np.testing.assert_allclose(r["out"][t], F.round_bf16(np.array(acc)), rtol=2 ** -7, atol=1e-12)
+
+
+def test_relu2_e1_k1_equals_dense_relu2_mlp():
+    T, H, I = 16, 64, 32
+    x, w1, w2, logits = _relu2_case(T, H, 1, 1, I, seed=22)
+    r = O.moe_forward(logits, x, w1, w2, 1, O.SCORE_SOFTMAX, O.DTYPE_BF16, act=O.ACT_RELU2)
+    h = torch.relu(torch.from_numpy(x) @ torch.from_numpy(w1[0]).T) ** 2
+    np.testing.assert_allclose(_unsort(r, r["h_val"], T), F.round_bf16(h.numpy()), rtol=2 ** -8, atol=0)
+    y = torch.from_numpy(F.round_bf16(h.numpy())) @ torch.from_numpy(w2[0]).T
+    np.testing.assert_array_equal(r["out"], F.round_bf16(y.numpy()))
+
+
+def test_relu2_negative_preactivations_give_zero_h():
+    # every pre-activation negative: h must be exactly 0 (no leak, no square of a negative)
+    T, H, I = 8, 16, 8
+    x = np.abs(_bf16(np.random.default_rng(3).standard_normal((T, H)))) + 0.5
+    w1 = -np.abs(_bf16(np.random.default_rng(4).standard_normal((1, I, H)))) - 0.25
+    w2 = _bf16(np.random.default_rng(5).standard_normal((1, H, I)))
+    logits = np.zeros((T, 1), np.float32)
+    r = O.moe_forward(logits, x, w1, w2, 1, O.SCORE_SOFTMAX, O.DTYPE_BF16, act=O.ACT_RELU2)
+    assert np.all(r["h_val"] == 0.0) and np.all(r["out"] == 0.0)
+    # and the squared branch: W1 -> -W1 makes every pre-activation positive
+    r2 = O.moe_forward(logits, x, -w1, w2, 1, O.SCORE_SOFTMAX, O.DTYPE_BF16, act=O.ACT_RELU2)
+    g = x @ (-w1[0]).T
+    np.testing.assert_array_equal(_unsort(r2, r2["h_val"], T), F.round_bf16(g * g))
+
+
+def test_relu2_flops():
+    assert O.routed_flops(8192, 6, 2688, 1856, O.ACT_RELU2) == 4 * 8192 * 6 * 2688 * 1856
+    assert O.routed_flops(8192, 6, 2688, 1856) == 6 * 8192 * 6 * 2688 * 1856
