@@ -29,9 +29,10 @@ DTYPE_NAME = {0: "bf16", 1: "fp8_e4m3 (128-block scales)", 2: "mxfp4 weights x m
 # Liger-Kernel PR #1463, MoEBenchmark results, H200, Qwen3-30B-A3B, T=8192, BF16 forward.
 PAGE_BASELINE = {"qwen3_30b_a3b_bf16": (354.38, "H200 1-GPU BF16 forward, Liger-Kernel PR #1463 MoEBenchmark"),
                  "llama4_scout_bf16": (511.36, "H200 1-GPU BF16 forward, Liger-Kernel PR #1463 MoEBenchmark")}
-STAGES = ["route", "align_sort", "quantize_x", "gemm1_swiglu", "gemm2_down", "combine"]
 KERNEL_SRC = {"gemm1_swiglu": {0: "gemm_bf16.hip", 1: "gemm_scaled.hip", 2: "gemm_scaled.hip"},
+              "gemm1_relu2": {0: "gemm_bf16.hip"},
               "gemm2_down": {0: "gemm_bf16.hip", 1: "gemm_scaled.hip", 2: "gemm_scaled.hip"}}
+GEMM1_STAGE = {0: "gemm1_swiglu", 1: "gemm1_relu2"}     # by activation
 
 
 def _src_hash(fname: str) -> str:
@@ -66,7 +67,7 @@ def _kernel_role(name: str):
     if "gemm_bf16_kernel<" not in name and "gemm_scaled_kernel<" not in name:
         return None
     args = name.split("<", 1)[1].split(">", 1)[0]
-    return "gemm1_swiglu" if "true" in args else "gemm2_down"
+    return "gemm1" if "true" in args else "gemm2_down"
 
 
 def _read_counter(csv_path: str, counter: str):
@@ -93,9 +94,11 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str, copy_mib: int, 
     f_fac = nbytes / (1024.0 * sum(copy_f) / len(copy_f))
     w_fac = nbytes / (1024.0 * sum(copy_w) / len(copy_w))
     out = []
-    for role in ("gemm1_swiglu", "gemm2_down"):
+    for role in ("gemm1", "gemm2_down"):
         fk = [v for k, vs in fetch.items() if _kernel_role(k) == role for v in vs]
         wk = [v for k, vs in write.items() if _kernel_role(k) == role for v in vs]
+        if role == "gemm1":
+            role = GEMM1_STAGE[cfg.act]
         if not fk or not wk:
             continue
         f_kib, w_kib = sum(fk) / len(fk), sum(wk) / len(wk)
@@ -164,7 +167,7 @@ def cpu_baseline(cfg, inp, budget_s: float = 15.0):
         logits = inp.logits[:t].numpy()
         x = to_f64(inp.x[:t])
         t0 = time.perf_counter()
-        O.moe_forward(logits, x, w1, w2, cfg.k, cfg.score, cfg.dtype, block_m=16)
+        O.moe_forward(logits, x, w1, w2, cfg.k, cfg.score, cfg.dtype, block_m=16, act=cfg.act)
         return time.perf_counter() - t0
 
     # grow the token prefix until one oracle run takes about budget_s
@@ -173,7 +176,7 @@ def cpu_baseline(cfg, inp, budget_s: float = 15.0):
     while dt < 0.5 * budget_s and t_sample < cfg.T:
         t_sample = int(min(cfg.T, max(t_sample + 1, t_sample * budget_s / max(dt, 1e-3))))
         dt = run(t_sample)
-    flops = 6 * t_sample * cfg.k * cfg.H * cfg.I
+    flops = cfg.flops // cfg.T * t_sample
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"float64 numpy oracle on the first {t_sample} of {cfg.T} tokens of the same batch "
                       f"(same weights), {dt:.2f} s"}
@@ -242,7 +245,7 @@ def measure(cfg, inp, steps: int, warmup: int, block_m=None, data=None) -> dict:
     import mixture_experts_routed_top_amd as M
 
     dev = "cuda:0"
-    layer = M.MoeLayer(cfg.dtype, inp.w1.to(dev), inp.w2.to(dev), cfg.k, cfg.score)
+    layer = M.MoeLayer(cfg.dtype, inp.w1.to(dev), inp.w2.to(dev), cfg.k, cfg.score, cfg.act)
     x, logits = inp.x.to(dev), inp.logits.to(dev)
     plan = layer.plan(cfg.T, block_m=block_m)
     torch.cuda.synchronize()
@@ -283,14 +286,16 @@ def measure(cfg, inp, steps: int, warmup: int, block_m=None, data=None) -> dict:
     compute_us = sum(v for n, v in stage_us.items() if n != "quantize_x")
 
     # roofline of the dominant kernel (largest average duration)
-    dom = max(("gemm1_swiglu", "gemm2_down"), key=lambda n: stage_us[n])
-    dom_flops = (4 if dom == "gemm1_swiglu" else 2) * cfg.T * cfg.k * cfg.H * cfg.I
+    g1 = GEMM1_STAGE[cfg.act]
+    dom = max((g1, "gemm2_down"), key=lambda n: stage_us[n])
+    fl_mult = {"gemm1_swiglu": 4, "gemm1_relu2": 2, "gemm2_down": 2}[dom]
+    dom_flops = fl_mult * cfg.T * cfg.k * cfg.H * cfg.I
     achieved = dom_flops / (stage_us[dom] * 1e-6) / 1e12
     peak = PEAK_TFLOPS[cfg.dtype]
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": _traffic(cfg.name, dom, cfg.dtype),
                 "avg_launch_us": stage_us[dom],
-                "algorithmic": f"{4 if dom == 'gemm1_swiglu' else 2}*T*k*H*I = {dom_flops} FLOP per launch"}
+                "algorithmic": f"{fl_mult}*T*k*H*I = {dom_flops} FLOP per launch"}
 
     rec = {
         "metric": "routed MoE-MLP forward TFLOP/s on 1 MI355X (+% of dtype MFMA peak)",
@@ -354,8 +359,9 @@ def _stage_fns(layer, plan, x, logits):
         a, a_s = plan.xq, plan.xs
     else:
         a, a_s = x, None
-    fns.append(("gemm1_swiglu", lambda: M.moe_grouped_gemm_swiglu(d, a, a_s, layer.w1, layer.w1_scale, plan.sort,
-                                                                    layer.H, layer.I, plan.h, plan.h_scale)))
+    gemm1 = M.moe_grouped_gemm_swiglu if layer.act == M.ACT_SWIGLU else M.moe_grouped_gemm_relu2
+    fns.append((GEMM1_STAGE[layer.act], lambda: gemm1(d, a, a_s, layer.w1, layer.w1_scale, plan.sort,
+                                                      layer.H, layer.I, plan.h, plan.h_scale)))
     fns.append(("gemm2_down", lambda: M.moe_grouped_gemm_down(d, plan.h, plan.h_scale, layer.w2, layer.w2_scale,
                                                                 plan.sort, layer.H, layer.I, plan.y)))
     fns.append(("combine", lambda: M.moe_combine(plan.y, plan.w, plan.out)))

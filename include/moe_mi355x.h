@@ -222,6 +222,28 @@ moe_status_t moe_grouped_gemm_swiglu(int32_t dtype, const void* x, const void* x
                                      void* h, void* h_scale, void* stream);
 
 /*
+ * moe_grouped_gemm_relu2 -- GEMM1 of an ungated expert with the squared-ReLU
+ * activation, over the sorted rows. FlashInfer PR #5129, Tests (the sorted
+ * path runs SwiGLU and ReLU2) and Measured (the Nemotron shape, ReLU2).
+ *
+ * As moe_grouped_gemm_swiglu, except that W1 has one projection per output
+ * column and the activation is a square of the positive part:
+ *   g[r, n] = sum_c x_row[c] * W1[e, n, c]   (fp32 accumulate)
+ *   h[r, n] = bf16( max(g, 0)^2 )
+ *   BF16 only: x [T, H] bf16; W1 [E, I, H] bf16; h [cap, I] bf16; x_scale,
+ *   w1_scale and h_scale are ignored (pass NULL).
+ * Errors as for moe_grouped_gemm_swiglu; dtype other than BF16 ->
+ * MOE_ERR_UNSUPPORTED_SHAPE.
+ */
+moe_status_t moe_grouped_gemm_relu2(int32_t dtype, const void* x, const void* x_scale,
+                                    const void* w1, const void* w1_scale,
+                                    const int32_t* sorted_ids, const int32_t* tile_expert,
+                                    const int32_t* num_tiles,
+                                    int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                                    int32_t block_m, int64_t cap,
+                                    void* h, void* h_scale, void* stream);
+
+/*
  * moe_grouped_gemm_down -- GEMM2 (down projection) over the sorted rows; the
  * epilogue writes each real row to assignment order and drops pad rows.
  * FlashInfer PR #5129, Description (GEMM2 loads its A tiles contiguously and

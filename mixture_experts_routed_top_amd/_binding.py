@@ -25,6 +25,8 @@ MOE_ERR_DEVICE = 4
 DTYPE_BF16 = 0
 DTYPE_FP8_BLOCK128 = 1
 DTYPE_MXFP4W_MXFP8A = 2
+ACT_SWIGLU = 0      # W1 [E, 2I, H] gate + up, h = silu(gate) * up
+ACT_RELU2 = 1       # W1 [E, I, H], h = max(g, 0)^2
 SCORE_SOFTMAX = 0
 SCORE_SIGMOID = 1
 
@@ -41,6 +43,8 @@ SIGNATURES = {
     "moe_quantize_mxfp4": (_I32, [_P, _I64, _I64, _P, _P, _P]),
     "moe_grouped_gemm_swiglu": (_I32, [_I32, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32,
                                        _I32, _I64, _P, _P, _P]),
+    "moe_grouped_gemm_relu2": (_I32, [_I32, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32,
+                                      _I32, _I64, _P, _P, _P]),
     "moe_grouped_gemm_down": (_I32, [_I32, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32,
                                      _I32, _I64, _P, _P]),
     "moe_combine": (_I32, [_P, _P, _I64, _I32, _I32, _P, _P]),
@@ -198,6 +202,17 @@ def moe_grouped_gemm_swiglu(dtype: int, x, x_scale, w1, w1_scale, sort: SortResu
     if h is None:
         h, h_scale = _h_alloc(dtype, max(sort.cap, 1), I, x.device)
     _check("moe_grouped_gemm_swiglu", lib().moe_grouped_gemm_swiglu(
+        dtype, _p(x), _p(x_scale), _p(w1), _p(w1_scale), _p(sort.sorted_ids), _p(sort.tile_expert),
+        _p(sort.num_tiles), sort.T, H, I, sort.E, sort.k, sort.block_m, sort.cap, _p(h), _p(h_scale),
+        _s(stream)))
+    return h, h_scale
+
+
+def moe_grouped_gemm_relu2(dtype: int, x, x_scale, w1, w1_scale, sort: SortResult, H: int, I: int,
+                           h=None, h_scale=None, stream=None):
+    if h is None:
+        h, h_scale = _h_alloc(dtype, max(sort.cap, 1), I, x.device)
+    _check("moe_grouped_gemm_relu2", lib().moe_grouped_gemm_relu2(
         dtype, _p(x), _p(x_scale), _p(w1), _p(w1_scale), _p(sort.sorted_ids), _p(sort.tile_expert),
         _p(sort.num_tiles), sort.T, H, I, sort.E, sort.k, sort.block_m, sort.cap, _p(h), _p(h_scale),
         _s(stream)))

@@ -33,16 +33,18 @@ namespace moe {
 namespace {
 
 constexpr int kXcds = 8;
+constexpr int kActSwiglu = 0;   // h = silu(gate) * up
+constexpr int kActRelu2 = 1;    // h = max(g, 0)^2, one projection
 
-template <int BM, int BN, int WM, int WN, bool GEMM1>
+template <int BM, int BN, int WM, int WN, bool GEMM1, int ACT>
 struct Cfg {
   static constexpr int BK = 64;                       // bf16 per k-step: 128-byte LDS rows
-  static constexpr int B_ROWS = GEMM1 ? 2 * BN : BN;  // weight rows staged per k-step
+  static constexpr int HALVES = GEMM1 && ACT == kActSwiglu ? 2 : 1;   // gate + up, or one projection
+  static constexpr int B_ROWS = HALVES * BN;          // weight rows staged per k-step
   static constexpr int TM = BM / WM;                  // token rows per wave
   static constexpr int TN = BN / WN;                  // output columns per wave
   static constexpr int FM = TM / 32;
   static constexpr int FN = TN / 32;
-  static constexpr int HALVES = GEMM1 ? 2 : 1;
   static constexpr int WAVES = WM * WN;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int ROWS = BM + B_ROWS;            // LDS rows per stage
@@ -80,7 +82,7 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 struct Params {
   const uint16_t* a;       // GEMM1: x [T, H]; GEMM2: h [cap, I]
-  const uint16_t* w;       // GEMM1: W1 [E, 2I, H]; GEMM2: W2 [E, H, I]
+  const uint16_t* w;       // GEMM1: W1 [E, 2I, H] (SwiGLU) or [E, I, H] (ReLU2); GEMM2: W2 [E, H, I]
   const int32_t* sorted_ids;
   const int32_t* tile_expert;
   const int32_t* num_tiles;
@@ -90,9 +92,9 @@ struct Params {
   int H, I, k;
 };
 
-template <int BM, int BN, int WM, int WN, bool GEMM1>
+template <int BM, int BN, int WM, int WN, bool GEMM1, int ACT>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
-  using C = Cfg<BM, BN, WM, WN, GEMM1>;
+  using C = Cfg<BM, BN, WM, WN, GEMM1, ACT>;
   constexpr int BK = C::BK;
   // two separate LDS arrays, so the compiler can tell the stage being filled
   // by the direct-to-LDS loads from the stage being read
@@ -130,7 +132,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
     // source of every LDS row this lane fills: a byte offset into the token
     // operand (rows < BM) or into expert e's weights (kOob: zeros)
     const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(p.a, p.a_bytes);
-    const int wrows = GEMM1 ? 2 * p.I : p.H;           // weight rows of one expert
+    const int wrows = GEMM1 ? C::HALVES * p.I : p.H;   // weight rows of one expert
     const __amdgpu_buffer_rsrc_t b_rsrc =
         make_rsrc(p.w + static_cast<int64_t>(e) * wrows * K, static_cast<uint32_t>(wrows) * K * 2);
     uint32_t off[C::GPW];
@@ -247,9 +249,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float gv = acc[0][i][j][g * 4 + r];
-            if (GEMM1) {
+            if (GEMM1 && ACT == kActSwiglu) {
               const float uv = acc[C::HALVES - 1][i][j][g * 4 + r];
               o[r] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+            } else if (GEMM1) {
+              o[r] = gv > 0.0f ? gv * gv : 0.0f;
             } else {
               o[r] = gv;
             }
@@ -266,9 +270,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool GEMM1>
+template <int BM, int BN, int WM, int WN, bool GEMM1, int ACT = kActSwiglu>
 hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
-  using C = Cfg<BM, BN, WM, WN, GEMM1>;
+  using C = Cfg<BM, BN, WM, WN, GEMM1, ACT>;
   Params p;
   p.a = static_cast<const uint16_t*>(g.a);
   p.w = static_cast<const uint16_t*>(g.w);
@@ -286,7 +290,7 @@ hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   int64_t grid = dev.num_cus;
   if (grid > max_tasks) grid = max_tasks;
   if (grid < 1) grid = 1;
-  gemm_bf16_kernel<BM, BN, WM, WN, GEMM1><<<static_cast<unsigned>(grid), C::THREADS, 0, s>>>(p);
+  gemm_bf16_kernel<BM, BN, WM, WN, GEMM1, ACT><<<static_cast<unsigned>(grid), C::THREADS, 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -300,6 +304,17 @@ hipError_t launch_gemm1_bf16(const GemmArgs& g, const DeviceInfo& dev, hipStream
     case 128: return launch<128, 256, 2, 4, true>(g, dev, s);
     case 64: return launch<64, 256, 1, 8, true>(g, dev, s);
     case 32: return launch<32, 256, 1, 8, true>(g, dev, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// ReLU2: one projection per output column, so the tiles of GEMM2's shape
+hipError_t launch_gemm1_relu2_bf16(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
+  switch (g.block_m) {
+    case 256: return launch<256, 256, 4, 2, true, kActRelu2>(g, dev, s);
+    case 128: return launch<128, 512, 2, 4, true, kActRelu2>(g, dev, s);
+    case 64: return launch<64, 512, 1, 8, true, kActRelu2>(g, dev, s);
+    case 32: return launch<32, 512, 1, 8, true, kActRelu2>(g, dev, s);
     default: return hipErrorInvalidValue;
   }
 }

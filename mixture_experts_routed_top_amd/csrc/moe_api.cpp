@@ -59,7 +59,7 @@ moe_status_t check_gemm(int32_t dtype, const void* act, const void* act_scale, c
                         const void* w_scale, const int32_t* sorted_ids, const int32_t* tile_expert,
                         const int32_t* num_tiles, int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
                         int32_t block_m, int64_t cap, const void* out, const void* out_scale,
-                        bool gemm1) {
+                        bool gemm1, bool gated = true) {
   if (!valid_dtype(dtype)) return MOE_ERR_INVALID_ARG;
   if (T < 0 || H <= 0 || I <= 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > E || k > MOE_MAX_TOPK)
     return MOE_ERR_INVALID_ARG;
@@ -84,7 +84,7 @@ moe_status_t check_gemm(int32_t dtype, const void* act, const void* act_scale, c
   // byte offsets
   const int64_t elt = dtype == MOE_DTYPE_BF16 ? 2 : 1;
   const int64_t act_bytes = gemm1 ? T * H * elt : cap * I * elt;
-  const int64_t wexp_bytes = (gemm1 ? int64_t{2} * I * H : int64_t{H} * I) * elt;
+  const int64_t wexp_bytes = (gemm1 && gated ? int64_t{2} * I * H : int64_t{H} * I) * elt;
   if (act_bytes >= (int64_t{1} << 31) || wexp_bytes >= (int64_t{1} << 31)) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (T == 0) return MOE_OK;
   if (!act || !w || !sorted_ids || !tile_expert || !num_tiles || !out) return MOE_ERR_INVALID_ARG;
@@ -230,6 +230,23 @@ moe_status_t moe_grouped_gemm_swiglu(int32_t dtype, const void* x, const void* x
     case MOE_DTYPE_FP8_BLOCK128: return launched(moe::launch_gemm1_fp8(g, dev, s));
     default: return launched(moe::launch_gemm1_mx(g, dev, s));
   }
+}
+
+moe_status_t moe_grouped_gemm_relu2(int32_t dtype, const void* x, const void* x_scale, const void* w1,
+                                    const void* w1_scale, const int32_t* sorted_ids, const int32_t* tile_expert,
+                                    const int32_t* num_tiles, int64_t T, int32_t H, int32_t I, int32_t E,
+                                    int32_t k, int32_t block_m, int64_t cap, void* h, void* h_scale,
+                                    void* stream) {
+  if (moe_status_t st = check_gemm(dtype, x, x_scale, w1, w1_scale, sorted_ids, tile_expert, num_tiles, T, H,
+                                   I, E, k, block_m, cap, h, h_scale, true, false))
+    return st;
+  if (dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (T == 0) return MOE_OK;
+  moe::DeviceInfo dev;
+  if (moe_status_t st = current_device(&dev)) return st;
+  moe::GemmArgs g{x, x_scale, w1, w1_scale, sorted_ids, tile_expert, num_tiles, h, h_scale,
+                  T, H, I, E, k, block_m, cap};
+  return launched(moe::launch_gemm1_relu2_bf16(g, dev, static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_grouped_gemm_down(int32_t dtype, const void* h, const void* h_scale, const void* w2,

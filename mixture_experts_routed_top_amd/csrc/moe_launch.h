@@ -52,6 +52,7 @@ struct GemmArgs {
 bool gemm_bf16_supports(int block_m);
 hipError_t launch_gemm1_bf16(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s);
 hipError_t launch_gemm2_bf16(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s);
+hipError_t launch_gemm1_relu2_bf16(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s);
 
 bool gemm_fp8_supports(int block_m);
 hipError_t launch_gemm1_fp8(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s);

@@ -1,5 +1,5 @@
 """The routed forward as one object: weights prepared once, buffers planned
-per token count, then route -> align_sort -> [quantise x] -> GEMM1+SwiGLU ->
+per token count, then route -> align_sort -> [quantise x] -> GEMM1+activation ->
 GEMM2 -> combine on one stream with no allocation and no host sync.
 """
 from __future__ import annotations
@@ -30,16 +30,22 @@ class Plan:
 class MoeLayer:
     """Routed-expert MoE MLP forward on one GPU.
 
-    w1: [E, 2I, H] bf16 (gate rows [0, I), up rows [I, 2I)); w2: [E, H, I] bf16.
+    w1: [E, 2I, H] bf16 (gate rows [0, I), up rows [I, 2I)), or [E, I, H] for
+    the ungated squared-ReLU expert (act=ACT_RELU2, BF16 only); w2: [E, H, I] bf16.
     For the FP8 path the weights are quantised here to E4M3 with 128x128 fp32
     block scales, for the MX path to E2M1 with E8M0 per 32 along K (weight
     preparation, outside the timed forward).
     """
 
-    def __init__(self, dtype: int, w1: torch.Tensor, w2: torch.Tensor, k: int, score: int = B.SCORE_SOFTMAX):
+    def __init__(self, dtype: int, w1: torch.Tensor, w2: torch.Tensor, k: int, score: int = B.SCORE_SOFTMAX,
+                 act: int = B.ACT_SWIGLU):
         E, twoI, H = w1.shape
-        self.dtype, self.k, self.score = dtype, k, score
-        self.E, self.H, self.I = E, H, twoI // 2
+        if act not in (B.ACT_SWIGLU, B.ACT_RELU2):
+            raise ValueError("unknown activation")
+        if act == B.ACT_RELU2 and dtype != B.DTYPE_BF16:
+            raise ValueError("the squared-ReLU expert is BF16 only")
+        self.dtype, self.k, self.score, self.act = dtype, k, score, act
+        self.E, self.H, self.I = E, H, (twoI // 2 if act == B.ACT_SWIGLU else twoI)
         if w2.shape != (E, H, self.I):
             raise ValueError("w2 must be [E, H, I]")
         self.w1_scale = self.w2_scale = None
@@ -87,8 +93,9 @@ class MoeLayer:
             a, a_scale = B.moe_quantize_fp8(x, 1, p.xq, p.xs, stream=stream)
         else:
             a, a_scale = B.moe_quantize_mxfp8(x, p.xq, p.xs, stream=stream)
-        B.moe_grouped_gemm_swiglu(self.dtype, a, a_scale, self.w1, self.w1_scale, p.sort, self.H, self.I,
-                                  p.h, p.h_scale, stream=stream)
+        gemm1 = B.moe_grouped_gemm_swiglu if self.act == B.ACT_SWIGLU else B.moe_grouped_gemm_relu2
+        gemm1(self.dtype, a, a_scale, self.w1, self.w1_scale, p.sort, self.H, self.I, p.h, p.h_scale,
+              stream=stream)
         B.moe_grouped_gemm_down(self.dtype, p.h, p.h_scale, self.w2, self.w2_scale, p.sort, self.H, self.I,
                                 p.y, stream=stream)
         return B.moe_combine(p.y, p.w, p.out, stream=stream)

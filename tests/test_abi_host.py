@@ -118,8 +118,12 @@ def _gemm_args(dtype=0, T=64, H=256, I=128, E=8, k=2, bm=32, cap=None, x=FAKE, w
 def test_gemm_host_validation():
     L = _lib()
     sw = lambda *a, **kw: L.moe_grouped_gemm_swiglu(*_gemm_args(*a, **kw), FAKE, FAKE, NULL)
+    r2 = lambda *a, **kw: L.moe_grouped_gemm_relu2(*_gemm_args(*a, **kw), FAKE, FAKE, NULL)
     dn = lambda *a, **kw: L.moe_grouped_gemm_down(*_gemm_args(*a, **kw), FAKE, NULL)
-    for f in (sw, dn):
+    # the squared-ReLU GEMM1 is BF16 only, rejected before anything is enqueued
+    assert r2(dtype=1, H=256, I=128) == 2
+    assert r2(dtype=2, H=256, I=128, T=0, x=NULL, w=NULL) == 2
+    for f in (sw, r2, dn):
         assert f(dtype=5) == 1
         assert f(H=100) == 2                    # bf16 needs H % 8 == 0
         assert f(dtype=1, H=192) == 2           # fp8 needs H % 128 == 0

@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _run(cfg, inp, block_m=None):
-    layer = M.MoeLayer(cfg.dtype, cuda(inp.w1), cuda(inp.w2), cfg.k, cfg.score)
+    layer = M.MoeLayer(cfg.dtype, cuda(inp.w1), cuda(inp.w2), cfg.k, cfg.score, cfg.act)
     plan = layer.plan(cfg.T, block_m=block_m)
     out = layer(cuda(inp.x), cuda(inp.logits), plan)
     torch.cuda.synchronize()
@@ -29,7 +29,7 @@ def _full_compare(cfg, inp, block_m=None):
     say("forward full", cfg.name, cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, block_m)
     layer, plan, out = _run(cfg, inp, block_m)
     ref = O.moe_forward(inp.logits.numpy(), to_f64(inp.x), to_f64(inp.w1), to_f64(inp.w2), cfg.k, cfg.score,
-                        cfg.dtype, block_m=plan.block_m)
+                        cfg.dtype, block_m=plan.block_m, act=cfg.act)
     np.testing.assert_array_equal(plan.ids.cpu().numpy(), ref["ids"])
     np.testing.assert_array_equal(plan.sort.sorted_ids.cpu().numpy()[:len(ref["sorted_ids"])], ref["sorted_ids"])
     got = f64(out)
@@ -141,7 +141,7 @@ def _sampled_compare(name, n_experts=4, rows_per_expert=3, n_tokens=0):
                                                                        replace=False)]))
         w1h, w2h = _oracle_expert(cfg, layer, e, to_f64(inp.w1[e]), to_f64(inp.w2[e]))
         xr = _oracle_tokens(cfg, to_f64(inp.x[torch.from_numpy(pick // cfg.k)]))
-        refs += [O.assignment_forward(xr[i], w1h, w2h, cfg.dtype) for i in range(len(pick))]
+        refs += [O.assignment_forward(xr[i], w1h, w2h, cfg.dtype, cfg.act) for i in range(len(pick))]
         assigned += list(pick)
     got = f64(plan.y[torch.from_numpy(np.array(assigned)).to(out.device)])
     ref = np.stack(refs)
@@ -162,7 +162,7 @@ def _sampled_compare(name, n_experts=4, rows_per_expert=3, n_tokens=0):
         w1 = {e: to_f64(inp.w1[e]) for e in experts}
         w2 = {e: to_f64(inp.w2[e]) for e in experts}
         x = to_f64(inp.x[torch.from_numpy(toks)])
-        ref = np.stack([O.token_forward(x[i], w1, w2, rid[t], rw[t], cfg.dtype) for i, t in enumerate(toks)])
+        ref = np.stack([O.token_forward(x[i], w1, w2, rid[t], rw[t], cfg.dtype, cfg.act) for i, t in enumerate(toks)])
         got = f64(out[torch.from_numpy(toks).to(out.device)])
         assert rel_fro(got, ref) <= TOL_FRO[cfg.dtype]
         assert min_row_cos(got, ref) >= TOL_COS
@@ -171,6 +171,17 @@ def _sampled_compare(name, n_experts=4, rows_per_expert=3, n_tokens=0):
 @pytest.mark.parametrize("name", ["qwen3_30b_a3b_bf16", "qwen3_30b_a3b_bf16_zipf", "llama4_scout_bf16"])
 def test_full_size_bf16_sampled(name):
     _sampled_compare(name, n_experts=4, n_tokens=6)
+
+
+@pytest.mark.parametrize("T,H,E,k,I", [(64, 256, 8, 2, 128), (129, 384, 16, 4, 200), (1, 256, 4, 2, 128),
+                                       (300, 2688, 32, 6, 1856)])
+def test_relu2_forward_small(T, H, E, k, I):
+    cfg = get_config("nemotron_relu2_bf16").with_(T=T, H=H, E=E, k=k, I=I, w_std=0.05)
+    _full_compare(cfg, make_inputs(cfg, seed=T + 7))
+
+
+def test_relu2_full_size_sampled():
+    _sampled_compare("nemotron_relu2_bf16", n_experts=4, n_tokens=6)
 
 
 @pytest.mark.parametrize("name", ["grid_d2048_e8_k1", "grid_d2048_e128_k8", "grid_d4096_e16_k4", "grid_d4096_e64_k2"])

@@ -113,6 +113,34 @@ def test_gemm1_swiglu_bf16(T, H, E, k, I, bm, integer):
 
 @pytest.mark.parametrize("integer", [True, False])
 @pytest.mark.parametrize("T,H,E,k,I,bm", SHAPES)
+def test_gemm1_relu2_bf16(T, H, E, k, I, bm, integer):
+    """The ungated squared-ReLU GEMM1 (W1 [E, I, H])."""
+    x, w1g, _, ids = _problem(T, H, E, k, I, T + 3 * H + I, integer)
+    w1 = np.ascontiguousarray(w1g[:, :I])
+    sort, (sorted_ids, tile_expert, num_tiles) = _sort_from_oracle(ids, E, bm)
+    say("gemm1 relu2 bf16", T, H, E, k, I, bm, integer)
+    h, _ = M.moe_grouped_gemm_relu2(M.DTYPE_BF16, cuda(_bf16(x)), None, cuda(_bf16(w1)), None, sort, H, I)
+    torch.cuda.synchronize()
+    rows = num_tiles * bm
+    (ref, _), _ = O.grouped_gemm_swiglu(x, w1, sorted_ids, tile_expert, num_tiles, bm, k, O.DTYPE_BF16,
+                                        act=O.ACT_RELU2)
+    got = f64(h[:rows])
+    # g: fp32 accumulation of H products, |g' - g| <= dg = H 2^-24 sum|x w|;
+    # h = max(g, 0)^2 then moves by at most (2|g| + dg) dg, plus one fp32
+    # rounding of the square
+    w_both = np.concatenate([w1, w1], axis=1)
+    ga, _ = _abs_sums(x, w_both, sorted_ids, tile_expert, num_tiles, bm, k, rows)
+    gv, _ = _values(x, w_both, sorted_ids, tile_expert, num_tiles, bm, k, rows)
+    dg = H * U32 * ga
+    delta = (2 * np.abs(gv) + dg) * dg + 2 * U32 * gv * gv
+    assert_within_rounding(got, ref, delta, min_exact=0.99)
+    assert np.all(got >= 0)
+    pad = sorted_ids[:rows] == T * k
+    assert np.all(got[pad] == 0)
+
+
+@pytest.mark.parametrize("integer", [True, False])
+@pytest.mark.parametrize("T,H,E,k,I,bm", SHAPES)
 def test_gemm2_down_bf16(T, H, E, k, I, bm, integer):
     x, w1, w2, ids = _problem(T, H, E, k, I, T + 7 * H + I, integer)
     sort, (sorted_ids, tile_expert, num_tiles) = _sort_from_oracle(ids, E, bm)

@@ -16,6 +16,8 @@ DTYPE_FP8_BLOCK128 = 1
 DTYPE_MXFP4W_MXFP8A = 2
 SCORE_SOFTMAX = 0
 SCORE_SIGMOID = 1
+ACT_SWIGLU = 0       # W1 [E, 2I, H]: gate and up
+ACT_RELU2 = 1        # W1 [E, I, H]: one projection, squared ReLU
 
 
 @dataclass(frozen=True)
@@ -32,6 +34,12 @@ class Config:
     w_std: float         # std of W1 / W2 entries
     wr_std: float = 0.02  # std of the router projection
     routing: str = "uniform"   # "uniform" (x . Wr) or "zipf" (Gumbel-top-k, s = 1.2)
+    act: int = ACT_SWIGLU
+
+    @property
+    def w1_rows(self) -> int:
+        """Rows of one expert's W1."""
+        return 2 * self.I if self.act == ACT_SWIGLU else self.I
 
     def with_(self, **kw) -> "Config":
         return replace(self, **kw)
@@ -42,7 +50,7 @@ class Config:
 
     @property
     def flops(self) -> int:
-        return 6 * self.T * self.k * self.H * self.I
+        return (6 if self.act == ACT_SWIGLU else 4) * self.T * self.k * self.H * self.I
 
 
 CONFIGS = {
@@ -69,6 +77,10 @@ CONFIGS = {
                               DTYPE_MXFP4W_MXFP8A, SCORE_SOFTMAX, 0.02),
     "mxfp4_moe_t16384": Config("mxfp4_moe_t16384", 5, 16384, 2560, 512, 10, 640,
                                DTYPE_MXFP4W_MXFP8A, SCORE_SOFTMAX, 0.02),
+    # the Nemotron shape with ungated squared-ReLU experts (FlashInfer PR #5129,
+    # Measured: H=2688, I=1856, 128 experts, top-6, ReLU2; 2048..8192 tokens)
+    "nemotron_relu2_bf16": Config("nemotron_relu2_bf16", 6, 8192, 2688, 128, 6, 1856,
+                                  DTYPE_BF16, SCORE_SOFTMAX, 0.02, act=ACT_RELU2),
 }
 
 

@@ -4,7 +4,8 @@ Recipe (each stream is numpy's default_rng(SeedSequence([cfg_id, tensor_id,
 index, seed]))):
   tensor 0  x   [T, H]  ~ N(0, 1)            index = T
   tensor 1  Wr  [H, E]  ~ N(0, wr_std)       index = 0
-  tensor 2  W1  [E, 2I, H] ~ N(0, w_std)     index = expert (one stream per expert)
+  tensor 2  W1  [E, 2I, H] ~ N(0, w_std)     index = expert (one stream per expert;
+                                              [E, I, H] for the ungated ReLU2 expert)
   tensor 3  W2  [E, H, I]  ~ N(0, w_std)     index = expert
   tensor 4  Gumbel noise [T, E] (Zipf routing only)   index = T
   tensor 5  permutation of expert popularity ranks (Zipf routing only)
@@ -49,14 +50,14 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
 
 
 def make_expert_weights(cfg: Config, tensor_id: int, e: int, seed: int = 0) -> torch.Tensor:
-    """One expert's W1 ([2I, H], tensor_id 2) or W2 ([H, I], tensor_id 3) in bf16."""
-    shape = (2 * cfg.I, cfg.H) if tensor_id == 2 else (cfg.H, cfg.I)
+    """One expert's W1 ([2I or I, H], tensor_id 2) or W2 ([H, I], tensor_id 3) in bf16."""
+    shape = (cfg.w1_rows, cfg.H) if tensor_id == 2 else (cfg.H, cfg.I)
     g = _rng(cfg, tensor_id, e, seed)
     return _bf16(g.standard_normal(shape, dtype=np.float32) * np.float32(cfg.w_std))
 
 
 def _stack_experts(cfg: Config, tensor_id: int, seed: int) -> torch.Tensor:
-    shape = (2 * cfg.I, cfg.H) if tensor_id == 2 else (cfg.H, cfg.I)
+    shape = (cfg.w1_rows, cfg.H) if tensor_id == 2 else (cfg.H, cfg.I)
     out = torch.empty((cfg.E,) + shape, dtype=torch.bfloat16)
 
     def fill(e):
@@ -125,9 +126,9 @@ def make_inputs_device(cfg: Config, device, seed: int = 0) -> Inputs:
     x = torch.randn((cfg.T, cfg.H), generator=gen(0, cfg.T), device=device).to(torch.bfloat16)
     wr = (torch.randn((cfg.H, cfg.E), generator=gen(1, 0), device=device) * cfg.wr_std).to(torch.bfloat16)
     logits = x.float() @ wr.float()
-    w1 = torch.empty((cfg.E, 2 * cfg.I, cfg.H), dtype=torch.bfloat16, device=device)
+    w1 = torch.empty((cfg.E, cfg.w1_rows, cfg.H), dtype=torch.bfloat16, device=device)
     w2 = torch.empty((cfg.E, cfg.H, cfg.I), dtype=torch.bfloat16, device=device)
     for e in range(cfg.E):
-        w1[e] = (torch.randn((2 * cfg.I, cfg.H), generator=gen(2, e), device=device) * cfg.w_std).to(torch.bfloat16)
+        w1[e] = (torch.randn((cfg.w1_rows, cfg.H), generator=gen(2, e), device=device) * cfg.w_std).to(torch.bfloat16)
         w2[e] = (torch.randn((cfg.H, cfg.I), generator=gen(3, e), device=device) * cfg.w_std).to(torch.bfloat16)
     return Inputs(cfg, x, logits, w1, w2, seed)
