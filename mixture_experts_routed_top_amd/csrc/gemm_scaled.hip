@@ -289,6 +289,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_scaled_kernel(Params p) 
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) acc[h][i][j] = f32x16{};
+    // FP8: the scale product acc is expressed in (see compute)
+    float fprev[C::HALVES][C::FM];
+#pragma unroll
+    for (int h = 0; h < C::HALVES; ++h)
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i) fprev[h][i] = 0.0f;
 
     auto compute = [&](const char* base, int kt) {
       const uint32_t* sc = reinterpret_cast<const uint32_t*>(base + C::A_REGION + C::W_REGION);
@@ -330,7 +336,23 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_scaled_kernel(Params p) 
           // here): it waits on its own counter, not behind the stage loads
           wsc[h] = ((const_f32_ptr)p.w_scale)[__builtin_amdgcn_readfirstlane(
               static_cast<int>(wsb[h] * (K / 128) + kt))];
-        f32x16 part[C::HALVES][C::FM][C::FN];
+        // Per-128 promotion without a second accumulator set: acc holds the
+        // sum in units of the current step's scale product f = s_x * s_w, so
+        // each step rescales acc by f_prev / f and adds the unscaled MFMA
+        // products; the epilogue multiplies by the last f. (A pad row has
+        // s_x = 0: its acc stays 0 and its last f is 0.)
+#pragma unroll
+        for (int h = 0; h < C::HALVES; ++h)
+#pragma unroll
+          for (int i = 0; i < C::FM; ++i) {
+            const float f = __uint_as_float(tsc[i]) * wsc[h];
+            const float ratio = f > 0.0f ? fprev[h][i] * __builtin_amdgcn_rcpf(f) : 1.0f;
+            if (f > 0.0f) fprev[h][i] = f;
+#pragma unroll
+            for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+              for (int v = 0; v < 16; ++v) acc[h][i][j][v] *= ratio;
+          }
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
           i32x8 xf[C::FM];
@@ -348,21 +370,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_scaled_kernel(Params p) 
                                       base + C::A_REGION + w_off<WB>(r, s * 4 + 2 + hl));
 #pragma unroll
               for (int i = 0; i < C::FM; ++i)
-                part[h][i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    wf, xf[i], s == 0 ? f32x16{} : part[h][i][j], 0, 0, 0, 127, 0, 127);
+                acc[h][i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf, xf[i], acc[h][i][j], 0, 0, 0,
+                                                                             127, 0, 127);
             }
           }
         }
-#pragma unroll
-        for (int h = 0; h < C::HALVES; ++h)
-#pragma unroll
-          for (int i = 0; i < C::FM; ++i) {
-            const float f = __uint_as_float(tsc[i]) * wsc[h];
-#pragma unroll
-            for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-              for (int v = 0; v < 16; ++v) acc[h][i][j][v] = __builtin_fmaf(f, part[h][i][j][v], acc[h][i][j][v]);
-          }
       }
     };
 
@@ -422,17 +434,19 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_scaled_kernel(Params p) 
     }
 
     // ------------------------------------------------------------ epilogue
+    // (FP8: acc is in units of the last scale product, applied where it is read)
     if (GEMM1) {
       // h = silu(g) * u for every accumulator element, then requantise along I
       // (h overwrites the gate accumulators in place)
-      f32x16 hv[C::FM][C::FN];
+      f32x16 (&hv)[C::FM][C::FN] = acc[0];
 #pragma unroll
       for (int i = 0; i < C::FM; ++i)
 #pragma unroll
         for (int j = 0; j < C::FN; ++j)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const float g = acc[0][i][j][v], u = acc[C::HALVES - 1][i][j][v];
+            const float g = acc[0][i][j][v] * (MODE == kFp8Block ? fprev[0][i] : 1.0f);
+            const float u = acc[C::HALVES - 1][i][j][v] * (MODE == kFp8Block ? fprev[C::HALVES - 1][i] : 1.0f);
             hv[i][j][v] = g / (1.0f + expf(-g)) * u;
           }
       uint8_t* hq = static_cast<uint8_t*>(p.out);
@@ -504,6 +518,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_scaled_kernel(Params p) 
         const int m = wm * C::TM + i * 32 + (lane & 31);
         const int sid = p.sorted_ids[row0 + m];
         if (sid >= p.A) continue;
+        const float fs = MODE == kFp8Block ? fprev[0][i] : 1.0f;
 #pragma unroll
         for (int j = 0; j < C::FN; ++j)
 #pragma unroll
@@ -511,8 +526,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_scaled_kernel(Params p) 
             const int n = n0 + wn * C::TN + j * 32 + g * 8 + (lane >> 5) * 4;
             if (n < N) {
               uint2 st;
-              st.x = pack_bf16x2(acc[0][i][j][4 * g], acc[0][i][j][4 * g + 1]);
-              st.y = pack_bf16x2(acc[0][i][j][4 * g + 2], acc[0][i][j][4 * g + 3]);
+              st.x = pack_bf16x2(acc[0][i][j][4 * g] * fs, acc[0][i][j][4 * g + 1] * fs);
+              st.y = pack_bf16x2(acc[0][i][j][4 * g + 2] * fs, acc[0][i][j][4 * g + 3] * fs);
               *reinterpret_cast<uint2*>(y + static_cast<int64_t>(sid) * N + n) = st;
             }
           }
@@ -551,6 +566,7 @@ hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
 
 hipError_t launch_gemm1_mx_tiles(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   switch (g.block_m) {
+    case 256: return launch<256, 128, 4, 2, true, kMx>(g, dev, s);
     case 128: return launch<128, 256, 4, 2, true, kMx>(g, dev, s);
     case 64: return launch<64, 256, 1, 8, true, kMx>(g, dev, s);
     case 32: return launch<32, 256, 1, 8, true, kMx, 4>(g, dev, s);
@@ -560,6 +576,7 @@ hipError_t launch_gemm1_mx_tiles(const GemmArgs& g, const DeviceInfo& dev, hipSt
 
 hipError_t launch_gemm2_mx_tiles(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   switch (g.block_m) {
+    case 256: return launch<256, 256, 4, 2, false, kMx>(g, dev, s);
     case 128: return launch<128, 512, 2, 4, false, kMx>(g, dev, s);
     case 64: return launch<64, 512, 1, 8, false, kMx>(g, dev, s);
     case 32: return launch<32, 512, 1, 8, false, kMx, 4>(g, dev, s);
@@ -569,6 +586,7 @@ hipError_t launch_gemm2_mx_tiles(const GemmArgs& g, const DeviceInfo& dev, hipSt
 
 hipError_t launch_gemm1_fp8_tiles(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   switch (g.block_m) {
+    case 256: return launch<256, 128, 4, 2, true, kFp8Block>(g, dev, s);
     case 128: return launch<128, 128, 2, 4, true, kFp8Block>(g, dev, s);
     case 64: return launch<64, 128, 2, 4, true, kFp8Block>(g, dev, s);
     case 32: return launch<32, 128, 1, 4, true, kFp8Block, 4>(g, dev, s);
@@ -578,6 +596,7 @@ hipError_t launch_gemm1_fp8_tiles(const GemmArgs& g, const DeviceInfo& dev, hipS
 
 hipError_t launch_gemm2_fp8_tiles(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   switch (g.block_m) {
+    case 256: return launch<256, 128, 4, 2, false, kFp8Block>(g, dev, s);
     case 128: return launch<128, 256, 2, 4, false, kFp8Block>(g, dev, s);
     case 64: return launch<64, 256, 2, 4, false, kFp8Block>(g, dev, s);
     case 32: return launch<32, 256, 1, 4, false, kFp8Block, 4>(g, dev, s);
@@ -587,8 +606,8 @@ hipError_t launch_gemm2_fp8_tiles(const GemmArgs& g, const DeviceInfo& dev, hipS
 
 }  // namespace
 
-bool gemm_fp8_supports(int block_m) { return block_m == 32 || block_m == 64 || block_m == 128; }
-bool gemm_mx_supports(int block_m) { return block_m == 32 || block_m == 64 || block_m == 128; }
+bool gemm_fp8_supports(int block_m) { return block_m == 32 || block_m == 64 || block_m == 128 || block_m == 256; }
+bool gemm_mx_supports(int block_m) { return block_m == 32 || block_m == 64 || block_m == 128 || block_m == 256; }
 
 hipError_t launch_gemm1_fp8(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   return launch_gemm1_fp8_tiles(g, dev, s);

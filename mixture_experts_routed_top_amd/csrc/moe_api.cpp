@@ -136,6 +136,7 @@ int32_t moe_pick_block_m(int32_t dtype, int64_t T, int32_t k, int32_t E, int32_t
   // BF16: 256 x 256 workgroup tiles stage the fewest bytes per MFMA once the
   // experts hold enough rows that the extra padding stays small
   if (dtype == MOE_DTYPE_BF16 && mean >= 384) return 256;
+  if (dtype == MOE_DTYPE_FP8_BLOCK128 && mean >= 768) return 256;
   if (mean >= 256) return 128;
   if (mean >= 48) return 64;
   return 32;

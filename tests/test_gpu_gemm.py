@@ -229,6 +229,7 @@ SCALED_SHAPES = [  # T, H, E, k, I, block_m
     (129, 384, 16, 4, 256, 64),
     (300, 1024, 32, 8, 512, 128),
     (1, 256, 4, 2, 128, 32),
+    (700, 1024, 8, 4, 384, 256),   # 256-row tiles: full and ragged tiles, partial column tiles
 ]
 
 
