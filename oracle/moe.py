@@ -26,6 +26,10 @@ Readings where the pages are silent (each listed in the design doc):
     Measured, the Nemotron shape) the expert is not gated: W1 is [E, I, H]
     and h = max(g, 0)^2;
   * the top-k weights are applied in the combine, in slot order j = 0..k-1;
+  * shared experts (folded into the compute in the GC-MoE Abstract; fused
+    shared-expert execution in [TS70] Summary) are S further experts every
+    token uses, after its k routed slots, with weight 1 and no gate: expert
+    ids E..E+S-1 (W1/W2 carry them as their last S experts), slots k..k+S-1;
   * storage points: h is bf16 (BF16 path), FP8 E4M3 + fp32 1x128 scale along
     I (FP8 path) or E4M3 + E8M0 1x32 along I (MX path); Y and out are bf16.
 Everything between two storage points is float64.
@@ -76,6 +80,18 @@ def route(logits: np.ndarray, k: int, score: int = SCORE_SOFTMAX):
     else:
         raise ValueError("route: unknown score function")
     return ids, F.round_fp32(w).astype(np.float32)
+
+
+def route_with_shared(logits: np.ndarray, k: int, score: int, n_shared: int):
+    """Routing plus S shared experts: the top-k slots of `route` over the E
+    routed logits, then slots k..k+S-1 holding experts E..E+S-1 with weight 1.
+
+    Returns ids int32 [T, k+S], w fp32 [T, k+S]."""
+    ids, w = route(logits, k, score)
+    T, E = np.asarray(logits).shape
+    sid = np.broadcast_to(np.arange(E, E + n_shared, dtype=np.int32), (T, n_shared))
+    return (np.concatenate([ids, sid], axis=1).astype(np.int32),
+            np.concatenate([w, np.ones((T, n_shared), np.float32)], axis=1))
 
 
 # ============================================================================ align / sort
@@ -330,11 +346,12 @@ def combine(y: np.ndarray, w: np.ndarray) -> np.ndarray:
 
 # ============================================================================ whole forward
 def moe_forward(logits, x_bf16, w1_bf16, w2_bf16, k: int, score: int, dtype: int,
-                block_m: int = 16, w1_q=None, w2_q=None, act: int = ACT_SWIGLU):
+                block_m: int = 16, w1_q=None, w2_q=None, act: int = ACT_SWIGLU, n_shared: int = 0):
     """The whole routed forward for one batch.
 
     x_bf16 [T, H], w1_bf16 [E, 2I, H] (SwiGLU) or [E, I, H] (ReLU2),
-    w2_bf16 [E, H, I]: float64 arrays of bf16 values. For the FP8 path x is
+    w2_bf16 [E, H, I]: float64 arrays of bf16 values; with n_shared = S > 0
+    the last S experts of w1/w2 are shared (logits cover the E - S routed ones). For the FP8 path x is
     quantised 1x128 and the weights 128x128 (w1_q / w2_q may pass precomputed
     (codes, scales)); for the MX path x is MXFP8 1x32 and the weights MXFP4
     1x32 along K.
@@ -344,7 +361,11 @@ def moe_forward(logits, x_bf16, w1_bf16, w2_bf16, k: int, score: int, dtype: int
     T, H = x_bf16.shape
     E, twoI, _ = w1_bf16.shape     # twoI: rows of one expert's W1 (2I, or I for ReLU2)
     I = intermediate_size(twoI, act)
-    ids, w = route(logits, k, score)
+    if n_shared:
+        ids, w = route_with_shared(logits, k, score, n_shared)
+        k = k + n_shared
+    else:
+        ids, w = route(logits, k, score)
     counts, offsets, sorted_ids, tile_expert, num_tiles = align_sort(ids, E, block_m)
     out = {"ids": ids, "w": w, "counts": counts, "offsets": offsets,
            "sorted_ids": sorted_ids, "tile_expert": tile_expert, "num_tiles": num_tiles}

@@ -256,3 +256,58 @@ def test_relu2_negative_preactivations_give_zero_h():
 def test_relu2_flops():
     assert O.routed_flops(8192, 6, 2688, 1856, O.ACT_RELU2) == 4 * 8192 * 6 * 2688 * 1856
     assert O.routed_flops(8192, 6, 2688, 1856) == 6 * 8192 * 6 * 2688 * 1856
+
+
+# ------------------------------------------------------------------ shared experts
+def test_route_with_shared_appends_fixed_slots():
+    logits = np.random.default_rng(0).standard_normal((7, 6)).astype(np.float32)
+    ids, w = O.route_with_shared(logits, 2, O.SCORE_SOFTMAX, 3)
+    rid, rw = O.route(logits, 2, O.SCORE_SOFTMAX)
+    assert ids.shape == (7, 5) and w.shape == (7, 5)
+    np.testing.assert_array_equal(ids[:, :2], rid)
+    np.testing.assert_array_equal(w[:, :2], rw)
+    np.testing.assert_array_equal(ids[:, 2:], np.tile([6, 7, 8], (7, 1)))
+    assert np.all(w[:, 2:] == 1.0)
+
+
+def test_shared_expert_adds_a_dense_mlp():
+    """out = bf16( sum_j w_j y_j + y_shared ), y_shared = bf16 of the dense
+    SwiGLU MLP of the shared weights (torch float64), y_j the routed rows."""
+    T, H, E, k, I = 12, 32, 5, 2, 16
+    x, w1, w2, logits = _case(T, H, E + 1, k, I, seed=31)
+    logits = np.ascontiguousarray(logits[:, :E])     # the router scores the E routed experts only
+    routed = O.moe_forward(logits, x, w1[:E], w2[:E], k, O.SCORE_SOFTMAX, O.DTYPE_BF16)
+    shared = O.moe_forward(logits, x, w1, w2, k, O.SCORE_SOFTMAX, O.DTYPE_BF16, n_shared=1)
+    xt = torch.from_numpy(x)
+    hs = torch.nn.functional.silu(xt @ torch.from_numpy(w1[E, :I]).T) * (xt @ torch.from_numpy(w1[E, I:]).T)
+    ys = F.round_bf16((torch.from_numpy(F.round_bf16(hs.numpy())) @ torch.from_numpy(w2[E]).T).numpy())
+    yr = routed["y"].reshape(T, k, H)
+    w = routed["w"].astype(np.float64)
+    expect = F.round_bf16((w[:, :, None] * yr).sum(1) + ys)
+    np.testing.assert_array_equal(shared["y"].reshape(T, k + 1, H)[:, :k], yr)
+    np.testing.assert_array_equal(shared["y"].reshape(T, k + 1, H)[:, k], ys)
+    np.testing.assert_array_equal(shared["out"], expect)
+
+
+def test_wide_shared_expert_equals_two_narrow_ones():
+    # a shared expert of width 2I is two of width I (its intermediate columns
+    # split in two) up to the bf16 rounding of each half's Y row
+    T, H, E, k, I = 10, 32, 4, 2, 8
+    x, w1, w2, logits = _case(T, H, E, k, I, seed=32)
+    rng = np.random.default_rng(33)
+    g = _bf16(rng.standard_normal((2 * I, H)) * 0.3)
+    u = _bf16(rng.standard_normal((2 * I, H)) * 0.3)
+    d = _bf16(rng.standard_normal((H, 2 * I)) * 0.3)
+    # one layer holds one I: the routed experts are zero-padded to width 2I there
+    pad = lambda a, axis: np.concatenate([a, np.zeros_like(a)], axis=axis)
+    w1r = np.concatenate([pad(w1[:, :I], 1), pad(w1[:, I:], 1)], axis=1)    # routed, zero-padded to 2I
+    w2r = pad(w2, 2)
+    wide_w1 = np.concatenate([w1r, np.concatenate([g, u])[None]], axis=0)
+    wide_w2 = np.concatenate([w2r, d[None]], axis=0)
+    a = O.moe_forward(logits, x, wide_w1, wide_w2, k, O.SCORE_SOFTMAX, O.DTYPE_BF16, n_shared=1)
+    halves_w1 = np.stack([np.concatenate([g[:I], u[:I]]), np.concatenate([g[I:], u[I:]])])
+    halves_w2 = np.stack([d[:, :I], d[:, I:]])
+    narrow_w1 = np.concatenate([w1, halves_w1], axis=0)
+    narrow_w2 = np.concatenate([w2, halves_w2], axis=0)
+    b = O.moe_forward(logits, x, narrow_w1, narrow_w2, k, O.SCORE_SOFTMAX, O.DTYPE_BF16, n_shared=2)
+    np.testing.assert_allclose(b["out"], a["out"], rtol=2 ** -6, atol=2 ** -6)   # one bf16 step of O(1) values
