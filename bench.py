@@ -167,7 +167,7 @@ def cpu_baseline(cfg, inp, budget_s: float = 15.0):
         logits = inp.logits[:t].numpy()
         x = to_f64(inp.x[:t])
         t0 = time.perf_counter()
-        O.moe_forward(logits, x, w1, w2, cfg.k, cfg.score, cfg.dtype, block_m=16, act=cfg.act)
+        O.moe_forward(logits, x, w1, w2, cfg.k, cfg.score, cfg.dtype, block_m=16, act=cfg.act, n_shared=cfg.n_shared)
         return time.perf_counter() - t0
 
     # grow the token prefix until one oracle run takes about budget_s
@@ -245,7 +245,7 @@ def measure(cfg, inp, steps: int, warmup: int, block_m=None, data=None) -> dict:
     import mixture_experts_routed_top_amd as M
 
     dev = "cuda:0"
-    layer = M.MoeLayer(cfg.dtype, inp.w1.to(dev), inp.w2.to(dev), cfg.k, cfg.score, cfg.act)
+    layer = M.MoeLayer(cfg.dtype, inp.w1.to(dev), inp.w2.to(dev), cfg.k, cfg.score, cfg.act, cfg.n_shared)
     x, logits = inp.x.to(dev), inp.logits.to(dev)
     plan = layer.plan(cfg.T, block_m=block_m)
     torch.cuda.synchronize()
@@ -289,13 +289,13 @@ def measure(cfg, inp, steps: int, warmup: int, block_m=None, data=None) -> dict:
     g1 = GEMM1_STAGE[cfg.act]
     dom = max((g1, "gemm2_down"), key=lambda n: stage_us[n])
     fl_mult = {"gemm1_swiglu": 4, "gemm1_relu2": 2, "gemm2_down": 2}[dom]
-    dom_flops = fl_mult * cfg.T * cfg.k * cfg.H * cfg.I
+    dom_flops = fl_mult * cfg.T * (cfg.k + cfg.n_shared) * cfg.H * cfg.I   # rows the kernel computes
     achieved = dom_flops / (stage_us[dom] * 1e-6) / 1e12
     peak = PEAK_TFLOPS[cfg.dtype]
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": _traffic(cfg.name, dom, cfg.dtype),
                 "avg_launch_us": stage_us[dom],
-                "algorithmic": f"{fl_mult}*T*k*H*I = {dom_flops} FLOP per launch"}
+                "algorithmic": f"{fl_mult}*T*(k+shared)*H*I = {dom_flops} FLOP per launch"}
 
     rec = {
         "metric": "routed MoE-MLP forward TFLOP/s on 1 MI355X (+% of dtype MFMA peak)",
@@ -305,6 +305,7 @@ def measure(cfg, inp, steps: int, warmup: int, block_m=None, data=None) -> dict:
         "dtype": "bf16" if cfg.dtype == 0 else ("fp8" if cfg.dtype == 1 else "mxfp4xmxfp8"),
         "data": data or "synthetic (seeded N(0,1) tokens, N(0,sigma) bf16 weights, router logits x.Wr)",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k, "I": cfg.I,
+                   "n_shared": cfg.n_shared, "activation": "swiglu" if cfg.act == 0 else "relu2",
                    "routing": cfg.routing, "score": "softmax" if cfg.score == 0 else "sigmoid",
                    "numeric_path": DTYPE_NAME[cfg.dtype], "block_m": plan.block_m, "parallelism": "none (1 GPU)"},
         "pct_of_dtype_peak": round(100 * value / peak, 2),
@@ -349,7 +350,9 @@ def sweep(a) -> int:
 def _stage_fns(layer, plan, x, logits):
     import mixture_experts_routed_top_amd as M
     d = layer.dtype
-    fns = [("route", lambda: M.moe_route(logits, layer.k, layer.score, plan.ids, plan.w)),
+    route = (lambda: M.moe_route_shared(logits, layer.k_routed, layer.score, layer.n_shared, plan.ids, plan.w)) \
+        if layer.n_shared else (lambda: M.moe_route(logits, layer.k, layer.score, plan.ids, plan.w))
+    fns = [("route", route),
            ("align_sort", lambda: M.moe_align_sort(plan.ids, layer.E, plan.block_m, out=plan.sort))]
     if d == M.DTYPE_FP8_BLOCK128:
         fns.append(("quantize_x", lambda: M.moe_quantize_fp8(x, 1, plan.xq, plan.xs)))

@@ -87,6 +87,24 @@ moe_status_t moe_route(const float* logits, int64_t T, int32_t E, int32_t k, int
                        int32_t* topk_ids, float* topk_w, void* stream);
 
 /*
+ * moe_route_shared -- moe_route plus shared experts: the layer's S = n_shared
+ * shared experts, numbered E .. E+S-1 after the E routed ones, are used by
+ * every token with weight 1 and no gate (GC-MoE on SM120, Abstract: shared
+ * experts folded into the compute; TileScale PR #70, Summary: fused
+ * shared-expert execution). They then run through moe_align_sort and the
+ * grouped GEMMs as experts E .. E+S-1 in the same task queue, with k + S slots.
+ *
+ *   logits   [T, E] fp32, device: scores of the routed experts only.
+ *   topk_ids [T, k+S] int32, out: slots 0..k-1 as moe_route; slot k+s = E+s.
+ *   topk_w   [T, k+S] fp32, out: slots 0..k-1 as moe_route; slots k.. = 1.0f.
+ * Requires n_shared >= 0, k + n_shared <= MOE_MAX_TOPK and
+ * E + n_shared <= MOE_MAX_EXPERTS, otherwise as moe_route. n_shared = 0 is
+ * moe_route. Errors: MOE_ERR_INVALID_ARG, MOE_ERR_DEVICE.
+ */
+moe_status_t moe_route_shared(const float* logits, int64_t T, int32_t E, int32_t k, int32_t score,
+                              int32_t n_shared, int32_t* topk_ids, float* topk_w, void* stream);
+
+/*
  * moe_pick_block_m -- host only. The tile height (rows per tile of the
  * expert-sorted layout) this library's kernels use for a problem, from the
  * mean number of rows per expert (the adaptive token-tile geometry named in

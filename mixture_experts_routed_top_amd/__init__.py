@@ -8,6 +8,6 @@ from ._binding import (  # noqa: F401
     ACT_RELU2, ACT_SWIGLU, DTYPE_BF16, DTYPE_FP8_BLOCK128, DTYPE_MXFP4W_MXFP8A, SCORE_SIGMOID, SCORE_SOFTMAX,
     MoeError, SortResult, lib, moe_align_sort, moe_align_sort_workspace_bytes, moe_combine,
     moe_grouped_gemm_down, moe_grouped_gemm_relu2, moe_grouped_gemm_swiglu, moe_pick_block_m, moe_quantize_fp8,
-    moe_quantize_mxfp4, moe_quantize_mxfp8, moe_route, moe_sorted_capacity, moe_status_string,
+    moe_quantize_mxfp4, moe_quantize_mxfp8, moe_route, moe_route_shared, moe_sorted_capacity, moe_status_string,
 )
 from .forward import MoeLayer, Plan  # noqa: F401

@@ -34,6 +34,7 @@ SCORE_SIGMOID = 1
 _P, _I32, _I64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 SIGNATURES = {
     "moe_route": (_I32, [_P, _I64, _I32, _I32, _I32, _P, _P, _P]),
+    "moe_route_shared": (_I32, [_P, _I64, _I32, _I32, _I32, _I32, _P, _P, _P]),
     "moe_pick_block_m": (_I32, [_I32, _I64, _I32, _I32, _I32, _I32]),
     "moe_sorted_capacity": (_I64, [_I64, _I32, _I32, _I32]),
     "moe_align_sort_workspace_bytes": (_SZ, [_I64, _I32, _I32]),
@@ -123,6 +124,19 @@ def moe_route(logits: torch.Tensor, k: int, score: int = SCORE_SOFTMAX, topk_ids
     if topk_w is None:
         topk_w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
     _check("moe_route", lib().moe_route(_p(logits), T, E, k, score, _p(topk_ids), _p(topk_w), _s(stream)))
+    return topk_ids, topk_w
+
+
+def moe_route_shared(logits: torch.Tensor, k: int, score: int, n_shared: int, topk_ids=None, topk_w=None,
+                     stream=None):
+    _need(logits, torch.float32, "logits")
+    T, E = logits.shape
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k + n_shared), dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, k + n_shared), dtype=torch.float32, device=logits.device)
+    _check("moe_route_shared", lib().moe_route_shared(_p(logits), T, E, k, score, n_shared, _p(topk_ids),
+                                                      _p(topk_w), _s(stream)))
     return topk_ids, topk_w
 
 

@@ -114,19 +114,25 @@ const char* moe_status_string(moe_status_t s) {
   }
 }
 
-moe_status_t moe_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t score,
-                       int32_t* topk_ids, float* topk_w, void* stream) {
-  if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > E || k > MOE_MAX_TOPK)
+moe_status_t moe_route_shared(const float* logits, int64_t T, int32_t E, int32_t k, int32_t score,
+                              int32_t n_shared, int32_t* topk_ids, float* topk_w, void* stream) {
+  if (T < 0 || E < 1 || k < 1 || k > E || n_shared < 0 || k + n_shared > MOE_MAX_TOPK)
     return MOE_ERR_INVALID_ARG;
+  if (E + n_shared > MOE_MAX_EXPERTS) return MOE_ERR_INVALID_ARG;
   if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
-  if (T > (int64_t{1} << 31) / k) return MOE_ERR_INVALID_ARG;
+  if (T > (int64_t{1} << 31) / (k + n_shared)) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (!logits || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
   if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4)) return MOE_ERR_INVALID_ARG;
   moe::DeviceInfo dev;
   if (moe_status_t st = current_device(&dev)) return st;
-  return launched(moe::launch_route(logits, T, E, k, score, topk_ids, topk_w,
+  return launched(moe::launch_route(logits, T, E, k, score, n_shared, topk_ids, topk_w,
                                     static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_route(const float* logits, int64_t T, int32_t E, int32_t k, int32_t score,
+                       int32_t* topk_ids, float* topk_w, void* stream) {
+  return moe_route_shared(logits, T, E, k, score, 0, topk_ids, topk_w, stream);
 }
 
 int32_t moe_pick_block_m(int32_t dtype, int64_t T, int32_t k, int32_t E, int32_t H, int32_t I) {

@@ -13,7 +13,7 @@ struct DeviceInfo {
   int num_cus;   // compute units of the current device
 };
 
-hipError_t launch_route(const float* logits, int64_t T, int E, int k, int score,
+hipError_t launch_route(const float* logits, int64_t T, int E, int k, int score, int n_shared,
                         int32_t* ids, float* w, hipStream_t s);
 
 // align_sort: chunked, deterministic counting sort (see align_sort.hip).

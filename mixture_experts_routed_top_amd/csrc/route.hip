@@ -34,7 +34,7 @@ __device__ __forceinline__ int popc(uint64_t m) { return __popcll(m); }
 
 template <int PER_LANE>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void route_kernel(const float* __restrict__ logits, int64_t T,
-                                                                    int E, int k, int score,
+                                                                    int E, int k, int score, int n_shared,
                                                                     int32_t* __restrict__ ids,
                                                                     float* __restrict__ w) {
   __shared__ uint32_t s_key[kWavesPerBlock][32];
@@ -128,22 +128,27 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void route_kernel(const float*
   } else {
     wj = __fdiv_rn(1.0f, 1.0f + expf(-my_v));
   }
+  // slots k .. k + n_shared - 1: the shared experts E .. E + n_shared - 1, weight 1
+  const int kk = k + n_shared;
   if (lane < k) {
-    ids[t * k + lane] = my_e;
-    w[t * k + lane] = wj;
+    ids[t * kk + lane] = my_e;
+    w[t * kk + lane] = wj;
+  } else if (lane < kk) {
+    ids[t * kk + lane] = E + (lane - k);
+    w[t * kk + lane] = 1.0f;
   }
 }
 
 }  // namespace
 
-hipError_t launch_route(const float* logits, int64_t T, int E, int k, int score, int32_t* ids,
+hipError_t launch_route(const float* logits, int64_t T, int E, int k, int score, int n_shared, int32_t* ids,
                         float* w, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((T + kWavesPerBlock - 1) / kWavesPerBlock)), block(64 * kWavesPerBlock);
-  if (E <= 64) route_kernel<1><<<grid, block, 0, s>>>(logits, T, E, k, score, ids, w);
-  else if (E <= 128) route_kernel<2><<<grid, block, 0, s>>>(logits, T, E, k, score, ids, w);
-  else if (E <= 256) route_kernel<4><<<grid, block, 0, s>>>(logits, T, E, k, score, ids, w);
-  else if (E <= 512) route_kernel<8><<<grid, block, 0, s>>>(logits, T, E, k, score, ids, w);
-  else route_kernel<16><<<grid, block, 0, s>>>(logits, T, E, k, score, ids, w);
+  if (E <= 64) route_kernel<1><<<grid, block, 0, s>>>(logits, T, E, k, score, n_shared, ids, w);
+  else if (E <= 128) route_kernel<2><<<grid, block, 0, s>>>(logits, T, E, k, score, n_shared, ids, w);
+  else if (E <= 256) route_kernel<4><<<grid, block, 0, s>>>(logits, T, E, k, score, n_shared, ids, w);
+  else if (E <= 512) route_kernel<8><<<grid, block, 0, s>>>(logits, T, E, k, score, n_shared, ids, w);
+  else route_kernel<16><<<grid, block, 0, s>>>(logits, T, E, k, score, n_shared, ids, w);
   return hipGetLastError();
 }
 

@@ -32,19 +32,23 @@ class MoeLayer:
 
     w1: [E, 2I, H] bf16 (gate rows [0, I), up rows [I, 2I)), or [E, I, H] for
     the ungated squared-ReLU expert (act=ACT_RELU2, BF16 only); w2: [E, H, I] bf16.
+    With n_shared = S > 0 the last S experts of w1/w2 are shared experts that
+    every token uses with weight 1 (the router scores the first E - S only);
+    they run in the same sorted layout and task queue as the routed ones.
     For the FP8 path the weights are quantised here to E4M3 with 128x128 fp32
     block scales, for the MX path to E2M1 with E8M0 per 32 along K (weight
     preparation, outside the timed forward).
     """
 
     def __init__(self, dtype: int, w1: torch.Tensor, w2: torch.Tensor, k: int, score: int = B.SCORE_SOFTMAX,
-                 act: int = B.ACT_SWIGLU):
+                 act: int = B.ACT_SWIGLU, n_shared: int = 0):
         E, twoI, H = w1.shape
         if act not in (B.ACT_SWIGLU, B.ACT_RELU2):
             raise ValueError("unknown activation")
         if act == B.ACT_RELU2 and dtype != B.DTYPE_BF16:
             raise ValueError("the squared-ReLU expert is BF16 only")
-        self.dtype, self.k, self.score, self.act = dtype, k, score, act
+        self.dtype, self.score, self.act, self.n_shared = dtype, score, act, n_shared
+        self.k_routed, self.k = k, k + n_shared          # slots per token: routed, then shared
         self.E, self.H, self.I = E, H, (twoI // 2 if act == B.ACT_SWIGLU else twoI)
         if w2.shape != (E, H, self.I):
             raise ValueError("w2 must be [E, H, I]")
@@ -85,7 +89,10 @@ class MoeLayer:
         p = plan if plan is not None else self.plan(T, device=x.device)
         if p.T != T:
             raise ValueError("plan was made for another token count")
-        B.moe_route(logits, self.k, self.score, p.ids, p.w, stream=stream)
+        if self.n_shared:
+            B.moe_route_shared(logits, self.k_routed, self.score, self.n_shared, p.ids, p.w, stream=stream)
+        else:
+            B.moe_route(logits, self.k, self.score, p.ids, p.w, stream=stream)
         B.moe_align_sort(p.ids, self.E, p.block_m, out=p.sort, stream=stream)
         if self.dtype == B.DTYPE_BF16:
             a, a_scale = x, None

@@ -87,6 +87,10 @@ def test_route_host_validation():
     assert L.moe_route(MIS, 4, 8, 2, 0, FAKE, FAKE, NULL) == 1
     assert L.moe_route(NULL, 0, 8, 2, 0, NULL, NULL, NULL) == 0                              # T = 0
     assert L.moe_route(FAKE, -1, 8, 2, 0, FAKE, FAKE, NULL) == 1
+    assert L.moe_route_shared(FAKE, 4, 8, 2, 0, -1, FAKE, FAKE, NULL) == 1                    # n_shared < 0
+    assert L.moe_route_shared(FAKE, 4, 64, 30, 0, 3, FAKE, FAKE, NULL) == 1                   # k + S > 32
+    assert L.moe_route_shared(FAKE, 4, 1024, 2, 0, 1, FAKE, FAKE, NULL) == 1                  # E + S > 1024
+    assert L.moe_route_shared(NULL, 0, 8, 2, 0, 1, NULL, NULL, NULL) == 0
 
 
 def test_align_sort_host_validation():

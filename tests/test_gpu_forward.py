@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _run(cfg, inp, block_m=None):
-    layer = M.MoeLayer(cfg.dtype, cuda(inp.w1), cuda(inp.w2), cfg.k, cfg.score, cfg.act)
+    layer = M.MoeLayer(cfg.dtype, cuda(inp.w1), cuda(inp.w2), cfg.k, cfg.score, cfg.act, cfg.n_shared)
     plan = layer.plan(cfg.T, block_m=block_m)
     out = layer(cuda(inp.x), cuda(inp.logits), plan)
     torch.cuda.synchronize()
@@ -29,7 +29,7 @@ def _full_compare(cfg, inp, block_m=None):
     say("forward full", cfg.name, cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, block_m)
     layer, plan, out = _run(cfg, inp, block_m)
     ref = O.moe_forward(inp.logits.numpy(), to_f64(inp.x), to_f64(inp.w1), to_f64(inp.w2), cfg.k, cfg.score,
-                        cfg.dtype, block_m=plan.block_m, act=cfg.act)
+                        cfg.dtype, block_m=plan.block_m, act=cfg.act, n_shared=cfg.n_shared)
     np.testing.assert_array_equal(plan.ids.cpu().numpy(), ref["ids"])
     np.testing.assert_array_equal(plan.sort.sorted_ids.cpu().numpy()[:len(ref["sorted_ids"])], ref["sorted_ids"])
     got = f64(out)
@@ -120,10 +120,10 @@ def _sampled_compare(name, n_experts=4, rows_per_expert=3, n_tokens=0):
     say("forward full-size sampled", name)
     layer, plan, out = _run(cfg, inp)
     # every routing and layout output is compared in full
-    rid, rw = O.route(inp.logits.numpy(), cfg.k, cfg.score)
+    rid, rw = O.route_with_shared(inp.logits.numpy(), cfg.k, cfg.score, cfg.n_shared)
     np.testing.assert_array_equal(plan.ids.cpu().numpy(), rid)
     np.testing.assert_allclose(plan.w.cpu().numpy(), rw, rtol=0, atol=4e-6)
-    counts, offsets, sorted_ids, tile_expert, num_tiles = O.align_sort(rid, cfg.E, plan.block_m)
+    counts, offsets, sorted_ids, tile_expert, num_tiles = O.align_sort(rid, cfg.E_total, plan.block_m)
     np.testing.assert_array_equal(plan.sort.counts.cpu().numpy(), counts)
     np.testing.assert_array_equal(plan.sort.sorted_ids.cpu().numpy()[:len(sorted_ids)], sorted_ids)
     np.testing.assert_array_equal(plan.sort.tile_expert.cpu().numpy()[:len(tile_expert)], tile_expert)
@@ -140,7 +140,7 @@ def _sampled_compare(name, n_experts=4, rows_per_expert=3, n_tokens=0):
         pick = np.unique(np.concatenate([[seg[0], seg[-1]], rng.choice(seg, min(rows_per_expert, len(seg)),
                                                                        replace=False)]))
         w1h, w2h = _oracle_expert(cfg, layer, e, to_f64(inp.w1[e]), to_f64(inp.w2[e]))
-        xr = _oracle_tokens(cfg, to_f64(inp.x[torch.from_numpy(pick // cfg.k)]))
+        xr = _oracle_tokens(cfg, to_f64(inp.x[torch.from_numpy(pick // (cfg.k + cfg.n_shared))]))
         refs += [O.assignment_forward(xr[i], w1h, w2h, cfg.dtype, cfg.act) for i in range(len(pick))]
         assigned += list(pick)
     got = f64(plan.y[torch.from_numpy(np.array(assigned)).to(out.device)])
@@ -150,10 +150,11 @@ def _sampled_compare(name, n_experts=4, rows_per_expert=3, n_tokens=0):
     # the combine at full size, as a property of the kernel's own Y and weights
     toks = rng.choice(cfg.T, min(cfg.T, 256), replace=False)
     tsel = torch.from_numpy(toks).to(out.device)
-    yk = f64(plan.y.view(cfg.T, cfg.k, cfg.H)[tsel].reshape(-1, cfg.H)).reshape(len(toks), cfg.k, cfg.H)
+    kk = cfg.k + cfg.n_shared
+    yk = f64(plan.y.view(cfg.T, kk, cfg.H)[tsel].reshape(-1, cfg.H)).reshape(len(toks), kk, cfg.H)
     wk = plan.w.cpu().numpy()[toks].astype(np.float64)
     assert_within_rounding(f64(out[tsel]), O.combine(yk.reshape(-1, cfg.H), wk),
-                           cfg.k * U32 * np.abs(wk[:, :, None] * yk).sum(1), min_exact=0.98)
+                           kk * U32 * np.abs(wk[:, :, None] * yk).sum(1), min_exact=0.98)
     assert torch.isfinite(out.float()).all()
     # whole tokens through the oracle (cheap for the BF16 shapes)
     if n_tokens:
@@ -171,6 +172,17 @@ def _sampled_compare(name, n_experts=4, rows_per_expert=3, n_tokens=0):
 @pytest.mark.parametrize("name", ["qwen3_30b_a3b_bf16", "qwen3_30b_a3b_bf16_zipf", "llama4_scout_bf16"])
 def test_full_size_bf16_sampled(name):
     _sampled_compare(name, n_experts=4, n_tokens=6)
+
+
+@pytest.mark.parametrize("T,E,k,S", [(64, 8, 2, 1), (129, 16, 4, 2), (1, 4, 2, 1), (300, 32, 8, 1)])
+def test_shared_experts_forward_small(T, E, k, S):
+    cfg = get_config("qwen3_30b_a3b_bf16_shared").with_(T=T, H=256, E=E, k=k, I=128, n_shared=S, w_std=0.05)
+    _full_compare(cfg, make_inputs(cfg, seed=T + 11))
+
+
+def test_shared_experts_full_size_sampled():
+    # the most loaded expert is the shared one (every token): sampled first
+    _sampled_compare("qwen3_30b_a3b_bf16_shared", n_experts=4, n_tokens=6)
 
 
 @pytest.mark.parametrize("T,H,E,k,I", [(64, 256, 8, 2, 128), (129, 384, 16, 4, 200), (1, 256, 4, 2, 128),

@@ -54,6 +54,19 @@ def test_route_edges_and_ties(T, E, k, score):
     np.testing.assert_allclose(w.cpu().numpy(), rw, rtol=0, atol=4e-6)
 
 
+@pytest.mark.parametrize("T,E,k,S", [(100, 16, 4, 1), (33, 64, 8, 3), (5, 4, 2, 2), (257, 512, 10, 1)])
+def test_route_shared_matches_oracle(T, E, k, S):
+    rng = np.random.default_rng(T + E)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    say("route-shared", T, E, k, S)
+    ids, w = M.moe_route_shared(cuda(torch.from_numpy(logits)), k, O.SCORE_SOFTMAX, S)
+    torch.cuda.synchronize()
+    rid, rw = O.route_with_shared(logits, k, O.SCORE_SOFTMAX, S)
+    np.testing.assert_array_equal(ids.cpu().numpy(), rid)
+    np.testing.assert_allclose(w.cpu().numpy(), rw, rtol=0, atol=4e-6)
+    assert np.all(w.cpu().numpy()[:, k:] == 1.0)
+
+
 # ------------------------------------------------------------------ align_sort
 def _align_check(ids_np, E, bm, runs=1):
     T, k = ids_np.shape

@@ -35,6 +35,11 @@ class Config:
     wr_std: float = 0.02  # std of the router projection
     routing: str = "uniform"   # "uniform" (x . Wr) or "zipf" (Gumbel-top-k, s = 1.2)
     act: int = ACT_SWIGLU
+    n_shared: int = 0    # shared experts (used by every token, weight 1), after the E routed ones
+
+    @property
+    def E_total(self) -> int:
+        return self.E + self.n_shared
 
     @property
     def w1_rows(self) -> int:
@@ -50,6 +55,7 @@ class Config:
 
     @property
     def flops(self) -> int:
+        """Routed GEMM FLOPs (shared experts are not counted, as on the pages)."""
         return (6 if self.act == ACT_SWIGLU else 4) * self.T * self.k * self.H * self.I
 
 
@@ -77,6 +83,9 @@ CONFIGS = {
                               DTYPE_MXFP4W_MXFP8A, SCORE_SOFTMAX, 0.02),
     "mxfp4_moe_t16384": Config("mxfp4_moe_t16384", 5, 16384, 2560, 512, 10, 640,
                                DTYPE_MXFP4W_MXFP8A, SCORE_SOFTMAX, 0.02),
+    # the Qwen3-30B-A3B shape plus one shared expert of the routed experts' size
+    "qwen3_30b_a3b_bf16_shared": Config("qwen3_30b_a3b_bf16_shared", 7, 8192, 2048, 128, 8, 768,
+                                        DTYPE_BF16, SCORE_SOFTMAX, 0.02, n_shared=1),
     # the Nemotron shape with ungated squared-ReLU experts (FlashInfer PR #5129,
     # Measured: H=2688, I=1856, 128 experts, top-6, ReLU2; 2048..8192 tokens)
     "nemotron_relu2_bf16": Config("nemotron_relu2_bf16", 6, 8192, 2688, 128, 6, 1856,

@@ -7,6 +7,7 @@ index, seed]))):
   tensor 2  W1  [E, 2I, H] ~ N(0, w_std)     index = expert (one stream per expert;
                                               [E, I, H] for the ungated ReLU2 expert)
   tensor 3  W2  [E, H, I]  ~ N(0, w_std)     index = expert
+  (W1 and W2 carry E + n_shared experts: the shared ones last)
   tensor 4  Gumbel noise [T, E] (Zipf routing only)   index = T
   tensor 5  permutation of expert popularity ranks (Zipf routing only)
 Draws are fp32 and rounded RN to bf16 with torch. Router logits:
@@ -58,14 +59,14 @@ def make_expert_weights(cfg: Config, tensor_id: int, e: int, seed: int = 0) -> t
 
 def _stack_experts(cfg: Config, tensor_id: int, seed: int) -> torch.Tensor:
     shape = (cfg.w1_rows, cfg.H) if tensor_id == 2 else (cfg.H, cfg.I)
-    out = torch.empty((cfg.E,) + shape, dtype=torch.bfloat16)
+    out = torch.empty((cfg.E_total,) + shape, dtype=torch.bfloat16)
 
     def fill(e):
         out[e].copy_(make_expert_weights(cfg, tensor_id, e, seed))
 
     workers = max(1, min(16, os.cpu_count() or 1))
     with ThreadPoolExecutor(workers) as ex:
-        list(ex.map(fill, range(cfg.E)))
+        list(ex.map(fill, range(cfg.E_total)))
     return out
 
 
@@ -126,9 +127,9 @@ def make_inputs_device(cfg: Config, device, seed: int = 0) -> Inputs:
     x = torch.randn((cfg.T, cfg.H), generator=gen(0, cfg.T), device=device).to(torch.bfloat16)
     wr = (torch.randn((cfg.H, cfg.E), generator=gen(1, 0), device=device) * cfg.wr_std).to(torch.bfloat16)
     logits = x.float() @ wr.float()
-    w1 = torch.empty((cfg.E, cfg.w1_rows, cfg.H), dtype=torch.bfloat16, device=device)
-    w2 = torch.empty((cfg.E, cfg.H, cfg.I), dtype=torch.bfloat16, device=device)
-    for e in range(cfg.E):
+    w1 = torch.empty((cfg.E_total, cfg.w1_rows, cfg.H), dtype=torch.bfloat16, device=device)
+    w2 = torch.empty((cfg.E_total, cfg.H, cfg.I), dtype=torch.bfloat16, device=device)
+    for e in range(cfg.E_total):
         w1[e] = (torch.randn((cfg.w1_rows, cfg.H), generator=gen(2, e), device=device) * cfg.w_std).to(torch.bfloat16)
         w2[e] = (torch.randn((cfg.H, cfg.I), generator=gen(3, e), device=device) * cfg.w_std).to(torch.bfloat16)
     return Inputs(cfg, x, logits, w1, w2, seed)
