@@ -436,3 +436,101 @@ def token_forward(x_row, w1_hat, w2_hat, ids_row, w_row, dtype: int = DTYPE_BF16
 
 
 __all__ = [n for n in dir() if not n.startswith("_") and n not in ("math", "np", "F")]
+
+
+# ============================================================================ backward
+# The backward of the BF16 SwiGLU routed forward, for a given output gradient
+# dout (training). Readings (the design doc lists them): the top-k selection is
+# piecewise constant (no gradient through the choice); the forward saves the
+# gate/up pre-activations in bf16 beside h; storage points of the backward:
+# dY and dGU (the operands of the next GEMMs) and the per-assignment dx rows
+# are bf16, dx is bf16, the weight gradients and dw / dlogits are fp32.
+def route_backward(w: np.ndarray, ids: np.ndarray, dw: np.ndarray, E: int, score: int) -> np.ndarray:
+    """dlogits [T, E] from the gradient dw [T, k] of the routed weights.
+
+    SOFTMAX over the selected logits: dl_i = w_i (dw_i - sum_j w_j dw_j) for
+    selected i; SIGMOID: dl_i = dw_i w_i (1 - w_i). Unselected logits: 0."""
+    w = np.asarray(w, np.float64)
+    dw = np.asarray(dw, np.float64)
+    T, k = w.shape
+    if score == SCORE_SOFTMAX:
+        g = w * (dw - (w * dw).sum(axis=1, keepdims=True))
+    else:
+        g = dw * w * (1.0 - w)
+    dl = np.zeros((T, E), dtype=np.float64)
+    np.put_along_axis(dl, np.asarray(ids, np.int64), g, axis=1)
+    return F.round_fp32(dl).astype(np.float32)
+
+
+def moe_backward(logits, x_bf16, w1_bf16, w2_bf16, dout_bf16, k: int, score: int, block_m: int = 16,
+                 n_shared: int = 0, exact: bool = False):
+    """Gradients of the BF16 SwiGLU routed forward (moe_forward) for dout.
+
+    Returns a dict: dx [T, H], dw1 [E, 2I, H], dw2 [E, H, I], dw [T, k(+S)],
+    dlogits [T, E_routed], and the stored intermediates dy (sorted rows),
+    dgu (sorted rows), dx_rows (assignment order). exact=True drops every
+    storage rounding (forward and backward), which makes the result the
+    mathematical gradient of the unrounded forward.
+    """
+    rb = (lambda v: np.asarray(v, np.float64)) if exact else F.round_bf16
+    x = np.asarray(x_bf16, np.float64)
+    w1 = np.asarray(w1_bf16, np.float64)
+    w2 = np.asarray(w2_bf16, np.float64)
+    dout = np.asarray(dout_bf16, np.float64)
+    T, H = x.shape
+    E, twoI, _ = w1.shape
+    I = twoI // 2
+    E_routed = E - n_shared
+    if n_shared:
+        ids, w = route_with_shared(logits, k, score, n_shared)
+    else:
+        ids, w = route(logits, k, score)
+    kk = k + n_shared
+    A = T * kk
+    counts, offsets, sorted_ids, tile_expert, num_tiles = align_sort(ids, E, block_m)
+    rows = num_tiles * block_m
+    srt = sorted_ids[:rows].astype(np.int64)
+    real = srt < A
+    e_of = np.repeat(tile_expert[:num_tiles].astype(np.int64), block_m)
+    tok = np.where(real, srt // kk, 0)
+
+    # forward, saving what the backward reads
+    xs = np.where(real[:, None], x[tok], 0.0)                       # gathered tokens, sorted rows
+    g = np.einsum("rh,rnh->rn", xs, w1[e_of, :I])
+    u = np.einsum("rh,rnh->rn", xs, w1[e_of, I:])
+    h = rb(silu(g) * u)
+    y_sorted = rb(np.einsum("ri,rhi->rh", h, w2[e_of]))
+    y = np.zeros((A, H))
+    y[srt[real]] = y_sorted[real]
+    g_s, u_s = rb(g), rb(u)                                         # saved pre-activations
+
+    # combine backward
+    wa = np.asarray(w, np.float64).reshape(A)
+    dy = np.where(real[:, None], rb(wa[np.where(real, srt, 0)][:, None] * dout[tok]), 0.0)
+    dw = (dout[np.arange(A) // kk] * y).sum(axis=1).reshape(T, kk)
+    dw32 = F.round_fp32(dw).astype(np.float32)
+    dlogits = route_backward(w[:, :k], ids[:, :k], dw[:, :k], E_routed, score)
+
+    # GEMM2 backward: dh and the SwiGLU backward; dW2
+    dh = np.einsum("rh,rhi->ri", dy, w2[e_of])
+    sg = 1.0 / (1.0 + np.exp(-g_s))
+    dg = dh * u_s * sg * (1.0 + g_s * (1.0 - sg))
+    du = dh * g_s * sg
+    dgu = rb(np.concatenate([dg, du], axis=1))
+    dw2 = np.zeros_like(w2)
+    dw1 = np.zeros_like(w1)
+    for e in range(E):
+        sel = (e_of == e) & real
+        if sel.any():
+            dw2[e] = dy[sel].T @ h[sel]
+            dw1[e] = dgu[sel].T @ xs[sel]
+    # GEMM1 backward: dx rows per assignment, then the sum over each token's slots
+    dx_sorted = rb(np.einsum("rn,rnh->rh", dgu, w1[e_of]))
+    dx_rows = np.zeros((A, H))
+    dx_rows[srt[real]] = dx_sorted[real]
+    dx = rb(dx_rows.reshape(T, kk, H).sum(axis=1))
+    f32 = (lambda v: v) if exact else (lambda v: F.round_fp32(v))
+    return {"ids": ids, "w": w, "sorted_ids": sorted_ids, "tile_expert": tile_expert, "num_tiles": num_tiles,
+            "gu": np.concatenate([g_s, u_s], axis=1), "h": h, "y": y,
+            "dy": dy, "dw": dw32, "dlogits": dlogits, "dgu": dgu, "dx_rows": dx_rows, "dx": dx,
+            "dw1": f32(dw1), "dw2": f32(dw2)}
