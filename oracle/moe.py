@@ -494,12 +494,22 @@ def moe_backward(logits, x_bf16, w1_bf16, w2_bf16, dout_bf16, k: int, score: int
     e_of = np.repeat(tile_expert[:num_tiles].astype(np.int64), block_m)
     tok = np.where(real, srt // kk, 0)
 
+    # every product below runs over one expert's rows at a time: row r of the
+    # sorted layout belongs to expert e_of[r]
+    def per_expert(f, out_cols):
+        out = np.zeros((rows, out_cols))
+        for e in range(E):
+            sel = e_of == e
+            if sel.any():
+                out[sel] = f(e, sel)
+        return out
+
     # forward, saving what the backward reads
     xs = np.where(real[:, None], x[tok], 0.0)                       # gathered tokens, sorted rows
-    g = np.einsum("rh,rnh->rn", xs, w1[e_of, :I])
-    u = np.einsum("rh,rnh->rn", xs, w1[e_of, I:])
+    g = per_expert(lambda e, sel: xs[sel] @ w1[e, :I].T, I)
+    u = per_expert(lambda e, sel: xs[sel] @ w1[e, I:].T, I)
     h = rb(silu(g) * u)
-    y_sorted = rb(np.einsum("ri,rhi->rh", h, w2[e_of]))
+    y_sorted = rb(per_expert(lambda e, sel: h[sel] @ w2[e].T, H))
     y = np.zeros((A, H))
     y[srt[real]] = y_sorted[real]
     g_s, u_s = rb(g), rb(u)                                         # saved pre-activations
@@ -512,7 +522,7 @@ def moe_backward(logits, x_bf16, w1_bf16, w2_bf16, dout_bf16, k: int, score: int
     dlogits = route_backward(w[:, :k], ids[:, :k], dw[:, :k], E_routed, score)
 
     # GEMM2 backward: dh and the SwiGLU backward; dW2
-    dh = np.einsum("rh,rhi->ri", dy, w2[e_of])
+    dh = per_expert(lambda e, sel: dy[sel] @ w2[e], I)
     sg = 1.0 / (1.0 + np.exp(-g_s))
     dg = dh * u_s * sg * (1.0 + g_s * (1.0 - sg))
     du = dh * g_s * sg
@@ -525,7 +535,7 @@ def moe_backward(logits, x_bf16, w1_bf16, w2_bf16, dout_bf16, k: int, score: int
             dw2[e] = dy[sel].T @ h[sel]
             dw1[e] = dgu[sel].T @ xs[sel]
     # GEMM1 backward: dx rows per assignment, then the sum over each token's slots
-    dx_sorted = rb(np.einsum("rn,rnh->rh", dgu, w1[e_of]))
+    dx_sorted = rb(per_expert(lambda e, sel: dgu[sel] @ w1[e], H))
     dx_rows = np.zeros((A, H))
     dx_rows[srt[real]] = dx_sorted[real]
     dx = rb(dx_rows.reshape(T, kk, H).sum(axis=1))
