@@ -301,6 +301,127 @@ moe_status_t moe_grouped_gemm_down(int32_t dtype, const void* h, const void* h_s
 moe_status_t moe_combine(const uint16_t* y, const float* topk_w, int64_t T, int32_t k, int32_t H,
                          uint16_t* out, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Backward of the BF16 SwiGLU routed forward (training). Liger-Kernel PR
+ * #1463, Summary (SM90 backward) and "MoEBenchmark results" (forward and
+ * backward throughput of the BF16 routed-expert MLP): the gradients run over
+ * the same padded expert-sorted rows and tile queue as the forward.
+ *
+ * One training step:
+ *   forward:  moe_route -> moe_align_sort -> moe_grouped_gemm_swiglu_save
+ *             -> moe_grouped_gemm_down -> moe_combine
+ *   backward: moe_backward_combine (dY, dw) -> moe_route_backward (dlogits)
+ *             -> moe_grouped_gemm_dh (dGU) -> moe_grouped_gemm_dx (dx rows)
+ *             -> moe_combine with unit weights (dx)
+ *             -> moe_gather_rows (x in sorted rows)
+ *             -> moe_grouped_gemm_wgrad twice (dW2: P = h, Q = dY;
+ *                dW1: P = x_sorted, Q = dGU)
+ * The GEMM steps need block_m == 256 (else MOE_ERR_UNSUPPORTED_SHAPE);
+ * the elementwise steps take any block_m. Shape rules otherwise as for the
+ * BF16 forward (H % 8 == 0, I % 8 == 0; one expert's W1 and every sorted-row
+ * operand below 2 GiB).
+ * ---------------------------------------------------------------------- */
+
+/*
+ * moe_grouped_gemm_swiglu_save -- the BF16 moe_grouped_gemm_swiglu that also
+ * stores the pre-activations the SwiGLU backward needs.
+ *   gu [cap, 2I] bf16, out: gu[r, n] = bf16(g_n), gu[r, I + n] = bf16(u_n) for
+ *   every sorted row r < num_tiles * block_m (pad rows: 0).
+ * Other arguments, outputs and errors as moe_grouped_gemm_swiglu with
+ * dtype = MOE_DTYPE_BF16; gu NULL or not 16-byte aligned -> MOE_ERR_INVALID_ARG.
+ */
+moe_status_t moe_grouped_gemm_swiglu_save(const void* x, const void* w1,
+                                          const int32_t* sorted_ids, const int32_t* tile_expert,
+                                          const int32_t* num_tiles,
+                                          int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                                          int32_t block_m, int64_t cap,
+                                          void* h, void* gu, void* stream);
+
+/*
+ * moe_backward_combine -- backward of moe_combine, per sorted row.
+ *   For each sorted row r < cap with a = sorted_ids[r] (t = a / k):
+ *     dy[r, c] = bf16( topk_w[a] * dout[t, c] ) if a < A, else 0;
+ *     dw[a]    = sum_c dout[t, c] * y[a, c] (fp32, each real a once).
+ *   dout [T, H] bf16; topk_w [T, k] fp32; y [T*k, H] bf16 (the forward's
+ *   GEMM2 rows); sorted_ids [cap] int32 from moe_align_sort; dy [cap, H]
+ *   bf16 out; dw [T, k] fp32 out.
+ * Rows of sorted_ids at or past num_tiles * block_m must hold ids >= A (the
+ * moe_align_sort layout fills them so). Requires H % 8 == 0.
+ */
+moe_status_t moe_backward_combine(const uint16_t* dout, const float* topk_w, const uint16_t* y,
+                                  const int32_t* sorted_ids, int64_t T, int32_t k, int32_t H, int64_t cap,
+                                  uint16_t* dy, float* dw, void* stream);
+
+/*
+ * moe_route_backward -- gradient of the router logits from the gradient of
+ * the top-k gate weights (the routed slots only; shared slots have weight 1
+ * and no gradient).
+ *   For token t and routed expert e = topk_ids[t, j] (j < k):
+ *     softmax: dlogits[t, e] = w_j (dw_j - sum_{q<k} w_q dw_q)
+ *     sigmoid: dlogits[t, e] = dw_j w_j (1 - w_j)
+ *   and dlogits[t, e] = 0 for every expert not selected.
+ *   topk_w, dw [T, k + n_shared] fp32; topk_ids [T, k + n_shared] int32;
+ *   dlogits [T, E] fp32 out (E routed experts).
+ */
+moe_status_t moe_route_backward(const float* topk_w, const int32_t* topk_ids, const float* dw, int64_t T,
+                                int32_t E, int32_t k, int32_t n_shared, int32_t score, float* dlogits,
+                                void* stream);
+
+/*
+ * moe_gather_rows -- the tokens in sorted-row order (the token operand of the
+ * W1 weight gradient): x_sorted[r, :] = x[sorted_ids[r] / k, :] for real rows,
+ * 0 for pad rows, every r < cap.
+ *   x [T, H] bf16; sorted_ids [cap] int32; x_sorted [cap, H] bf16 out.
+ * Requires H % 8 == 0.
+ */
+moe_status_t moe_gather_rows(const uint16_t* x, const int32_t* sorted_ids, int64_t T, int32_t k, int32_t H,
+                             int64_t cap, uint16_t* x_sorted, void* stream);
+
+/*
+ * moe_grouped_gemm_dh -- gradient through GEMM2 and the SwiGLU, per sorted
+ * row r < num_tiles * block_m of expert e = tile_expert[r / block_m]:
+ *   dh[r, i]     = sum_c dy[r, c] W2[e, c, i]          (fp32 accumulate)
+ *   s = sigmoid(g), with (g, u) = gu[r, i], gu[r, I + i]:
+ *   dgu[r, i]     = bf16( dh u s (1 + g (1 - s)) )
+ *   dgu[r, I + i] = bf16( dh g s )
+ *   dy [cap, H] bf16 (moe_backward_combine); W2 [E, H, I] bf16; gu [cap, 2I]
+ *   bf16 (moe_grouped_gemm_swiglu_save); dgu [cap, 2I] bf16 out.
+ * block_m must be 256.
+ */
+moe_status_t moe_grouped_gemm_dh(const void* dy, const void* w2, const void* gu, const int32_t* sorted_ids,
+                                 const int32_t* tile_expert, const int32_t* num_tiles, int64_t T, int32_t H,
+                                 int32_t I, int32_t E, int32_t k, int32_t block_m, int64_t cap, void* dgu,
+                                 void* stream);
+
+/*
+ * moe_grouped_gemm_dx -- gradient through GEMM1 to each assignment's row:
+ *   for each sorted row r < num_tiles * block_m with a = sorted_ids[r] < A:
+ *     dx_rows[a, c] = bf16( sum_n dgu[r, n] W1[e, n, c] ), n over [0, 2I).
+ *   dgu [cap, 2I] bf16; W1 [E, 2I, H] bf16; dx_rows [T*k, H] bf16 out
+ *   (every row a < A written once). Summing each token's k rows
+ *   (moe_combine with topk_w = 1) gives dx.
+ * block_m must be 256.
+ */
+moe_status_t moe_grouped_gemm_dx(const void* dgu, const void* w1, const int32_t* sorted_ids,
+                                 const int32_t* tile_expert, const int32_t* num_tiles, int64_t T, int32_t H,
+                                 int32_t I, int32_t E, int32_t k, int32_t block_m, int64_t cap, void* dx_rows,
+                                 void* stream);
+
+/*
+ * moe_grouped_gemm_wgrad -- per-expert weight gradient over the expert's
+ * sorted rows r in [offsets[e], offsets[e + 1]):
+ *   dw[e, n, m] = sum_r p_rows[r, m] q_rows[r, n]      (fp32 accumulate, fp32 out)
+ *   p_rows [cap, M] bf16; q_rows [cap, N] bf16; offsets [E + 1] int32 from
+ *   moe_align_sort; dw [E, N, M] fp32 out (experts without rows get 0).
+ *   dW2 [E, H, I]: p = h, q = dy, M = I, N = H.
+ *   dW1 [E, 2I, H]: p = x_sorted, q = dgu, M = H, N = 2I.
+ * Pad rows must be 0 in p or q (they are, for the operands above).
+ * Requires M % 8 == 0, N % 8 == 0, block_m == 256, 16-byte aligned pointers.
+ */
+moe_status_t moe_grouped_gemm_wgrad(const void* p_rows, const void* q_rows, int32_t M, int32_t N,
+                                    const int32_t* offsets, int64_t T, int32_t E, int32_t k, int32_t block_m,
+                                    int64_t cap, float* dw, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* moe_status_string(moe_status_t status);
 

@@ -49,6 +49,14 @@ SIGNATURES = {
     "moe_grouped_gemm_down": (_I32, [_I32, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32,
                                      _I32, _I64, _P, _P]),
     "moe_combine": (_I32, [_P, _P, _I64, _I32, _I32, _P, _P]),
+    "moe_grouped_gemm_swiglu_save": (_I32, [_P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I64,
+                                            _P, _P, _P]),
+    "moe_backward_combine": (_I32, [_P, _P, _P, _P, _I64, _I32, _I32, _I64, _P, _P, _P]),
+    "moe_route_backward": (_I32, [_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P]),
+    "moe_gather_rows": (_I32, [_P, _P, _I64, _I32, _I32, _I64, _P, _P]),
+    "moe_grouped_gemm_dh": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I64, _P, _P]),
+    "moe_grouped_gemm_dx": (_I32, [_P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I64, _P, _P]),
+    "moe_grouped_gemm_wgrad": (_I32, [_P, _P, _I32, _I32, _P, _I64, _I32, _I32, _I32, _I64, _P, _P]),
     "moe_status_string": (ctypes.c_char_p, [_I32]),
 }
 
@@ -252,3 +260,90 @@ def moe_combine(y: torch.Tensor, topk_w: torch.Tensor, out=None, stream=None):
         out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
     _check("moe_combine", lib().moe_combine(_p(y), _p(topk_w), T, k, H, _p(out), _s(stream)))
     return out
+
+
+# ---------------------------------------------------------------- backward (BF16)
+def moe_grouped_gemm_swiglu_save(x, w1, sort: SortResult, H: int, I: int, h=None, gu=None, stream=None):
+    """BF16 GEMM1 + SwiGLU that also stores the bf16 pre-activations gu [cap, 2I]."""
+    if h is None:
+        h = torch.empty((max(sort.cap, 1), I), dtype=torch.bfloat16, device=x.device)
+    if gu is None:
+        gu = torch.empty((max(sort.cap, 1), 2 * I), dtype=torch.bfloat16, device=x.device)
+    _check("moe_grouped_gemm_swiglu_save", lib().moe_grouped_gemm_swiglu_save(
+        _p(x), _p(w1), _p(sort.sorted_ids), _p(sort.tile_expert), _p(sort.num_tiles), sort.T, H, I, sort.E,
+        sort.k, sort.block_m, sort.cap, _p(h), _p(gu), _s(stream)))
+    return h, gu
+
+
+def moe_backward_combine(dout, topk_w, y, sort: SortResult, dy=None, dw=None, stream=None):
+    """dY [cap, H] bf16 (w * dout in sorted rows) and dw [T, k] fp32 (dout . y)."""
+    _need(dout, torch.bfloat16, "dout")
+    _need(topk_w, torch.float32, "topk_w")
+    _need(y, torch.bfloat16, "y")
+    T, k = topk_w.shape
+    H = dout.shape[1]
+    if dy is None:
+        dy = torch.empty((max(sort.cap, 1), H), dtype=torch.bfloat16, device=dout.device)
+    if dw is None:
+        dw = torch.empty((T, k), dtype=torch.float32, device=dout.device)
+    _check("moe_backward_combine", lib().moe_backward_combine(
+        _p(dout), _p(topk_w), _p(y), _p(sort.sorted_ids), T, k, H, sort.cap, _p(dy), _p(dw), _s(stream)))
+    return dy, dw
+
+
+def moe_route_backward(topk_w, topk_ids, dw, E: int, k: int, score: int, n_shared: int = 0, dlogits=None,
+                       stream=None):
+    """dlogits [T, E] fp32 from the gate-weight gradient dw [T, k + n_shared]."""
+    _need(topk_w, torch.float32, "topk_w")
+    _need(topk_ids, torch.int32, "topk_ids")
+    _need(dw, torch.float32, "dw")
+    T = topk_w.shape[0]
+    if dlogits is None:
+        dlogits = torch.empty((T, E), dtype=torch.float32, device=dw.device)
+    _check("moe_route_backward", lib().moe_route_backward(
+        _p(topk_w), _p(topk_ids), _p(dw), T, E, k, n_shared, score, _p(dlogits), _s(stream)))
+    return dlogits
+
+
+def moe_gather_rows(x, sort: SortResult, out=None, stream=None):
+    """x in sorted-row order [cap, H] (pad rows 0)."""
+    _need(x, torch.bfloat16, "x")
+    H = x.shape[1]
+    if out is None:
+        out = torch.empty((max(sort.cap, 1), H), dtype=torch.bfloat16, device=x.device)
+    _check("moe_gather_rows", lib().moe_gather_rows(_p(x), _p(sort.sorted_ids), sort.T, sort.k, H, sort.cap,
+                                                    _p(out), _s(stream)))
+    return out
+
+
+def moe_grouped_gemm_dh(dy, w2, gu, sort: SortResult, H: int, I: int, dgu=None, stream=None):
+    """dGU [cap, 2I] bf16: dY W2 through the SwiGLU backward."""
+    if dgu is None:
+        dgu = torch.empty((max(sort.cap, 1), 2 * I), dtype=torch.bfloat16, device=dy.device)
+    _check("moe_grouped_gemm_dh", lib().moe_grouped_gemm_dh(
+        _p(dy), _p(w2), _p(gu), _p(sort.sorted_ids), _p(sort.tile_expert), _p(sort.num_tiles), sort.T, H, I,
+        sort.E, sort.k, sort.block_m, sort.cap, _p(dgu), _s(stream)))
+    return dgu
+
+
+def moe_grouped_gemm_dx(dgu, w1, sort: SortResult, H: int, I: int, dx_rows=None, stream=None):
+    """dx rows [T*k, H] bf16 in assignment order."""
+    if dx_rows is None:
+        dx_rows = torch.empty((max(sort.T * sort.k, 1), H), dtype=torch.bfloat16, device=dgu.device)
+    _check("moe_grouped_gemm_dx", lib().moe_grouped_gemm_dx(
+        _p(dgu), _p(w1), _p(sort.sorted_ids), _p(sort.tile_expert), _p(sort.num_tiles), sort.T, H, I,
+        sort.E, sort.k, sort.block_m, sort.cap, _p(dx_rows), _s(stream)))
+    return dx_rows
+
+
+def moe_grouped_gemm_wgrad(p_rows, q_rows, sort: SortResult, dw=None, stream=None):
+    """dW [E, N, M] fp32 = sum over each expert's sorted rows of q_rows^T p_rows."""
+    _need(p_rows, torch.bfloat16, "p_rows")
+    _need(q_rows, torch.bfloat16, "q_rows")
+    M, N = p_rows.shape[1], q_rows.shape[1]
+    if dw is None:
+        dw = torch.empty((sort.E, N, M), dtype=torch.float32, device=p_rows.device)
+    _check("moe_grouped_gemm_wgrad", lib().moe_grouped_gemm_wgrad(
+        _p(p_rows), _p(q_rows), M, N, _p(sort.offsets), sort.T, sort.E, sort.k, sort.block_m, sort.cap,
+        _p(dw), _s(stream)))
+    return dw

@@ -87,6 +87,7 @@ struct Params {
   const int32_t* tile_expert;
   const int32_t* num_tiles;
   uint16_t* out;           // GEMM1: h [cap, I]; GEMM2: y [A, H]
+  uint16_t* gu;            // GEMM1 (SwiGLU), optional: saved pre-activations [cap, 2I] (gate, up)
   int64_t A;
   uint32_t a_bytes;        // bytes of the token operand (below 2^31)
   int H, I, k;
@@ -263,6 +264,16 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
             st.x = pack_bf16x2(o[0], o[1]);
             st.y = pack_bf16x2(o[2], o[3]);
             *reinterpret_cast<uint2*>(p.out + dst_row * N + n) = st;
+            if (GEMM1 && ACT == kActSwiglu && p.gu != nullptr) {
+              // training forward: the gate and up pre-activations for the backward
+              const float gv[4] = {acc[0][i][j][g * 4], acc[0][i][j][g * 4 + 1], acc[0][i][j][g * 4 + 2],
+                                   acc[0][i][j][g * 4 + 3]};
+              const float uv[4] = {acc[C::HALVES - 1][i][j][g * 4], acc[C::HALVES - 1][i][j][g * 4 + 1],
+                                   acc[C::HALVES - 1][i][j][g * 4 + 2], acc[C::HALVES - 1][i][j][g * 4 + 3]};
+              uint16_t* gr = p.gu + dst_row * 2 * N + n;
+              *reinterpret_cast<uint2*>(gr) = make_uint2(pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3]));
+              *reinterpret_cast<uint2*>(gr + N) = make_uint2(pack_bf16x2(uv[0], uv[1]), pack_bf16x2(uv[2], uv[3]));
+            }
           }
         }
       }
@@ -280,6 +291,7 @@ hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   p.tile_expert = g.tile_expert;
   p.num_tiles = g.num_tiles;
   p.out = static_cast<uint16_t*>(g.out);
+  p.gu = static_cast<uint16_t*>(g.out_scale);   // BF16 SwiGLU GEMM1: the optional saved pre-activations
   p.A = g.T * g.k;
   p.a_bytes = static_cast<uint32_t>((GEMM1 ? g.T * g.H : g.cap * g.I) * 2);
   p.H = g.H;

@@ -1,0 +1,366 @@
+// BF16 grouped GEMMs of the routed-expert MoE backward (the training pass of
+// the forward in gemm_bf16.hip; the pages' follow-up work: Liger-Kernel PR
+// #1463, MoEBenchmark results, forward and backward).
+//
+//   dH  (kDh):    dh[r, i]    = sum_c dY[r, c] W2[e, c, i], then the SwiGLU
+//                 backward with the saved pre-activations (g, u) of row r:
+//                 dGU[r, i] = dh u silu'(g), dGU[r, I + i] = dh silu(g)
+//   dX  (kDx):    dx_row[a, c] = sum_n dGU[r, n] W1[e, n, c], written to the
+//                 row of assignment a = sorted_ids[r] (pad rows dropped)
+//   dW  (kWgrad): dW[e, n, m]  = sum over expert e's sorted rows r of
+//                 P[r, m] Q[r, n] (dW2: P = h, Q = dY; dW1: P = x gathered into
+//                 sorted rows, Q = dGU), fp32 output
+//
+// Every operand sits in memory with the reduction index K as its slow index
+// for at least one side: the weights W[e] are [K, M] (M contiguous) in the
+// dgrad GEMMs, and both sorted-row operands are [K = row, M or N] in the
+// weight gradients. Such a tile is staged into LDS as it is in memory, rows
+// of K, and the MFMA fragments (8 consecutive K per lane) are read from it
+// with the gfx950 transposing LDS read ds_read_b64_tr_b16: within each group
+// of 16 lanes, lane j addresses 4 consecutive columns of row kb + j/4
+// (columns m0 + 4 (j % 4) ...), and lane i receives column m0 + i of rows
+// kb .. kb + 3. The operand whose K is contiguous (the sorted rows of dY or
+// dGU in the dgrad GEMMs) is staged and read as in the forward kernels.
+//
+// Pipeline, XCD-aware persistent task slices, zero-filled out-of-range
+// buffer loads and the 8-wave 256 x 256 workgroup tile follow the forward
+// BF16 kernels.
+#include "moe_common.cuh"
+#include "moe_launch.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int kXcds = 8;
+constexpr int kDh = 0;
+constexpr int kDx = 1;
+constexpr int kWgrad = 2;
+constexpr uint32_t kOob = 0x7FFFFFF0u;
+constexpr int BK = 64;            // K per pipeline step
+constexpr int BO = 256;           // output tile: M (and N) extent per workgroup
+constexpr int WM = 4, WN = 2;     // waves along M and N
+constexpr int WAVES = WM * WN;
+constexpr int THREADS = 64 * WAVES;
+constexpr int TM = BO / WM, TN = BO / WN;
+constexpr int FM = TM / 32, FN = TN / 32;
+constexpr int T_TILE = BK * BO * 2;      // a transposed tile: BK rows of K x BO columns
+constexpr int N_TILE = BO * BK * 2;      // a K-contiguous tile: BO rows x BK
+constexpr int STAGE = T_TILE + N_TILE;   // both tiles have the same size
+constexpr int GROUPS = STAGE / 1024;     // 1 KB direct-to-LDS loads per step
+constexpr int GPW = GROUPS / WAVES;
+static_assert(T_TILE == N_TILE && GROUPS % WAVES == 0, "uniform loads per wave");
+static_assert(2 * STAGE <= 160 * 1024, "two stages fit in LDS");
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s* lds_v4s_ptr;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+// Transposed tile: row k of the tile (one K index), 16-byte chunk c of its
+// BO columns; the chunk index is XOR-swizzled by 4 (k & 3) so that the four
+// rows one 16-lane group reads land on distinct banks.
+__device__ __forceinline__ uint32_t t_off(int k, int c) {
+  return static_cast<uint32_t>(k * (BO * 2) + ((c ^ ((k & 3) << 2)) << 4));
+}
+// K-contiguous tile: row r (one output column of the N side), 16-byte chunk c
+// of its BK elements, swizzled by r & 7 as in the forward kernels.
+__device__ __forceinline__ uint32_t n_off(int r, int c) {
+  return static_cast<uint32_t>(r * (BK * 2) + ((c ^ (r & 7)) << 4));
+}
+
+// Fragment of 8 consecutive K (k0 + 8 (lane / 32) ...) for column m_base +
+// lane % 32 of a transposed tile, by two transposing reads of 4 K each.
+__device__ __forceinline__ bf16x8 t_frag(const char* tile, int lane, int m_base, int k0) {
+  const int g16 = lane >> 4, j = lane & 15;
+  const int m0 = m_base + 16 * (g16 & 1) + 4 * (j & 3);
+  const int kb = k0 + 8 * (g16 >> 1) + (j >> 2);
+  const int c = m0 >> 3, half = (m0 & 7) * 2;            // 16-byte chunk and byte within it
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4s_ptr)(tile + t_off(kb, c) + half));
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4s_ptr)(tile + t_off(kb + 4, c) + half));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ __forceinline__ bf16x8 n_frag(const char* tile, int row, int chunk) {
+  const uint4 v = *reinterpret_cast<const uint4*>(tile + n_off(row, chunk));
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+struct Params {
+  const uint16_t* a;        // transposed operand: dgrad W [E, K, M]; wgrad P [cap, M]
+  const uint16_t* b;        // dgrad: sorted rows [cap, K]; wgrad: Q [cap, N] (transposed)
+  const uint16_t* gu;       // kDh: saved pre-activations [cap, 2M] (g in [0, M), u in [M, 2M))
+  const int32_t* sorted_ids;
+  const int32_t* tile_expert;
+  const int32_t* num_tiles;
+  const int32_t* offsets;   // kWgrad: padded expert offsets [E + 1]
+  void* out;                // kDh: dGU [cap, 2M] bf16; kDx: dx rows [A, M] bf16; kWgrad: fp32 [E, N, M]
+  int64_t A;
+  int M, N, K, E, block_m;
+  uint32_t a_bytes, b_bytes;  // bytes of the operands (below 2^31)
+};
+
+template <int MODE>
+__global__ __launch_bounds__(THREADS, 1) void gemm_bwd_kernel(Params p) {
+  constexpr bool WGRAD = MODE == kWgrad;
+  __shared__ __attribute__((aligned(1024))) char stage0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage1[STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int ntm = (p.M + BO - 1) / BO;
+  // dgrad: tasks (row tile, m tile); wgrad: (expert, n tile, m tile)
+  const int ntn_w = (p.N + BO - 1) / BO;
+  const int64_t total = WGRAD ? static_cast<int64_t>(p.E) * ntn_w * ntm : static_cast<int64_t>(*p.num_tiles) * ntm;
+
+  const int G = gridDim.x;
+  const int xcd = blockIdx.x % kXcds, local = blockIdx.x / kXcds;
+  const int per_xcd = (G + kXcds - 1 - xcd) / kXcds;
+  const int64_t t0 = total * (xcd * (G / kXcds) + (xcd < G % kXcds ? xcd : G % kXcds)) / G;
+  const int64_t t1 = total * ((xcd + 1) * (G / kXcds) + (xcd + 1 < G % kXcds ? xcd + 1 : G % kXcds)) / G;
+
+  for (int64_t task = t0 + local; task < t1; task += per_xcd) {
+    int e, m0, n0, nk;
+    int64_t row0 = 0;          // dgrad: first sorted row of the row tile; wgrad: first row of expert e
+    if (WGRAD) {
+      e = static_cast<int>(task / (static_cast<int64_t>(ntn_w) * ntm));
+      const int rem = static_cast<int>(task - static_cast<int64_t>(e) * ntn_w * ntm);
+      n0 = (rem / ntm) * BO;
+      m0 = (rem % ntm) * BO;
+      row0 = p.offsets[e];
+      nk = (p.offsets[e + 1] - p.offsets[e] + BK - 1) / BK;
+    } else {
+      const int rt = static_cast<int>(task / ntm);
+      m0 = static_cast<int>(task - static_cast<int64_t>(rt) * ntm) * BO;
+      e = p.tile_expert[rt];
+      row0 = static_cast<int64_t>(rt) * p.block_m;
+      n0 = 0;
+      nk = (p.K + BK - 1) / BK;
+    }
+    const int rows_e = WGRAD ? p.offsets[e + 1] - p.offsets[e] : 0;
+
+    // A (transposed): dgrad W[e] rows of K; wgrad P rows of expert e
+    const __amdgpu_buffer_rsrc_t a_rsrc =
+        WGRAD ? make_rsrc(p.a, p.a_bytes)
+              : make_rsrc(p.a + static_cast<int64_t>(e) * p.K * p.M, static_cast<uint32_t>(p.K) * p.M * 2);
+    const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(p.b, p.b_bytes);
+
+    // per-lane source of each 1 KB group: groups [0, GROUPS/2) fill the A
+    // tile, the rest the B tile. A transposed tile row is BO * 2 = 512 bytes,
+    // so a group covers 2 rows; a K-contiguous row is 128 bytes, 8 per group.
+    uint32_t off[GPW];
+    int krow[GPW];                 // K row (transposed tiles) or K column of the chunk (K-contiguous tile)
+#pragma unroll
+    for (int q = 0; q < GPW; ++q) {
+      const int grp = wave * GPW + q;
+      off[q] = kOob;
+      krow[q] = 0;
+      const bool in_a = grp < GROUPS / 2;
+      const int gl = in_a ? grp : grp - GROUPS / 2;
+      if (in_a || WGRAD) {
+        // transposed tile: row k = 2 gl + lane / 32, physical chunk lane % 32
+        const int k = 2 * gl + (lane >> 5), pc = lane & 31;
+        const int lc = pc ^ ((k & 3) << 2);
+        const int col = (in_a ? m0 : n0) + lc * 8;
+        const int width = in_a ? p.M : p.N;
+        krow[q] = k;
+        if (col < width) {
+          if (WGRAD)
+            off[q] = static_cast<uint32_t>((row0 + k) * width + col) * 2;
+          else
+            off[q] = static_cast<uint32_t>(k * width + col) * 2;
+        }
+      } else {
+        // K-contiguous rows of the sorted operand: row r = 8 gl + lane / 8
+        const int r = 8 * gl + (lane >> 3), pc = lane & 7;
+        const int lc = pc ^ (r & 7);
+        krow[q] = lc * 8;
+        off[q] = static_cast<uint32_t>((row0 + r) * p.K + lc * 8) * 2;
+      }
+    }
+    // issue the loads of step kt into `stage`; rows / columns past the end
+    // (and steps past the end) read zeros
+    auto load = [&](char* stage, int kt) {
+#pragma unroll
+      for (int q = 0; q < GPW; ++q) {
+        const int grp = wave * GPW + q;
+        const bool in_a = grp < GROUPS / 2;
+        uint32_t o, soff;
+        if (in_a || WGRAD) {
+          const int width = in_a ? p.M : p.N;
+          const int k = kt * BK + krow[q];
+          const bool live = WGRAD ? k < rows_e : k < p.K;
+          o = live ? off[q] : kOob;
+          soff = static_cast<uint32_t>(kt) * BK * width * 2;
+        } else {
+          o = kt * BK + krow[q] < p.K ? off[q] : kOob;
+          soff = static_cast<uint32_t>(kt) * BK * 2;
+        }
+        const __amdgpu_buffer_rsrc_t rsrc = in_a ? a_rsrc : b_rsrc;
+        char* const dst = stage + grp * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)dst, 16, o, soff, 0, 0);
+      }
+    };
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+
+    auto compute = [&](const char* base) {
+      const char* ta = base;
+      const char* tb = base + T_TILE;
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        bf16x8 af[FM];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) af[i] = t_frag(ta, lane, wm * TM + i * 32, kk * 16);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const bf16x8 bf = WGRAD ? t_frag(tb, lane, wn * TN + j * 32, kk * 16)
+                                  : n_frag(tb, wn * TN + j * 32 + (lane & 31), kk * 2 + (lane >> 5));
+#pragma unroll
+          for (int i = 0; i < FM; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf, acc[i][j], 0, 0, 0);
+        }
+      }
+    };
+
+    load(stage0, 0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt += 2) {
+      load(stage1, kt + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(stage0);
+      __syncthreads();
+      load(stage0, kt + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(stage1);
+      __syncthreads();
+    }
+
+    // epilogue: lane holds M indices 8 (v / 4) + 4 (lane / 32) + v % 4 of N index lane % 32
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int nl = wn * TN + j * 32 + (lane & 31);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int m = m0 + wm * TM + i * 32 + g * 8 + (lane >> 5) * 4;
+          if (m >= p.M) continue;
+          const float a4[4] = {acc[i][j][g * 4], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2], acc[i][j][g * 4 + 3]};
+          if (MODE == kWgrad) {
+            const int n = n0 + nl;
+            if (n < p.N) {
+              float4 st = make_float4(a4[0], a4[1], a4[2], a4[3]);
+              *reinterpret_cast<float4*>(static_cast<float*>(p.out) +
+                                         (static_cast<int64_t>(e) * p.N + n) * p.M + m) = st;
+            }
+          } else if (MODE == kDh) {
+            const int64_t r = row0 + nl;
+            const uint2 gq = *reinterpret_cast<const uint2*>(p.gu + r * 2 * p.M + m);
+            const uint2 uq = *reinterpret_cast<const uint2*>(p.gu + r * 2 * p.M + p.M + m);
+            const uint32_t gw[2] = {gq.x, gq.y}, uw[2] = {uq.x, uq.y};
+            float dg[4], du[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const uint32_t gb = (gw[v >> 1] >> (16 * (v & 1))) & 0xFFFFu;
+              const uint32_t ub = (uw[v >> 1] >> (16 * (v & 1))) & 0xFFFFu;
+              const float gv = __uint_as_float(gb << 16), uv = __uint_as_float(ub << 16);
+              const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gv));
+              dg[v] = a4[v] * uv * sg * (1.0f + gv * (1.0f - sg));
+              du[v] = a4[v] * gv * sg;
+            }
+            uint16_t* o = static_cast<uint16_t*>(p.out) + r * 2 * p.M + m;
+            *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+            *reinterpret_cast<uint2*>(o + p.M) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+          } else {
+            const int sid = p.sorted_ids[row0 + nl];
+            if (sid < p.A) {
+              uint16_t* o = static_cast<uint16_t*>(p.out) + static_cast<int64_t>(sid) * p.M + m;
+              *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(a4[0], a4[1]), pack_bf16x2(a4[2], a4[3]));
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int MODE>
+hipError_t launch(const Params& p, int64_t tasks, const DeviceInfo& dev, hipStream_t s) {
+  int64_t grid = dev.num_cus;
+  if (grid > tasks) grid = tasks;
+  if (grid < 1) grid = 1;
+  gemm_bwd_kernel<MODE><<<static_cast<unsigned>(grid), THREADS, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool gemm_bwd_supports(int block_m) { return block_m == 256; }
+
+hipError_t launch_bwd_dh(const BwdArgs& g, const DeviceInfo& dev, hipStream_t s) {
+  Params p{};
+  p.a = static_cast<const uint16_t*>(g.w2);
+  p.b = static_cast<const uint16_t*>(g.dy);
+  p.gu = static_cast<const uint16_t*>(g.gu);
+  p.sorted_ids = g.sorted_ids;
+  p.tile_expert = g.tile_expert;
+  p.num_tiles = g.num_tiles;
+  p.out = g.dgu;
+  p.A = g.A;
+  p.M = g.I;
+  p.N = g.block_m;
+  p.K = g.H;
+  p.E = g.E;
+  p.block_m = g.block_m;
+  p.b_bytes = static_cast<uint32_t>(g.cap * g.H * 2);
+  return launch<kDh>(p, (g.cap / g.block_m) * ((g.I + BO - 1) / BO), dev, s);
+}
+
+hipError_t launch_bwd_dx(const BwdArgs& g, const DeviceInfo& dev, hipStream_t s) {
+  Params p{};
+  p.a = static_cast<const uint16_t*>(g.w1);
+  p.b = static_cast<const uint16_t*>(g.dgu);
+  p.sorted_ids = g.sorted_ids;
+  p.tile_expert = g.tile_expert;
+  p.num_tiles = g.num_tiles;
+  p.out = g.dx_rows;
+  p.A = g.A;
+  p.M = g.H;
+  p.N = g.block_m;
+  p.K = 2 * g.I;
+  p.E = g.E;
+  p.block_m = g.block_m;
+  p.b_bytes = static_cast<uint32_t>(g.cap * 2 * g.I * 2);
+  return launch<kDx>(p, (g.cap / g.block_m) * ((g.H + BO - 1) / BO), dev, s);
+}
+
+hipError_t launch_bwd_wgrad(const void* pm, const void* qn, int M, int N, const BwdArgs& g, float* dw,
+                            const DeviceInfo& dev, hipStream_t s) {
+  Params p{};
+  p.a = static_cast<const uint16_t*>(pm);
+  p.b = static_cast<const uint16_t*>(qn);
+  p.offsets = g.offsets;
+  p.num_tiles = g.num_tiles;
+  p.out = dw;
+  p.A = g.A;
+  p.M = M;
+  p.N = N;
+  p.K = 0;
+  p.E = g.E;
+  p.block_m = g.block_m;
+  p.a_bytes = static_cast<uint32_t>(g.cap * M * 2);
+  p.b_bytes = static_cast<uint32_t>(g.cap * N * 2);
+  return launch<kWgrad>(p, static_cast<int64_t>(g.E) * ((N + BO - 1) / BO) * ((M + BO - 1) / BO), dev, s);
+}
+
+}  // namespace moe

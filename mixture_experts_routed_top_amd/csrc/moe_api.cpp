@@ -233,10 +233,27 @@ moe_status_t moe_grouped_gemm_swiglu(int32_t dtype, const void* x, const void* x
                   T, H, I, E, k, block_m, cap};
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (dtype) {
-    case MOE_DTYPE_BF16: return launched(moe::launch_gemm1_bf16(g, dev, s));
+    case MOE_DTYPE_BF16:
+      g.out_scale = nullptr;   // (h_scale is ignored on the BF16 path)
+      return launched(moe::launch_gemm1_bf16(g, dev, s));
     case MOE_DTYPE_FP8_BLOCK128: return launched(moe::launch_gemm1_fp8(g, dev, s));
     default: return launched(moe::launch_gemm1_mx(g, dev, s));
   }
+}
+
+moe_status_t moe_grouped_gemm_swiglu_save(const void* x, const void* w1, const int32_t* sorted_ids,
+                                          const int32_t* tile_expert, const int32_t* num_tiles, int64_t T,
+                                          int32_t H, int32_t I, int32_t E, int32_t k, int32_t block_m, int64_t cap,
+                                          void* h, void* gu, void* stream) {
+  if (moe_status_t st = check_gemm(MOE_DTYPE_BF16, x, nullptr, w1, nullptr, sorted_ids, tile_expert, num_tiles, T,
+                                   H, I, E, k, block_m, cap, h, nullptr, true))
+    return st;
+  if (T == 0) return MOE_OK;
+  if (!gu || !aligned(gu, 16)) return MOE_ERR_INVALID_ARG;
+  moe::DeviceInfo dev;
+  if (moe_status_t st = current_device(&dev)) return st;
+  moe::GemmArgs g{x, nullptr, w1, nullptr, sorted_ids, tile_expert, num_tiles, h, gu, T, H, I, E, k, block_m, cap};
+  return launched(moe::launch_gemm1_bf16(g, dev, static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_grouped_gemm_relu2(int32_t dtype, const void* x, const void* x_scale, const void* w1,
@@ -274,6 +291,111 @@ moe_status_t moe_grouped_gemm_down(int32_t dtype, const void* h, const void* h_s
     case MOE_DTYPE_FP8_BLOCK128: return launched(moe::launch_gemm2_fp8(g, dev, s));
     default: return launched(moe::launch_gemm2_mx(g, dev, s));
   }
+}
+
+// ------------------------------------------------------------------ backward (BF16)
+namespace {
+
+moe_status_t check_bwd(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k, int32_t block_m, int64_t cap) {
+  if (T < 0 || H <= 0 || I <= 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > MOE_MAX_TOPK)
+    return MOE_ERR_INVALID_ARG;
+  if (!valid_block_m(block_m)) return MOE_ERR_INVALID_ARG;
+  if (T > (int64_t{1} << 31) / k) return MOE_ERR_INVALID_ARG;
+  if (cap != capacity(T, k, E, block_m) || cap >= (int64_t{1} << 31)) return MOE_ERR_INVALID_ARG;
+  if (H % 8 || I % 8) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (!moe::gemm_bwd_supports(block_m)) return MOE_ERR_UNSUPPORTED_SHAPE;
+  // 32-bit buffer offsets: the sorted-row operands and one expert's weights
+  const int64_t big = cap * int64_t{2} * I * 2 > cap * int64_t{H} * 2 ? cap * int64_t{2} * I * 2 : cap * int64_t{H} * 2;
+  if (big >= (int64_t{1} << 31) || int64_t{2} * I * H * 2 >= (int64_t{1} << 31)) return MOE_ERR_UNSUPPORTED_SHAPE;
+  return MOE_OK;
+}
+
+}  // namespace
+
+moe_status_t moe_backward_combine(const uint16_t* dout, const float* topk_w, const uint16_t* y,
+                                  const int32_t* sorted_ids, int64_t T, int32_t k, int32_t H, int64_t cap,
+                                  uint16_t* dy, float* dw, void* stream) {
+  if (T < 0 || k < 1 || k > MOE_MAX_TOPK || H <= 0 || cap < 0) return MOE_ERR_INVALID_ARG;
+  if (H % 8) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (T == 0 || cap == 0) return MOE_OK;
+  if (!dout || !topk_w || !y || !sorted_ids || !dy || !dw) return MOE_ERR_INVALID_ARG;
+  if (!aligned(dout, 16) || !aligned(y, 16) || !aligned(dy, 16) || !aligned(topk_w, 4) || !aligned(dw, 4))
+    return MOE_ERR_INVALID_ARG;
+  moe::DeviceInfo dev;
+  if (moe_status_t st = current_device(&dev)) return st;
+  return launched(moe::launch_backward_combine(dout, topk_w, y, sorted_ids, T * k, k, H, cap, dy, dw,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_route_backward(const float* topk_w, const int32_t* topk_ids, const float* dw, int64_t T,
+                                int32_t E, int32_t k, int32_t n_shared, int32_t score, float* dlogits,
+                                void* stream) {
+  if (T < 0 || E < 1 || k < 1 || k > E || n_shared < 0 || k + n_shared > MOE_MAX_TOPK) return MOE_ERR_INVALID_ARG;
+  if (score != MOE_SCORE_SOFTMAX && score != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!topk_w || !topk_ids || !dw || !dlogits) return MOE_ERR_INVALID_ARG;
+  moe::DeviceInfo dev;
+  if (moe_status_t st = current_device(&dev)) return st;
+  return launched(moe::launch_route_backward(topk_w, topk_ids, dw, T, E, k, k + n_shared, score, dlogits,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_gather_rows(const uint16_t* x, const int32_t* sorted_ids, int64_t T, int32_t k, int32_t H,
+                             int64_t cap, uint16_t* x_sorted, void* stream) {
+  if (T < 0 || k < 1 || H <= 0 || cap < 0) return MOE_ERR_INVALID_ARG;
+  if (H % 8) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (T == 0 || cap == 0) return MOE_OK;
+  if (!x || !sorted_ids || !x_sorted || !aligned(x, 16) || !aligned(x_sorted, 16)) return MOE_ERR_INVALID_ARG;
+  moe::DeviceInfo dev;
+  if (moe_status_t st = current_device(&dev)) return st;
+  return launched(moe::launch_gather_rows(x, sorted_ids, T * k, k, H, cap, x_sorted, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_grouped_gemm_dh(const void* dy, const void* w2, const void* gu, const int32_t* sorted_ids,
+                                 const int32_t* tile_expert, const int32_t* num_tiles, int64_t T, int32_t H,
+                                 int32_t I, int32_t E, int32_t k, int32_t block_m, int64_t cap, void* dgu,
+                                 void* stream) {
+  if (moe_status_t st = check_bwd(T, H, I, E, k, block_m, cap)) return st;
+  if (T == 0) return MOE_OK;
+  if (!dy || !w2 || !gu || !dgu || !sorted_ids || !tile_expert || !num_tiles) return MOE_ERR_INVALID_ARG;
+  if (!aligned(dy, 16) || !aligned(w2, 16) || !aligned(gu, 16) || !aligned(dgu, 16)) return MOE_ERR_INVALID_ARG;
+  moe::DeviceInfo dev;
+  if (moe_status_t st = current_device(&dev)) return st;
+  moe::BwdArgs g{nullptr, w2, dy, gu, dgu, nullptr, sorted_ids, tile_expert, num_tiles, nullptr,
+                 T * k, H, I, E, block_m, cap};
+  return launched(moe::launch_bwd_dh(g, dev, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_grouped_gemm_dx(const void* dgu, const void* w1, const int32_t* sorted_ids,
+                                 const int32_t* tile_expert, const int32_t* num_tiles, int64_t T, int32_t H,
+                                 int32_t I, int32_t E, int32_t k, int32_t block_m, int64_t cap, void* dx_rows,
+                                 void* stream) {
+  if (moe_status_t st = check_bwd(T, H, I, E, k, block_m, cap)) return st;
+  if (T == 0) return MOE_OK;
+  if (!dgu || !w1 || !dx_rows || !sorted_ids || !tile_expert || !num_tiles) return MOE_ERR_INVALID_ARG;
+  if (!aligned(dgu, 16) || !aligned(w1, 16) || !aligned(dx_rows, 16)) return MOE_ERR_INVALID_ARG;
+  moe::DeviceInfo dev;
+  if (moe_status_t st = current_device(&dev)) return st;
+  moe::BwdArgs g{w1, nullptr, nullptr, nullptr, const_cast<void*>(dgu), dx_rows, sorted_ids, tile_expert, num_tiles,
+                 nullptr, T * k, H, I, E, block_m, cap};
+  return launched(moe::launch_bwd_dx(g, dev, static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_grouped_gemm_wgrad(const void* p_rows, const void* q_rows, int32_t M, int32_t N,
+                                    const int32_t* offsets, int64_t T, int32_t E, int32_t k, int32_t block_m,
+                                    int64_t cap, float* dw, void* stream) {
+  if (M <= 0 || N <= 0) return MOE_ERR_INVALID_ARG;
+  if (moe_status_t st = check_bwd(T, N, M, E, k, block_m, cap)) return st;
+  if (T == 0) return MOE_OK;
+  if (cap * int64_t{M} * 2 >= (int64_t{1} << 31) || cap * int64_t{N} * 2 >= (int64_t{1} << 31))
+    return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (!p_rows || !q_rows || !offsets || !dw) return MOE_ERR_INVALID_ARG;
+  if (!aligned(p_rows, 16) || !aligned(q_rows, 16) || !aligned(dw, 16)) return MOE_ERR_INVALID_ARG;
+  moe::DeviceInfo dev;
+  if (moe_status_t st = current_device(&dev)) return st;
+  moe::BwdArgs g{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, offsets,
+                 T * k, 0, 0, E, block_m, cap};
+  return launched(moe::launch_bwd_wgrad(p_rows, q_rows, M, N, g, dw, dev, static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_combine(const uint16_t* y, const float* topk_w, int64_t T, int32_t k, int32_t H,

@@ -54,6 +54,35 @@ hipError_t launch_gemm1_bf16(const GemmArgs& g, const DeviceInfo& dev, hipStream
 hipError_t launch_gemm2_bf16(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s);
 hipError_t launch_gemm1_relu2_bf16(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s);
 
+// Backward (BF16): operands of the dgrad and weight-gradient GEMMs.
+struct BwdArgs {
+  const void* w1;          // [E, 2I, H]
+  const void* w2;          // [E, H, I]
+  const void* dy;          // [cap, H] sorted rows
+  const void* gu;          // [cap, 2I] saved pre-activations
+  void* dgu;               // [cap, 2I] (written by dh, read by dx)
+  void* dx_rows;           // [A, H] assignment order
+  const int32_t* sorted_ids;
+  const int32_t* tile_expert;
+  const int32_t* num_tiles;
+  const int32_t* offsets;  // [E + 1] padded offsets
+  int64_t A;
+  int H, I, E, block_m;
+  int64_t cap;
+};
+bool gemm_bwd_supports(int block_m);
+hipError_t launch_bwd_dh(const BwdArgs& g, const DeviceInfo& dev, hipStream_t s);
+hipError_t launch_bwd_dx(const BwdArgs& g, const DeviceInfo& dev, hipStream_t s);
+hipError_t launch_bwd_wgrad(const void* pm, const void* qn, int M, int N, const BwdArgs& g, float* dw,
+                            const DeviceInfo& dev, hipStream_t s);
+hipError_t launch_backward_combine(const uint16_t* dout, const float* w, const uint16_t* y,
+                                   const int32_t* sorted_ids, int64_t A, int kk, int H, int64_t rows,
+                                   uint16_t* dy, float* dw, hipStream_t s);
+hipError_t launch_route_backward(const float* w, const int32_t* ids, const float* dw, int64_t T, int E, int k,
+                                 int kk, int score, float* dlogits, hipStream_t s);
+hipError_t launch_gather_rows(const uint16_t* x, const int32_t* sorted_ids, int64_t A, int kk, int H, int64_t rows,
+                              uint16_t* out, hipStream_t s);
+
 bool gemm_fp8_supports(int block_m);
 hipError_t launch_gemm1_fp8(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s);
 hipError_t launch_gemm2_fp8(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s);

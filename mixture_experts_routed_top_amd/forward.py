@@ -1,6 +1,11 @@
 """The routed forward as one object: weights prepared once, buffers planned
 per token count, then route -> align_sort -> [quantise x] -> GEMM1+activation ->
 GEMM2 -> combine on one stream with no allocation and no host sync.
+
+For the BF16 SwiGLU layer, forward_train / backward run one training step
+over the same sorted layout: the forward also keeps the pre-activations, and
+the backward chains combine-backward -> router-backward -> dGU -> dx rows ->
+dx, and the two weight gradients.
 """
 from __future__ import annotations
 
@@ -25,6 +30,23 @@ class Plan:
     h_scale: Optional[torch.Tensor]
     y: torch.Tensor
     out: torch.Tensor
+    train: Optional["TrainBuffers"] = None
+
+
+@dataclass
+class TrainBuffers:
+    """What the backward reads from the forward, and the gradient outputs."""
+    gu: torch.Tensor          # [cap, 2I] bf16 pre-activations
+    dy: torch.Tensor          # [cap, H] bf16
+    dw: torch.Tensor          # [T, k] fp32 gate-weight gradient
+    dlogits: torch.Tensor     # [T, E_routed] fp32
+    dgu: torch.Tensor         # [cap, 2I] bf16
+    dx_rows: torch.Tensor     # [T*k, H] bf16
+    dx: torch.Tensor          # [T, H] bf16
+    x_sorted: torch.Tensor    # [cap, H] bf16
+    ones: torch.Tensor        # [T, k] fp32, unit weights of the dx reduction
+    dw1: torch.Tensor         # [E, 2I, H] fp32
+    dw2: torch.Tensor         # [E, H, I] fp32
 
 
 class MoeLayer:
@@ -64,8 +86,12 @@ class MoeLayer:
         else:
             raise ValueError("unknown dtype")
 
-    def plan(self, T: int, block_m: Optional[int] = None, device=None) -> Plan:
+    def plan(self, T: int, block_m: Optional[int] = None, device=None, train: bool = False) -> Plan:
         device = device or self.w1.device
+        if train:
+            if self.dtype != B.DTYPE_BF16 or self.act != B.ACT_SWIGLU:
+                raise ValueError("the training step is implemented for the BF16 SwiGLU layer")
+            block_m = 256                                  # the backward GEMMs' row tile
         bm = block_m or B.moe_pick_block_m(self.dtype, T, self.k, self.E, self.H, self.I)
         sort = B.SortResult(T, self.k, self.E, bm, device)
         xq = xs = None
@@ -76,12 +102,28 @@ class MoeLayer:
             xq = torch.empty((T, self.H), dtype=torch.uint8, device=device)
             xs = torch.empty((T, self.H // 32), dtype=torch.uint8, device=device)
         h, h_scale = B._h_alloc(self.dtype, max(sort.cap, 1), self.I, device)
+        tb = None
+        if train:
+            cap, A, H, I, E = max(sort.cap, 1), max(T * self.k, 1), self.H, self.I, self.E
+            bf, f32 = torch.bfloat16, torch.float32
+            tb = TrainBuffers(
+                gu=torch.empty((cap, 2 * I), dtype=bf, device=device),
+                dy=torch.empty((cap, H), dtype=bf, device=device),
+                dw=torch.empty((T, self.k), dtype=f32, device=device),
+                dlogits=torch.empty((T, E - self.n_shared), dtype=f32, device=device),
+                dgu=torch.empty((cap, 2 * I), dtype=bf, device=device),
+                dx_rows=torch.empty((A, H), dtype=bf, device=device),
+                dx=torch.empty((T, H), dtype=bf, device=device),
+                x_sorted=torch.empty((cap, H), dtype=bf, device=device),
+                ones=torch.ones((T, self.k), dtype=f32, device=device),
+                dw1=torch.empty((E, 2 * I, H), dtype=f32, device=device),
+                dw2=torch.empty((E, H, I), dtype=f32, device=device))
         return Plan(T, bm,
                     torch.empty((T, self.k), dtype=torch.int32, device=device),
                     torch.empty((T, self.k), dtype=torch.float32, device=device),
                     sort, xq, xs, h, h_scale,
                     torch.empty((max(T * self.k, 1), self.H), dtype=torch.bfloat16, device=device),
-                    torch.empty((T, self.H), dtype=torch.bfloat16, device=device))
+                    torch.empty((T, self.H), dtype=torch.bfloat16, device=device), tb)
 
     def forward(self, x: torch.Tensor, logits: torch.Tensor, plan: Optional[Plan] = None,
                 stream=None) -> torch.Tensor:
@@ -89,10 +131,7 @@ class MoeLayer:
         p = plan if plan is not None else self.plan(T, device=x.device)
         if p.T != T:
             raise ValueError("plan was made for another token count")
-        if self.n_shared:
-            B.moe_route_shared(logits, self.k_routed, self.score, self.n_shared, p.ids, p.w, stream=stream)
-        else:
-            B.moe_route(logits, self.k, self.score, p.ids, p.w, stream=stream)
+        self._route(logits, p, stream)
         B.moe_align_sort(p.ids, self.E, p.block_m, out=p.sort, stream=stream)
         if self.dtype == B.DTYPE_BF16:
             a, a_scale = x, None
@@ -108,3 +147,37 @@ class MoeLayer:
         return B.moe_combine(p.y, p.w, p.out, stream=stream)
 
     __call__ = forward
+
+    def _route(self, logits, p: Plan, stream):
+        if self.n_shared:
+            B.moe_route_shared(logits, self.k_routed, self.score, self.n_shared, p.ids, p.w, stream=stream)
+        else:
+            B.moe_route(logits, self.k, self.score, p.ids, p.w, stream=stream)
+
+    def forward_train(self, x: torch.Tensor, logits: torch.Tensor, plan: Plan, stream=None) -> torch.Tensor:
+        """The BF16 SwiGLU forward that keeps what backward needs (plan made with train=True)."""
+        if plan.train is None or plan.T != x.shape[0]:
+            raise ValueError("forward_train needs a training plan for this token count")
+        p = plan
+        self._route(logits, p, stream)
+        B.moe_align_sort(p.ids, self.E, p.block_m, out=p.sort, stream=stream)
+        B.moe_grouped_gemm_swiglu_save(x, self.w1, p.sort, self.H, self.I, p.h, p.train.gu, stream=stream)
+        B.moe_grouped_gemm_down(self.dtype, p.h, None, self.w2, None, p.sort, self.H, self.I, p.y, stream=stream)
+        return B.moe_combine(p.y, p.w, p.out, stream=stream)
+
+    def backward(self, x: torch.Tensor, dout: torch.Tensor, plan: Plan, stream=None) -> TrainBuffers:
+        """Gradients for dout of the last forward_train with this plan: dx, dlogits, dw1, dw2 (fp32)."""
+        p, tb = plan, plan.train
+        if tb is None:
+            raise ValueError("backward needs a training plan")
+        H, I = self.H, self.I
+        B.moe_backward_combine(dout, p.w, p.y, p.sort, tb.dy, tb.dw, stream=stream)
+        B.moe_route_backward(p.w, p.ids, tb.dw, self.E - self.n_shared, self.k_routed, self.score, self.n_shared,
+                             tb.dlogits, stream=stream)
+        B.moe_grouped_gemm_dh(tb.dy, self.w2, tb.gu, p.sort, H, I, tb.dgu, stream=stream)
+        B.moe_grouped_gemm_dx(tb.dgu, self.w1, p.sort, H, I, tb.dx_rows, stream=stream)
+        B.moe_combine(tb.dx_rows, tb.ones, tb.dx, stream=stream)
+        B.moe_gather_rows(x, p.sort, tb.x_sorted, stream=stream)
+        B.moe_grouped_gemm_wgrad(p.h, tb.dy, p.sort, tb.dw2, stream=stream)
+        B.moe_grouped_gemm_wgrad(tb.x_sorted, tb.dgu, p.sort, tb.dw1, stream=stream)
+        return tb

@@ -33,7 +33,8 @@ def test_header_declares_the_boundary():
     for n in ["moe_route", "moe_align_sort", "moe_grouped_gemm_swiglu", "moe_grouped_gemm_down",
               "moe_combine", "moe_quantize_fp8", "moe_quantize_mxfp8", "moe_quantize_mxfp4",
               "moe_sorted_capacity", "moe_align_sort_workspace_bytes", "moe_pick_block_m",
-              "moe_status_string"]:
+              "moe_status_string", "moe_grouped_gemm_swiglu_save", "moe_backward_combine", "moe_route_backward",
+              "moe_gather_rows", "moe_grouped_gemm_dh", "moe_grouped_gemm_dx", "moe_grouped_gemm_wgrad"]:
         assert n in names, n
 
 
@@ -146,6 +147,40 @@ def test_combine_host_validation():
     assert L.moe_combine(FAKE, FAKE, 4, 0, 128, FAKE, NULL) == 1
     assert L.moe_combine(MIS, FAKE, 4, 2, 128, FAKE, NULL) == 1
     assert L.moe_combine(NULL, NULL, 0, 2, 128, NULL, NULL) == 0
+
+
+def test_backward_host_validation():
+    L = _lib()
+    T, k, E, H, I = 64, 2, 4, 128, 64
+    cap = O.sorted_capacity(T, k, E, 256)
+    dh = lambda T=T, H=H, I=I, bm=256, cap=cap, dy=FAKE, gu=FAKE: L.moe_grouped_gemm_dh(
+        dy, FAKE, gu, FAKE, FAKE, FAKE, T, H, I, E, k, bm, cap, FAKE, NULL)
+    dx = lambda T=T, H=H, I=I, bm=256, cap=cap, dgu=FAKE: L.moe_grouped_gemm_dx(
+        dgu, FAKE, FAKE, FAKE, FAKE, T, H, I, E, k, bm, cap, FAKE, NULL)
+    wg = lambda M=I, N=H, bm=256, cap=cap, p=FAKE, dw=FAKE: L.moe_grouped_gemm_wgrad(
+        p, FAKE, M, N, FAKE, T, E, k, bm, cap, dw, NULL)
+    for f in (dh, dx):
+        assert f(H=100) == 2                     # H % 8
+        assert f(I=60) == 2                      # I % 8
+        assert f(bm=64, cap=O.sorted_capacity(T, k, E, 64)) == 2   # the backward GEMMs tile 256 rows
+        assert f(bm=48) == 1
+        assert f(cap=cap + 256) == 1
+        assert f(T=0, cap=0) == 0
+    assert dh(dy=NULL) == 1 and dh(gu=MIS) == 1 and dx(dgu=MIS) == 1
+    assert wg(M=100) == 2 and wg(N=36) == 2 and wg(M=0) == 1
+    assert wg(bm=128, cap=O.sorted_capacity(T, k, E, 128)) == 2
+    assert wg(p=NULL) == 1 and wg(dw=MIS) == 1
+    save = lambda h=FAKE, gu=FAKE, T=T, cap=cap: L.moe_grouped_gemm_swiglu_save(
+        FAKE, FAKE, FAKE, FAKE, FAKE, T, H, I, E, k, 256, cap, h, gu, NULL)
+    assert save(gu=NULL) == 1 and save(gu=MIS) == 1 and save(T=0, cap=0, gu=NULL) == 0
+    assert L.moe_backward_combine(FAKE, FAKE, FAKE, FAKE, T, k, 100, cap, FAKE, FAKE, NULL) == 2
+    assert L.moe_backward_combine(FAKE, FAKE, MIS, FAKE, T, k, H, cap, FAKE, FAKE, NULL) == 1
+    assert L.moe_backward_combine(NULL, NULL, NULL, NULL, 0, k, H, cap, NULL, NULL, NULL) == 0
+    assert L.moe_route_backward(FAKE, FAKE, FAKE, T, E, 5, 0, 0, FAKE, NULL) == 1     # k > E
+    assert L.moe_route_backward(FAKE, FAKE, FAKE, T, E, 2, 0, 7, FAKE, NULL) == 1     # unknown score
+    assert L.moe_route_backward(FAKE, FAKE, NULL, T, E, 2, 0, 0, FAKE, NULL) == 1
+    assert L.moe_gather_rows(FAKE, FAKE, T, k, 100, cap, FAKE, NULL) == 2
+    assert L.moe_gather_rows(FAKE, FAKE, T, k, H, cap, MIS, NULL) == 1
 
 
 def test_device_check_without_gpu():

@@ -1,0 +1,114 @@
+"""GPU training step of the BF16 SwiGLU layer (forward with saved
+pre-activations, then every backward call through the C ABI) against the
+oracle's backward, on every element of every stored intermediate and
+gradient.
+
+Tolerances. Each bf16 intermediate (gu, dY, dGU, dx rows, dx) is the RN
+rounding of a value the kernel accumulates in fp32 and the oracle in fp64, so
+the two differ by at most one bf16 step wherever the fp32 error crosses a
+rounding boundary, plus what earlier such flips carry downstream: relative
+Frobenius error <= 5e-3 (one step is 2^-8 relative; only a small fraction of
+elements flips). The fp32 outputs (dw, dW1, dW2) inherit the same flips in
+their bf16 operands: relative Frobenius <= 5e-3. dlogits subtracts the
+weighted mean of dw (softmax), which cancels: judged against its largest
+element (atol 1e-2 of max) and by relative Frobenius <= 1e-2.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_routed_top_amd as M
+from oracle import moe as O
+from workloads import get_config, make_dout, make_inputs, to_f64
+from tests.gpu_util import cuda, f64, rel_fro, say
+
+pytestmark = pytest.mark.gpu
+
+TOL = 5e-3
+TOL_DLOGITS = 1e-2
+
+
+def _train_step(cfg, inp, dout):
+    layer = M.MoeLayer(M.DTYPE_BF16, cuda(inp.w1), cuda(inp.w2), cfg.k, cfg.score, n_shared=cfg.n_shared)
+    plan = layer.plan(cfg.T, train=True)
+    x = cuda(inp.x)
+    out = layer.forward_train(x, cuda(inp.logits), plan)
+    tb = layer.backward(x, cuda(dout), plan)
+    torch.cuda.synchronize()
+    return layer, plan, out, tb
+
+
+def _check(cfg, seed=0, inp=None):
+    inp = inp or make_inputs(cfg, seed=seed)
+    dout = make_dout(cfg, seed)
+    say("backward", cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.score, cfg.n_shared)
+    layer, plan, out, tb = _train_step(cfg, inp, dout)
+    ref = O.moe_backward(inp.logits.numpy(), to_f64(inp.x), to_f64(inp.w1), to_f64(inp.w2), to_f64(dout), cfg.k,
+                         cfg.score, block_m=256, n_shared=cfg.n_shared)
+    # routing and layout: exact
+    np.testing.assert_array_equal(plan.ids.cpu().numpy(), ref["ids"])
+    nt = int(plan.sort.num_tiles.item())
+    assert nt == ref["num_tiles"]
+    rows = nt * 256
+    np.testing.assert_array_equal(plan.sort.sorted_ids.cpu().numpy()[:rows], ref["sorted_ids"][:rows])
+    # forward intermediates
+    assert rel_fro(f64(tb.gu)[:rows], ref["gu"]) <= TOL
+    assert rel_fro(f64(plan.h)[:rows], ref["h"]) <= TOL
+    assert rel_fro(f64(plan.y), ref["y"]) <= TOL
+    # backward
+    assert rel_fro(f64(tb.dy)[:rows], ref["dy"]) <= TOL
+    assert rel_fro(tb.dw.cpu().numpy(), ref["dw"]) <= TOL
+    dl, dl_ref = tb.dlogits.cpu().numpy().astype(np.float64), ref["dlogits"]
+    assert rel_fro(dl, dl_ref) <= TOL_DLOGITS
+    np.testing.assert_allclose(dl, dl_ref, rtol=0, atol=TOL_DLOGITS * max(np.abs(dl_ref).max(), 1e-30))
+    # unselected experts carry exactly zero
+    sel = np.zeros_like(dl_ref, dtype=bool)
+    np.put_along_axis(sel, ref["ids"][:, :cfg.k].astype(np.int64), True, axis=1)
+    assert np.all(dl[~sel] == 0)
+    assert rel_fro(f64(tb.dgu)[:rows], ref["dgu"]) <= TOL
+    assert rel_fro(f64(tb.dx_rows), ref["dx_rows"]) <= TOL
+    assert rel_fro(f64(tb.dx), ref["dx"]) <= TOL
+    dw1, dw2 = tb.dw1.cpu().numpy(), tb.dw2.cpu().numpy()
+    assert rel_fro(dw1, ref["dw1"]) <= TOL
+    assert rel_fro(dw2, ref["dw2"]) <= TOL
+    # experts without rows have exactly zero weight gradients
+    counts = np.bincount(ref["ids"].reshape(-1), minlength=layer.E)
+    for e in np.nonzero(counts == 0)[0]:
+        assert not dw1[e].any() and not dw2[e].any()
+    return ref
+
+
+@pytest.mark.parametrize("T,H,E,k,I,score", [
+    (200, 256, 6, 2, 192, O.SCORE_SOFTMAX),     # I below one 256-wide tile
+    (333, 320, 8, 3, 200, O.SCORE_SIGMOID),     # ragged H and I tails, two m tiles of H
+    (700, 256, 4, 2, 320, O.SCORE_SOFTMAX),     # several 256-row tiles per expert, two m tiles of I
+    (100, 512, 4, 1, 256, O.SCORE_SOFTMAX),     # k = 1
+    (1, 256, 8, 2, 128, O.SCORE_SOFTMAX),       # one token
+])
+def test_backward_small(T, H, E, k, I, score):
+    cfg = get_config("tiny_bf16").with_(T=T, H=H, E=E, k=k, I=I, score=score, w_std=0.05)
+    _check(cfg, seed=T)
+
+
+def test_backward_shared_expert():
+    cfg = get_config("tiny_bf16").with_(T=150, H=256, E=6, k=2, I=128, n_shared=1, w_std=0.05)
+    ref = _check(cfg, seed=5)
+    assert ref["ids"].shape[1] == 3
+
+
+def test_backward_one_expert_takes_all():
+    cfg = get_config("tiny_bf16").with_(T=300, H=256, E=8, k=1, I=128, w_std=0.05)
+    inp = make_inputs(cfg, seed=3)
+    inp.logits[:] = -1.0
+    inp.logits[:, 5] = 2.0         # every token -> expert 5; the other experts stay empty
+    _check(cfg, seed=3, inp=inp)
+
+
+def test_backward_deterministic():
+    cfg = get_config("tiny_bf16").with_(T=513, H=256, E=16, k=4, I=128, w_std=0.05)
+    inp, dout = make_inputs(cfg, seed=9), make_dout(cfg, 9)
+    say("backward determinism")
+    a = _train_step(cfg, inp, dout)[3]
+    b = _train_step(cfg, inp, dout)[3]
+    for name in ("dx", "dlogits", "dw1", "dw2"):
+        assert torch.equal(getattr(a, name), getattr(b, name)), name

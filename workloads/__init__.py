@@ -11,4 +11,4 @@ rounded RN to bf16; router logits are the fp32 rounding of x . Wr computed in
 float64 on the host (the router projection is not part of the routed path).
 """
 from .configs import CONFIGS, P5_GRID, Config, get_config  # noqa: F401
-from .generate import Inputs, make_inputs, make_inputs_device, make_expert_weights, to_f64  # noqa: F401
+from .generate import Inputs, make_dout, make_inputs, make_inputs_device, make_expert_weights, to_f64  # noqa: F401

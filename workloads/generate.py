@@ -10,6 +10,8 @@ index, seed]))):
   (W1 and W2 carry E + n_shared experts: the shared ones last)
   tensor 4  Gumbel noise [T, E] (Zipf routing only)   index = T
   tensor 5  permutation of expert popularity ranks (Zipf routing only)
+  tensor 6  dout [T, H] ~ N(0, 1)            index = T (the output gradient of
+                                              a training step)
 Draws are fp32 and rounded RN to bf16 with torch. Router logits:
   uniform: fp32( x . Wr ) evaluated in float64 from the bf16 values;
   zipf:    fp32( log p_e + G[t, e] ), p_e proportional to (rank_e + 1)^-1.2,
@@ -84,6 +86,17 @@ class Inputs:
 
     def expert_w2(self, e: int) -> torch.Tensor:
         return self.w2[e] if self.w2 is not None else make_expert_weights(self.cfg, 3, e, self.seed)
+
+
+def make_dout(cfg: Config, seed: int = 0, device=None) -> torch.Tensor:
+    """Output gradient dout [T, H] bf16 ~ N(0, 1) (tensor 6). device: draw it
+    there with torch's generator (seeded from the same SeedSequence)."""
+    if device is None:
+        return _bf16(_rng(cfg, 6, cfg.T, seed).standard_normal((cfg.T, cfg.H), dtype=np.float32))
+    s = np.random.SeedSequence([cfg.cfg_id, 6, cfg.T, seed]).generate_state(1, np.uint64)[0]
+    g = torch.Generator(device=device)
+    g.manual_seed(int(s) & ((1 << 63) - 1))
+    return torch.randn((cfg.T, cfg.H), generator=g, device=device).to(torch.bfloat16)
 
 
 def make_logits(cfg: Config, x: torch.Tensor, seed: int = 0) -> torch.Tensor:
