@@ -29,6 +29,9 @@ DTYPE_NAME = {0: "bf16", 1: "fp8_e4m3 (128-block scales)", 2: "mxfp4 weights x m
 # Liger-Kernel PR #1463, MoEBenchmark results, H200, Qwen3-30B-A3B, T=8192, BF16 forward.
 PAGE_BASELINE = {"qwen3_30b_a3b_bf16": (354.38, "H200 1-GPU BF16 forward, Liger-Kernel PR #1463 MoEBenchmark"),
                  "llama4_scout_bf16": (511.36, "H200 1-GPU BF16 forward, Liger-Kernel PR #1463 MoEBenchmark")}
+PAGE_BASELINE_BWD = {
+    "qwen3_30b_a3b_bf16": (199.28, "H200 1-GPU BF16 backward, Liger-Kernel PR #1463 MoEBenchmark"),
+    "llama4_scout_bf16": (299.54, "H200 1-GPU BF16 backward, Liger-Kernel PR #1463 MoEBenchmark")}
 KERNEL_SRC = {"gemm1_swiglu": {0: "gemm_bf16.hip", 1: "gemm_scaled.hip", 2: "gemm_scaled.hip"},
               "gemm1_relu2": {0: "gemm_bf16.hip"},
               "gemm2_down": {0: "gemm_bf16.hip", 1: "gemm_scaled.hip", 2: "gemm_scaled.hip"}}
@@ -148,9 +151,11 @@ def copy_probe(mib: int):
     del src, dst
 
 
-def cpu_baseline(cfg, inp, budget_s: float = 15.0):
+def cpu_baseline(cfg, inp, budget_s: float = 15.0, backward: bool = False):
     """The oracle as it stands, timed on this host on a bounded prefix of the
-    same batch (same weights, the first T' tokens), scaled to TFLOP/s."""
+    same batch (same weights, the first T' tokens), scaled to TFLOP/s
+    (backward=True: the oracle's backward, which also recomputes the forward
+    it needs, counted at the backward's FLOPs only)."""
     import numpy as np
     from oracle import moe as O
     from workloads import to_f64
@@ -162,12 +167,20 @@ def cpu_baseline(cfg, inp, budget_s: float = 15.0):
         threads = os.cpu_count() or 1
     w1 = to_f64(inp.w1)
     w2 = to_f64(inp.w2)
+    dout = None
+    if backward:
+        from workloads import make_dout
+        dout = to_f64(make_dout(cfg, 0))
 
     def run(t):
         logits = inp.logits[:t].numpy()
         x = to_f64(inp.x[:t])
         t0 = time.perf_counter()
-        O.moe_forward(logits, x, w1, w2, cfg.k, cfg.score, cfg.dtype, block_m=16, act=cfg.act, n_shared=cfg.n_shared)
+        if backward:
+            O.moe_backward(logits, x, w1, w2, dout[:t], cfg.k, cfg.score, block_m=16, n_shared=cfg.n_shared)
+        else:
+            O.moe_forward(logits, x, w1, w2, cfg.k, cfg.score, cfg.dtype, block_m=16, act=cfg.act,
+                          n_shared=cfg.n_shared)
         return time.perf_counter() - t0
 
     # grow the token prefix until one oracle run takes about budget_s
@@ -176,9 +189,10 @@ def cpu_baseline(cfg, inp, budget_s: float = 15.0):
     while dt < 0.5 * budget_s and t_sample < cfg.T:
         t_sample = int(min(cfg.T, max(t_sample + 1, t_sample * budget_s / max(dt, 1e-3))))
         dt = run(t_sample)
-    flops = cfg.flops // cfg.T * t_sample
+    flops = (2 if backward else 1) * cfg.flops // cfg.T * t_sample
+    what = "backward" if backward else "forward"
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"float64 numpy oracle on the first {t_sample} of {cfg.T} tokens of the same batch "
+            "sample": f"float64 numpy oracle {what} on the first {t_sample} of {cfg.T} tokens of the same batch "
                       f"(same weights), {dt:.2f} s"}
 
 
@@ -198,6 +212,8 @@ def main(argv=None):
     ap.add_argument("--traffic-command", default="", help="the command that made the profile")
     ap.add_argument("--sweep", choices=("grid", "tokens"), default=None,
                     help="throughput sweep, one JSON line per shape: the BF16 parameter grid or the token sweep")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward of the BF16 SwiGLU layer instead of the forward")
     ap.add_argument("--stats-md", nargs=3, metavar=("STATS_CSV", "TITLE", "OUT_MD"),
                     help="write a markdown summary of a rocprofv3 --stats kernel table and exit")
     a = ap.parse_args(argv)
@@ -228,36 +244,29 @@ def main(argv=None):
     if a.tokens:
         cfg = cfg.with_(T=a.tokens)
     inp = make_inputs(cfg)
-    rec = measure(cfg, inp, a.steps, a.warmup, a.block_m)
-    base = PAGE_BASELINE.get(cfg.name) if not a.tokens else None
+    if a.backward:
+        rec = measure_backward(cfg, inp, a.steps, a.warmup)
+        base = PAGE_BASELINE_BWD.get(cfg.name) if not a.tokens else None
+    else:
+        rec = measure(cfg, inp, a.steps, a.warmup, a.block_m)
+        base = PAGE_BASELINE.get(cfg.name) if not a.tokens else None
     rec["vs_baseline"] = round(rec["value"] / base[0], 4) if base else None
     rec["baseline_ref"] = f"{base[0]} TFLOP/s, {base[1]} (other hardware, context only)" if base else None
     if not a.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(cfg, inp)
+        rec["cpu_baseline"] = cpu_baseline(cfg, inp, backward=a.backward)
     print(json.dumps(rec), flush=True)
     return 0
 
 
-def measure(cfg, inp, steps: int, warmup: int, block_m=None, data=None) -> dict:
-    """Time `steps` whole forwards of workload cfg on inputs inp (after
-    `warmup` untimed ones) and build the result record."""
+def _time_stages(stage_fns, steps: int, warmup: int):
+    """Run `warmup` untimed passes, then time `steps` passes of the stage
+    functions, with events on the launch stream around every stage."""
     import torch
-    import mixture_experts_routed_top_amd as M
-
-    dev = "cuda:0"
-    layer = M.MoeLayer(cfg.dtype, inp.w1.to(dev), inp.w2.to(dev), cfg.k, cfg.score, cfg.act, cfg.n_shared)
-    x, logits = inp.x.to(dev), inp.logits.to(dev)
-    plan = layer.plan(cfg.T, block_m=block_m)
-    torch.cuda.synchronize()
-
     stream = torch.cuda.current_stream()
-    stage_fns = _stage_fns(layer, plan, x, logits)
     for _ in range(warmup):
         for _, f in stage_fns:
             f()
     torch.cuda.synchronize()
-
-    # timed region: K whole forwards; events on the launch stream bracket each stage
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stage_fns) + 1)] for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -272,17 +281,40 @@ def measure(cfg, inp, steps: int, warmup: int, block_m=None, data=None) -> dict:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = start.elapsed_time(end) / steps
-
     stage_us = {}
     for i, (name, _) in enumerate(stage_fns):
         stage_us[name] = round(1000.0 * sum(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) / steps, 2)
-    flops = cfg.flops
-    value = flops / (ms / 1e3) / 1e12
-    # per-step distribution, and the compute-only rate (x already quantised:
-    # every stage but quantize_x) next to the end-to-end one
     steps_ms = sorted(ev[s][0].elapsed_time(ev[s][-1]) for s in range(steps))
     step_stats = {"median": round(steps_ms[len(steps_ms) // 2], 4), "min": round(steps_ms[0], 4),
                   "p90": round(steps_ms[min(len(steps_ms) - 1, int(0.9 * len(steps_ms)))], 4)}
+    return ms, stage_us, step_stats, wall
+
+
+def _config(cfg, plan):
+    return {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k, "I": cfg.I,
+            "n_shared": cfg.n_shared, "activation": "swiglu" if cfg.act == 0 else "relu2",
+            "routing": cfg.routing, "score": "softmax" if cfg.score == 0 else "sigmoid",
+            "numeric_path": DTYPE_NAME[cfg.dtype], "block_m": plan.block_m, "parallelism": "none (1 GPU)"}
+
+
+def measure(cfg, inp, steps: int, warmup: int, block_m=None, data=None) -> dict:
+    """Time `steps` whole forwards of workload cfg on inputs inp (after
+    `warmup` untimed ones) and build the result record."""
+    import torch
+    import mixture_experts_routed_top_amd as M
+
+    dev = "cuda:0"
+    layer = M.MoeLayer(cfg.dtype, inp.w1.to(dev), inp.w2.to(dev), cfg.k, cfg.score, cfg.act, cfg.n_shared)
+    x, logits = inp.x.to(dev), inp.logits.to(dev)
+    plan = layer.plan(cfg.T, block_m=block_m)
+    torch.cuda.synchronize()
+
+    # timed region: K whole forwards
+    ms, stage_us, step_stats, wall = _time_stages(_stage_fns(layer, plan, x, logits), steps, warmup)
+    flops = cfg.flops
+    value = flops / (ms / 1e3) / 1e12
+    # the compute-only rate (x already quantised: every stage but quantize_x)
+    # next to the end-to-end one
     compute_us = sum(v for n, v in stage_us.items() if n != "quantize_x")
 
     # roofline of the dominant kernel (largest average duration)
@@ -304,10 +336,7 @@ def measure(cfg, inp, steps: int, warmup: int, block_m=None, data=None) -> dict:
         "vs_baseline": None,
         "dtype": "bf16" if cfg.dtype == 0 else ("fp8" if cfg.dtype == 1 else "mxfp4xmxfp8"),
         "data": data or "synthetic (seeded N(0,1) tokens, N(0,sigma) bf16 weights, router logits x.Wr)",
-        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k, "I": cfg.I,
-                   "n_shared": cfg.n_shared, "activation": "swiglu" if cfg.act == 0 else "relu2",
-                   "routing": cfg.routing, "score": "softmax" if cfg.score == 0 else "sigmoid",
-                   "numeric_path": DTYPE_NAME[cfg.dtype], "block_m": plan.block_m, "parallelism": "none (1 GPU)"},
+        "config": _config(cfg, plan),
         "pct_of_dtype_peak": round(100 * value / peak, 2),
         "step_ms": step_stats,
         "compute_tflops": round(flops / (compute_us * 1e-6) / 1e12, 2),
@@ -318,6 +347,66 @@ def measure(cfg, inp, steps: int, warmup: int, block_m=None, data=None) -> dict:
     if cfg.dtype == 2:
         rec["pct_of_fp4_peak"] = round(100 * value / PEAK_FP4_TFLOPS, 2)
     return rec
+
+
+# FLOPs per launch of each backward GEMM, in units of T*(k+shared)*H*I
+BWD_GEMM_FLOPS = {"gemm_dh": 2, "gemm_dx": 4, "wgrad_w2": 2, "wgrad_w1": 4}
+
+
+def measure_backward(cfg, inp, steps: int, warmup: int, data=None) -> dict:
+    """Time `steps` backward passes of the BF16 SwiGLU layer (after one
+    training forward that saves what they read): combine backward, router
+    backward, dGU, dx rows, dx, row gather, dW2, dW1. Throughput counts the
+    routed backward GEMM FLOPs, 12 * T * k * H * I per step (twice the
+    forward's)."""
+    import torch
+    import mixture_experts_routed_top_amd as M
+    from workloads import make_dout
+
+    if cfg.dtype != 0 or cfg.act != 0:
+        raise SystemExit("the backward is implemented for the BF16 SwiGLU layer")
+    dev = "cuda:0"
+    layer = M.MoeLayer(cfg.dtype, inp.w1.to(dev), inp.w2.to(dev), cfg.k, cfg.score, cfg.act, cfg.n_shared)
+    x, logits = inp.x.to(dev), inp.logits.to(dev)
+    dout = make_dout(cfg, 0).to(dev)
+    p = layer.plan(cfg.T, train=True)
+    layer.forward_train(x, logits, p)
+    torch.cuda.synchronize()
+    tb, H, I = p.train, layer.H, layer.I
+    fns = [("backward_combine", lambda: M.moe_backward_combine(dout, p.w, p.y, p.sort, tb.dy, tb.dw)),
+           ("route_backward", lambda: M.moe_route_backward(p.w, p.ids, tb.dw, layer.E - layer.n_shared,
+                                                           layer.k_routed, layer.score, layer.n_shared,
+                                                           tb.dlogits)),
+           ("gemm_dh", lambda: M.moe_grouped_gemm_dh(tb.dy, layer.w2, tb.gu, p.sort, H, I, tb.dgu)),
+           ("gemm_dx", lambda: M.moe_grouped_gemm_dx(tb.dgu, layer.w1, p.sort, H, I, tb.dx_rows)),
+           ("dx_reduce", lambda: M.moe_combine(tb.dx_rows, tb.ones, tb.dx)),
+           ("gather_rows", lambda: M.moe_gather_rows(x, p.sort, tb.x_sorted)),
+           ("wgrad_w2", lambda: M.moe_grouped_gemm_wgrad(p.h, tb.dy, p.sort, tb.dw2)),
+           ("wgrad_w1", lambda: M.moe_grouped_gemm_wgrad(tb.x_sorted, tb.dgu, p.sort, tb.dw1))]
+    ms, stage_us, step_stats, wall = _time_stages(fns, steps, warmup)
+    unit = cfg.T * (cfg.k + cfg.n_shared) * cfg.H * cfg.I
+    flops = 2 * cfg.flops
+    value = flops / (ms / 1e3) / 1e12
+    dom = max(BWD_GEMM_FLOPS, key=lambda n: stage_us[n])
+    dom_flops = BWD_GEMM_FLOPS[dom] * unit
+    achieved = dom_flops / (stage_us[dom] * 1e-6) / 1e12
+    peak = PEAK_TFLOPS[0]
+    gemm_tflops = {n: round(BWD_GEMM_FLOPS[n] * unit / (stage_us[n] * 1e-6) / 1e12, 2) for n in BWD_GEMM_FLOPS}
+    return {
+        "metric": "routed MoE-MLP backward TFLOP/s on 1 MI355X (+% of dtype MFMA peak)",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16",
+        "data": data or "synthetic (seeded N(0,1) tokens and output gradient, N(0,sigma) bf16 weights, "
+                        "router logits x.Wr)",
+        "config": _config(cfg, p),
+        "pct_of_dtype_peak": round(100 * value / peak, 2),
+        "step_ms": step_stats, "stages_us": stage_us, "gemm_tflops": gemm_tflops, "wall_s_timed": round(wall, 4),
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "avg_launch_us": stage_us[dom],
+                     "algorithmic": f"{BWD_GEMM_FLOPS[dom]}*T*(k+shared)*H*I = {dom_flops} FLOP per launch"},
+    }
 
 
 def sweep(a) -> int:

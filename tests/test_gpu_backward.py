@@ -112,3 +112,46 @@ def test_backward_deterministic():
     b = _train_step(cfg, inp, dout)[3]
     for name in ("dx", "dlogits", "dw1", "dw2"):
         assert torch.equal(getattr(a, name), getattr(b, name)), name
+
+
+def test_backward_full_size_sampled():
+    """The Qwen3-30B-A3B-shaped layer at T = 8192, in the launch configuration
+    the backward benchmark times: routing and layout compared in full; dx,
+    dw and dlogits on sampled tokens, and dW1 / dW2 of the most and the least
+    loaded expert, each from the oracle run on just the tokens that
+    determine them (a token's gradients depend on that token alone; an
+    expert's weight gradients on the tokens routed to it)."""
+    cfg = get_config("qwen3_30b_a3b_bf16")
+    inp = make_inputs(cfg)
+    dout = make_dout(cfg, 0)
+    say("backward full-size sampled", cfg.name)
+    layer, plan, out, tb = _train_step(cfg, inp, dout)
+    logits = inp.logits.numpy()
+    rid, _ = O.route(logits, cfg.k, cfg.score)
+    np.testing.assert_array_equal(plan.ids.cpu().numpy(), rid)
+    counts, offsets, sorted_ids, tile_expert, num_tiles = O.align_sort(rid, cfg.E, 256)
+    np.testing.assert_array_equal(plan.sort.sorted_ids.cpu().numpy()[:len(sorted_ids)], sorted_ids)
+    np.testing.assert_array_equal(plan.sort.offsets.cpu().numpy(), offsets)
+    x64, w1, w2, d64 = to_f64(inp.x), to_f64(inp.w1), to_f64(inp.w2), to_f64(dout)
+
+    def oracle_on(tokens):
+        return O.moe_backward(logits[tokens], x64[tokens], w1, w2, d64[tokens], cfg.k, cfg.score)
+
+    rng = np.random.default_rng(1)
+    toks = np.unique(np.concatenate([[0, cfg.T - 1], rng.choice(cfg.T, 30, replace=False)]))
+    ref = oracle_on(toks)
+    assert rel_fro(f64(tb.dx)[toks], ref["dx"]) <= TOL
+    assert rel_fro(tb.dw.cpu().numpy()[toks], ref["dw"]) <= TOL
+    dl = tb.dlogits.cpu().numpy().astype(np.float64)[toks]
+    assert rel_fro(dl, ref["dlogits"]) <= TOL_DLOGITS
+    np.testing.assert_allclose(dl, ref["dlogits"], rtol=0, atol=TOL_DLOGITS * np.abs(ref["dlogits"]).max())
+    del ref
+
+    nonempty = np.flatnonzero(counts)
+    for e in (int(nonempty[np.argmax(counts[nonempty])]), int(nonempty[np.argmin(counts[nonempty])])):
+        sub = np.flatnonzero((rid == e).any(axis=1))
+        say("backward full-size expert", e, len(sub))
+        ref = oracle_on(sub)
+        assert rel_fro(tb.dw1[e].cpu().numpy(), ref["dw1"][e]) <= TOL
+        assert rel_fro(tb.dw2[e].cpu().numpy(), ref["dw2"][e]) <= TOL
+        del ref
