@@ -212,6 +212,8 @@ def main(argv=None):
     ap.add_argument("--traffic-command", default="", help="the command that made the profile")
     ap.add_argument("--sweep", choices=("grid", "tokens"), default=None,
                     help="throughput sweep, one JSON line per shape: the BF16 parameter grid or the token sweep")
+    ap.add_argument("--fused-combine", action="store_true",
+                    help="BF16: run GEMM2 with the weighted combine fused into its epilogue")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward of the BF16 SwiGLU layer instead of the forward")
     ap.add_argument("--stats-md", nargs=3, metavar=("STATS_CSV", "TITLE", "OUT_MD"),
@@ -248,7 +250,7 @@ def main(argv=None):
         rec = measure_backward(cfg, inp, a.steps, a.warmup)
         base = PAGE_BASELINE_BWD.get(cfg.name) if not a.tokens else None
     else:
-        rec = measure(cfg, inp, a.steps, a.warmup, a.block_m)
+        rec = measure(cfg, inp, a.steps, a.warmup, a.block_m, fused_combine=a.fused_combine)
         base = PAGE_BASELINE.get(cfg.name) if not a.tokens else None
     rec["vs_baseline"] = round(rec["value"] / base[0], 4) if base else None
     rec["baseline_ref"] = f"{base[0]} TFLOP/s, {base[1]} (other hardware, context only)" if base else None
@@ -294,17 +296,19 @@ def _config(cfg, plan):
     return {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "E": cfg.E, "k": cfg.k, "I": cfg.I,
             "n_shared": cfg.n_shared, "activation": "swiglu" if cfg.act == 0 else "relu2",
             "routing": cfg.routing, "score": "softmax" if cfg.score == 0 else "sigmoid",
-            "numeric_path": DTYPE_NAME[cfg.dtype], "block_m": plan.block_m, "parallelism": "none (1 GPU)"}
+            "numeric_path": DTYPE_NAME[cfg.dtype], "block_m": plan.block_m, "parallelism": "none (1 GPU)",
+            "fused_combine": plan.counters is not None}
 
 
-def measure(cfg, inp, steps: int, warmup: int, block_m=None, data=None) -> dict:
+def measure(cfg, inp, steps: int, warmup: int, block_m=None, data=None, fused_combine=False) -> dict:
     """Time `steps` whole forwards of workload cfg on inputs inp (after
     `warmup` untimed ones) and build the result record."""
     import torch
     import mixture_experts_routed_top_amd as M
 
     dev = "cuda:0"
-    layer = M.MoeLayer(cfg.dtype, inp.w1.to(dev), inp.w2.to(dev), cfg.k, cfg.score, cfg.act, cfg.n_shared)
+    layer = M.MoeLayer(cfg.dtype, inp.w1.to(dev), inp.w2.to(dev), cfg.k, cfg.score, cfg.act, cfg.n_shared,
+                       fused_combine=fused_combine)
     x, logits = inp.x.to(dev), inp.logits.to(dev)
     plan = layer.plan(cfg.T, block_m=block_m)
     torch.cuda.synchronize()
@@ -319,8 +323,9 @@ def measure(cfg, inp, steps: int, warmup: int, block_m=None, data=None) -> dict:
 
     # roofline of the dominant kernel (largest average duration)
     g1 = GEMM1_STAGE[cfg.act]
-    dom = max((g1, "gemm2_down"), key=lambda n: stage_us[n])
-    fl_mult = {"gemm1_swiglu": 4, "gemm1_relu2": 2, "gemm2_down": 2}[dom]
+    g2 = "gemm2_down_combine" if "gemm2_down_combine" in stage_us else "gemm2_down"
+    dom = max((g1, g2), key=lambda n: stage_us[n])
+    fl_mult = {"gemm1_swiglu": 4, "gemm1_relu2": 2, "gemm2_down": 2, "gemm2_down_combine": 2}[dom]
     dom_flops = fl_mult * cfg.T * (cfg.k + cfg.n_shared) * cfg.H * cfg.I   # rows the kernel computes
     achieved = dom_flops / (stage_us[dom] * 1e-6) / 1e12
     peak = PEAK_TFLOPS[cfg.dtype]
@@ -454,6 +459,11 @@ def _stage_fns(layer, plan, x, logits):
     gemm1 = M.moe_grouped_gemm_swiglu if layer.act == M.ACT_SWIGLU else M.moe_grouped_gemm_relu2
     fns.append((GEMM1_STAGE[layer.act], lambda: gemm1(d, a, a_s, layer.w1, layer.w1_scale, plan.sort,
                                                       layer.H, layer.I, plan.h, plan.h_scale)))
+    if layer.fused_combine:
+        fns.append(("gemm2_down_combine", lambda: M.moe_grouped_gemm_down_combine(
+            d, plan.h, plan.h_scale, layer.w2, layer.w2_scale, plan.sort, layer.H, layer.I, plan.w, plan.counters,
+            plan.y, plan.out)))
+        return fns
     fns.append(("gemm2_down", lambda: M.moe_grouped_gemm_down(d, plan.h, plan.h_scale, layer.w2, layer.w2_scale,
                                                                 plan.sort, layer.H, layer.I, plan.y)))
     fns.append(("combine", lambda: M.moe_combine(plan.y, plan.w, plan.out)))

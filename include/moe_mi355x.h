@@ -288,6 +288,42 @@ moe_status_t moe_grouped_gemm_down(int32_t dtype, const void* h, const void* h_s
                                    uint16_t* y, void* stream);
 
 /*
+ * moe_down_combine_workspace_bytes -- host only. Bytes of the counter
+ * workspace moe_grouped_gemm_down_combine needs: T * ceil(H / 128) int32.
+ * Returns 0 for invalid arguments.
+ */
+size_t moe_down_combine_workspace_bytes(int64_t T, int32_t H);
+
+/*
+ * moe_grouped_gemm_down_combine -- moe_grouped_gemm_down with the weighted
+ * top-k combine fused into its epilogue (TileScale PR #70, Design: "Kernel
+ * 2" runs the L2 GEMM, the scatter to (token, slot) rows and the reduce).
+ *
+ * Writes y exactly as moe_grouped_gemm_down and, in the same launch,
+ *   out[t, c] = bf16( sum_{j = 0..k-1} topk_w[t, j] * y[t*k + j, c] ),
+ * the result moe_combine gives, bit for bit: the workgroup that stores the
+ * last of a token's k rows for a block of columns sums that block in fp32 in
+ * slot order. The order in which workgroups finish does not change any value.
+ *   topk_w [T, k] fp32; out [T, H] bf16 (16-byte aligned);
+ *   counters: device workspace of at least
+ *     moe_down_combine_workspace_bytes(T, H) bytes, int32-aligned, which
+ *     must hold zeros before the call; every call leaves it zero again, so
+ *     clear it once when it is allocated. Two calls that overlap in time must
+ *     not share a workspace.
+ * BF16 only (other dtypes -> MOE_ERR_UNSUPPORTED_SHAPE); other arguments and
+ * errors as moe_grouped_gemm_down; a workspace below the size ->
+ * MOE_ERR_WORKSPACE.
+ */
+moe_status_t moe_grouped_gemm_down_combine(int32_t dtype, const void* h, const void* h_scale,
+                                           const void* w2, const void* w2_scale,
+                                           const int32_t* sorted_ids, const int32_t* tile_expert,
+                                           const int32_t* num_tiles,
+                                           int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                                           int32_t block_m, int64_t cap,
+                                           uint16_t* y, const float* topk_w, uint16_t* out,
+                                           int32_t* counters, size_t counters_bytes, void* stream);
+
+/*
  * moe_combine -- top-k weighted sum of each token's expert rows.
  * TileScale PR #70, review thread on the reduce tail (sum over the top-k
  * slots into the BF16 output); FlashInfer PR #5129, Description (the combine

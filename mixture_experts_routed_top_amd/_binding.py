@@ -49,6 +49,9 @@ SIGNATURES = {
     "moe_grouped_gemm_down": (_I32, [_I32, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32,
                                      _I32, _I64, _P, _P]),
     "moe_combine": (_I32, [_P, _P, _I64, _I32, _I32, _P, _P]),
+    "moe_down_combine_workspace_bytes": (_SZ, [_I64, _I32]),
+    "moe_grouped_gemm_down_combine": (_I32, [_I32, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32,
+                                             _I32, _I64, _P, _P, _P, _P, _SZ, _P]),
     "moe_grouped_gemm_swiglu_save": (_I32, [_P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I64,
                                             _P, _P, _P]),
     "moe_backward_combine": (_I32, [_P, _P, _P, _P, _I64, _I32, _I32, _I64, _P, _P, _P]),
@@ -249,6 +252,28 @@ def moe_grouped_gemm_down(dtype: int, h, h_scale, w2, w2_scale, sort: SortResult
         dtype, _p(h), _p(h_scale), _p(w2), _p(w2_scale), _p(sort.sorted_ids), _p(sort.tile_expert),
         _p(sort.num_tiles), sort.T, H, I, sort.E, sort.k, sort.block_m, sort.cap, _p(y), _s(stream)))
     return y
+
+
+def moe_down_combine_workspace(T: int, H: int, device) -> torch.Tensor:
+    """Zeroed counter workspace of moe_grouped_gemm_down_combine (calls leave it zero)."""
+    n = lib().moe_down_combine_workspace_bytes(T, H) // 4
+    return torch.zeros(max(n, 1), dtype=torch.int32, device=device)
+
+
+def moe_grouped_gemm_down_combine(dtype: int, h, h_scale, w2, w2_scale, sort: SortResult, H: int, I: int,
+                                  topk_w, counters, y=None, out=None, stream=None):
+    """GEMM2 with the weighted combine fused: returns (y, out)."""
+    _need(topk_w, torch.float32, "topk_w")
+    _need(counters, torch.int32, "counters")
+    if y is None:
+        y = torch.empty((max(sort.T * sort.k, 1), H), dtype=torch.bfloat16, device=h.device)
+    if out is None:
+        out = torch.empty((sort.T, H), dtype=torch.bfloat16, device=h.device)
+    _check("moe_grouped_gemm_down_combine", lib().moe_grouped_gemm_down_combine(
+        dtype, _p(h), _p(h_scale), _p(w2), _p(w2_scale), _p(sort.sorted_ids), _p(sort.tile_expert),
+        _p(sort.num_tiles), sort.T, H, I, sort.E, sort.k, sort.block_m, sort.cap, _p(y), _p(topk_w), _p(out),
+        _p(counters), counters.numel() * 4, _s(stream)))
+    return y, out
 
 
 def moe_combine(y: torch.Tensor, topk_w: torch.Tensor, out=None, stream=None):

@@ -88,14 +88,84 @@ struct Params {
   const int32_t* num_tiles;
   uint16_t* out;           // GEMM1: h [cap, I]; GEMM2: y [A, H]
   uint16_t* gu;            // GEMM1 (SwiGLU), optional: saved pre-activations [cap, 2I] (gate, up)
+  const float* topk_w;     // GEMM2 with the fused combine: gate weights [A]
+  uint16_t* comb;          //   combined output [T, H]
+  int32_t* counters;       //   [T, ceil(H / BN)] finished slots per (token, column tile); zero between calls
   int64_t A;
   uint32_t a_bytes;        // bytes of the token operand (below 2^31)
   int H, I, k;
 };
 
-template <int BM, int BN, int WM, int WN, bool GEMM1, int ACT>
+// The weighted top-k combine fused into GEMM2 (TileScale PR #70, Design:
+// "Kernel 2" runs L2, the scatter to (token, slot) rows and the reduce).
+// Called by the whole workgroup after it has stored the y rows of its tile
+// (sorted rows row0.., output columns [n0, n0 + BN)). Every real row bumps
+// the counter of its (token, column tile); the workgroup that brings a
+// counter to k stored the last of that token's k rows for these columns, so
+// all k rows are complete: it sums them in fp32 in slot order (the same
+// arithmetic as the separate combine, so the result is identical) and resets
+// the counter to zero for the next call. The release fence before the count
+// makes this workgroup's y rows visible to whichever workgroup finishes the
+// token; the acquire fence after it makes the other workgroups' rows visible
+// here. `last_tok` is LDS scratch of BM ints.
+template <int BM, int BN, int THREADS>
+__device__ __forceinline__ void fused_combine(const Params& p, int64_t row0, int nt, int ntn, int N,
+                                              int32_t* last_tok) {
+  constexpr int WAVES = THREADS / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n0 = nt * BN;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  for (int r = tid; r < BM; r += THREADS) {
+    const int sid = p.sorted_ids[row0 + r];
+    int t = -1;
+    if (sid < p.A) {
+      const int tt = sid / p.k;
+      int32_t* c = p.counters + static_cast<int64_t>(tt) * ntn + nt;
+      if (__hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == p.k - 1) {
+        t = tt;
+        __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    last_tok[r] = t;
+  }
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  for (int r = wave; r < BM; r += WAVES) {
+    const int t = last_tok[r];                 // the same for every lane of the wave
+    if (t < 0) continue;
+    const int64_t a0 = static_cast<int64_t>(t) * p.k;
+    for (int c = lane * 8; c < BN; c += 512) {
+      const int n = n0 + c;
+      if (n >= N) break;
+      float acc[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+      for (int j = 0; j < p.k; ++j) {
+        const float wj = p.topk_w[a0 + j];
+        const uint4 q = *reinterpret_cast<const uint4*>(p.out + (a0 + j) * N + n);
+        const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] = __builtin_fmaf(wj, __uint_as_float(w4[i] << 16), acc[2 * i]);
+          acc[2 * i + 1] = __builtin_fmaf(wj, __uint_as_float(w4[i] & 0xFFFF0000u), acc[2 * i + 1]);
+        }
+      }
+      uint4 o;
+      o.x = pack_bf16x2(acc[0], acc[1]);
+      o.y = pack_bf16x2(acc[2], acc[3]);
+      o.z = pack_bf16x2(acc[4], acc[5]);
+      o.w = pack_bf16x2(acc[6], acc[7]);
+      *reinterpret_cast<uint4*>(p.comb + static_cast<int64_t>(t) * N + n) = o;
+    }
+  }
+  __syncthreads();   // last_tok is read before the next task's loads reuse the LDS
+}
+
+template <int BM, int BN, int WM, int WN, bool GEMM1, int ACT, bool FUSE = false>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
   using C = Cfg<BM, BN, WM, WN, GEMM1, ACT>;
+  static_assert(!FUSE || !GEMM1, "the combine fuses into GEMM2");
   constexpr int BK = C::BK;
   // two separate LDS arrays, so the compiler can tell the stage being filled
   // by the direct-to-LDS loads from the stage being read
@@ -278,13 +348,17 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
         }
       }
     }
+    if constexpr (FUSE) fused_combine<BM, BN, C::THREADS>(p, row0, nt, ntn, N, reinterpret_cast<int32_t*>(stage1));
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool GEMM1, int ACT = kActSwiglu>
-hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
+template <int BM, int BN, int WM, int WN, bool GEMM1, int ACT = kActSwiglu, bool FUSE = false>
+hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s, const CombineArgs* cmb = nullptr) {
   using C = Cfg<BM, BN, WM, WN, GEMM1, ACT>;
   Params p;
+  p.topk_w = cmb ? cmb->topk_w : nullptr;
+  p.comb = cmb ? cmb->out : nullptr;
+  p.counters = cmb ? cmb->counters : nullptr;
   p.a = static_cast<const uint16_t*>(g.a);
   p.w = static_cast<const uint16_t*>(g.w);
   p.sorted_ids = g.sorted_ids;
@@ -302,7 +376,7 @@ hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   int64_t grid = dev.num_cus;
   if (grid > max_tasks) grid = max_tasks;
   if (grid < 1) grid = 1;
-  gemm_bf16_kernel<BM, BN, WM, WN, GEMM1, ACT><<<static_cast<unsigned>(grid), C::THREADS, 0, s>>>(p);
+  gemm_bf16_kernel<BM, BN, WM, WN, GEMM1, ACT, FUSE><<<static_cast<unsigned>(grid), C::THREADS, 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -337,6 +411,16 @@ hipError_t launch_gemm2_bf16(const GemmArgs& g, const DeviceInfo& dev, hipStream
     case 128: return launch<128, 512, 2, 4, false>(g, dev, s);
     case 64: return launch<64, 512, 1, 8, false>(g, dev, s);
     case 32: return launch<32, 512, 1, 8, false>(g, dev, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_gemm2_combine_bf16(const GemmArgs& g, const CombineArgs& c, const DeviceInfo& dev, hipStream_t s) {
+  switch (g.block_m) {
+    case 256: return launch<256, 256, 4, 2, false, kActSwiglu, true>(g, dev, s, &c);
+    case 128: return launch<128, 512, 2, 4, false, kActSwiglu, true>(g, dev, s, &c);
+    case 64: return launch<64, 512, 1, 8, false, kActSwiglu, true>(g, dev, s, &c);
+    case 32: return launch<32, 512, 1, 8, false, kActSwiglu, true>(g, dev, s, &c);
     default: return hipErrorInvalidValue;
   }
 }

@@ -293,6 +293,33 @@ moe_status_t moe_grouped_gemm_down(int32_t dtype, const void* h, const void* h_s
   }
 }
 
+size_t moe_down_combine_workspace_bytes(int64_t T, int32_t H) {
+  if (T < 0 || H <= 0) return 0;
+  return static_cast<size_t>(T) * static_cast<size_t>((H + 127) / 128) * sizeof(int32_t);
+}
+
+moe_status_t moe_grouped_gemm_down_combine(int32_t dtype, const void* h, const void* h_scale, const void* w2,
+                                           const void* w2_scale, const int32_t* sorted_ids,
+                                           const int32_t* tile_expert, const int32_t* num_tiles, int64_t T,
+                                           int32_t H, int32_t I, int32_t E, int32_t k, int32_t block_m, int64_t cap,
+                                           uint16_t* y, const float* topk_w, uint16_t* out, int32_t* counters,
+                                           size_t counters_bytes, void* stream) {
+  if (moe_status_t st = check_gemm(dtype, h, h_scale, w2, w2_scale, sorted_ids, tile_expert, num_tiles, T, H, I,
+                                   E, k, block_m, cap, y, nullptr, false))
+    return st;
+  if (dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED_SHAPE;
+  if (T == 0) return MOE_OK;
+  if (!topk_w || !out || !counters || !aligned(out, 16) || !aligned(topk_w, 4) || !aligned(counters, 4))
+    return MOE_ERR_INVALID_ARG;
+  if (counters_bytes < moe_down_combine_workspace_bytes(T, H)) return MOE_ERR_WORKSPACE;
+  moe::DeviceInfo dev;
+  if (moe_status_t st = current_device(&dev)) return st;
+  moe::GemmArgs g{h, h_scale, w2, w2_scale, sorted_ids, tile_expert, num_tiles, y, nullptr,
+                  T, H, I, E, k, block_m, cap};
+  moe::CombineArgs c{topk_w, out, counters};
+  return launched(moe::launch_gemm2_combine_bf16(g, c, dev, static_cast<hipStream_t>(stream)));
+}
+
 // ------------------------------------------------------------------ backward (BF16)
 namespace {
 

@@ -49,7 +49,17 @@ struct GemmArgs {
   int64_t cap;
 };
 
+// GEMM2 with the weighted combine fused: gate weights [T*k] fp32, the
+// combined output [T, H] bf16, and the per-(token, column tile) counters
+// (T * ceil(H / 128) int32 at most; zero before the call, zero after it).
+struct CombineArgs {
+  const float* topk_w;
+  uint16_t* out;
+  int32_t* counters;
+};
+
 bool gemm_bf16_supports(int block_m);
+hipError_t launch_gemm2_combine_bf16(const GemmArgs& g, const CombineArgs& c, const DeviceInfo& dev, hipStream_t s);
 hipError_t launch_gemm1_bf16(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s);
 hipError_t launch_gemm2_bf16(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s);
 hipError_t launch_gemm1_relu2_bf16(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s);

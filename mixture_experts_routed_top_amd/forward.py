@@ -31,6 +31,7 @@ class Plan:
     y: torch.Tensor
     out: torch.Tensor
     train: Optional["TrainBuffers"] = None
+    counters: Optional[torch.Tensor] = None      # fused combine: zeroed counter workspace
 
 
 @dataclass
@@ -63,13 +64,16 @@ class MoeLayer:
     """
 
     def __init__(self, dtype: int, w1: torch.Tensor, w2: torch.Tensor, k: int, score: int = B.SCORE_SOFTMAX,
-                 act: int = B.ACT_SWIGLU, n_shared: int = 0):
+                 act: int = B.ACT_SWIGLU, n_shared: int = 0, fused_combine: bool = False):
         E, twoI, H = w1.shape
         if act not in (B.ACT_SWIGLU, B.ACT_RELU2):
             raise ValueError("unknown activation")
         if act == B.ACT_RELU2 and dtype != B.DTYPE_BF16:
             raise ValueError("the squared-ReLU expert is BF16 only")
+        if fused_combine and dtype != B.DTYPE_BF16:
+            raise ValueError("the fused combine is implemented for the BF16 path")
         self.dtype, self.score, self.act, self.n_shared = dtype, score, act, n_shared
+        self.fused_combine = fused_combine
         self.k_routed, self.k = k, k + n_shared          # slots per token: routed, then shared
         self.E, self.H, self.I = E, H, (twoI // 2 if act == B.ACT_SWIGLU else twoI)
         if w2.shape != (E, H, self.I):
@@ -123,7 +127,8 @@ class MoeLayer:
                     torch.empty((T, self.k), dtype=torch.float32, device=device),
                     sort, xq, xs, h, h_scale,
                     torch.empty((max(T * self.k, 1), self.H), dtype=torch.bfloat16, device=device),
-                    torch.empty((T, self.H), dtype=torch.bfloat16, device=device), tb)
+                    torch.empty((T, self.H), dtype=torch.bfloat16, device=device), tb,
+                    B.moe_down_combine_workspace(T, self.H, device) if self.fused_combine else None)
 
     def forward(self, x: torch.Tensor, logits: torch.Tensor, plan: Optional[Plan] = None,
                 stream=None) -> torch.Tensor:
@@ -142,6 +147,10 @@ class MoeLayer:
         gemm1 = B.moe_grouped_gemm_swiglu if self.act == B.ACT_SWIGLU else B.moe_grouped_gemm_relu2
         gemm1(self.dtype, a, a_scale, self.w1, self.w1_scale, p.sort, self.H, self.I, p.h, p.h_scale,
               stream=stream)
+        if self.fused_combine:
+            B.moe_grouped_gemm_down_combine(self.dtype, p.h, p.h_scale, self.w2, self.w2_scale, p.sort, self.H,
+                                            self.I, p.w, p.counters, p.y, p.out, stream=stream)
+            return p.out
         B.moe_grouped_gemm_down(self.dtype, p.h, p.h_scale, self.w2, self.w2_scale, p.sort, self.H, self.I,
                                 p.y, stream=stream)
         return B.moe_combine(p.y, p.w, p.out, stream=stream)

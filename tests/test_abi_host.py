@@ -183,6 +183,20 @@ def test_backward_host_validation():
     assert L.moe_gather_rows(FAKE, FAKE, T, k, H, cap, MIS, NULL) == 1
 
 
+def test_down_combine_host_validation():
+    L = _lib()
+    T, k, E, H, I, bm = 64, 2, 4, 256, 128, 32
+    cap = O.sorted_capacity(T, k, E, bm)
+    need = L.moe_down_combine_workspace_bytes(T, H)
+    assert need == T * 2 * 4 and L.moe_down_combine_workspace_bytes(-1, H) == 0
+    f = lambda dtype=0, ws=FAKE, nbytes=need, out=FAKE, T=T, cap=cap: L.moe_grouped_gemm_down_combine(
+        dtype, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, T, H, I, E, k, bm, cap, FAKE, FAKE, out, ws, nbytes, NULL)
+    assert f(dtype=1) == 2 and f(dtype=2) == 2          # BF16 only
+    assert f(nbytes=need - 4) == 3                      # workspace below the size
+    assert f(ws=NULL) == 1 and f(out=MIS) == 1
+    assert f(T=0, cap=0) == 0
+
+
 def test_device_check_without_gpu():
     # valid arguments reach the device check; without a gfx950 device current
     # the call must fail with MOE_ERR_DEVICE and launch nothing
