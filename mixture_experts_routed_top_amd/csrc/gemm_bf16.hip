@@ -206,16 +206,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
     const int wrows = GEMM1 ? C::HALVES * p.I : p.H;   // weight rows of one expert
     const __amdgpu_buffer_rsrc_t b_rsrc =
         make_rsrc(p.w + static_cast<int64_t>(e) * wrows * K, static_cast<uint32_t>(wrows) * K * 2);
-    uint32_t off[C::GPW];
-    int kcol[C::GPW];                                   // first K column of this lane's chunk
-#pragma unroll
-    for (int q = 0; q < C::GPW; ++q) {
-      const int row = (wave * C::GPW + q) * 8 + g_row;
-      const int lc = g_pc ^ (row & 7);                  // logical chunk stored at this place
-      kcol[q] = lc * 8;
-      if (row >= C::ROWS) {
-        off[q] = kOob;
-      } else if (row < BM) {
+    // byte offset of the start of LDS row `row`'s source row: a token row
+    // (gathered by sorted id in GEMM1) or a weight row of expert e; kOob for
+    // pad rows, rows past N and rows past the tile
+    auto row_src = [&](int row) -> uint32_t {
+      if (row >= C::ROWS) return kOob;
+      if (row < BM) {
         int64_t src_row = -1;
         if (GEMM1) {
           const int sid = p.sorted_ids[row0 + row];
@@ -223,20 +219,29 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
         } else {
           src_row = row0 + row;
         }
-        off[q] = src_row < 0 ? kOob : static_cast<uint32_t>(src_row * K * 2 + lc * 16);
-      } else {
-        const int br = row - BM;
-        int n, wrow;
-        if (GEMM1) {
-          const int half = br >= BN ? 1 : 0;
-          n = n0 + br - half * BN;
-          wrow = half * p.I + n;
-        } else {
-          n = n0 + br;
-          wrow = n;
-        }
-        off[q] = n < N ? static_cast<uint32_t>(wrow) * K * 2 + lc * 16 : kOob;
+        return src_row < 0 ? kOob : static_cast<uint32_t>(src_row * K * 2);
       }
+      const int br = row - BM;
+      int n, wrow;
+      if (GEMM1) {
+        const int half = br >= BN ? 1 : 0;
+        n = n0 + br - half * BN;
+        wrow = half * p.I + n;
+      } else {
+        n = n0 + br;
+        wrow = n;
+      }
+      return n < N ? static_cast<uint32_t>(wrow) * K * 2 : kOob;
+    };
+    uint32_t off[C::GPW];
+    int kcol[C::GPW];                                   // first K column of this lane's chunk
+#pragma unroll
+    for (int q = 0; q < C::GPW; ++q) {
+      const int row = (wave * C::GPW + q) * 8 + g_row;
+      const int lc = g_pc ^ (row & 7);                  // logical chunk stored at this place
+      kcol[q] = lc * 8;
+      const uint32_t base = row_src(row);
+      off[q] = base == kOob ? kOob : base + lc * 16;
     }
     // issue the direct-to-LDS loads of k-step kt into `stage`
     auto load = [&](char* stage, int kt) {
@@ -261,22 +266,51 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
 #pragma unroll
         for (int j = 0; j < C::FN; ++j) acc[h][i][j] = f32x16{};
 
+    // the fragments of 16-K substep kk + 1 are read from LDS into the other
+    // register set while the MFMAs of substep kk run, so the LDS latency
+    // hides behind MFMA work instead of stalling the matrix pipe
     auto compute = [&](const char* base) {
+      bf16x8 xf[2][C::FM], wf[2][C::HALVES][C::FN];
+      auto read_frags = [&](int kk, int buf) {
+        const int ch = kk * 2 + (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) xf[buf][i] = lds_frag(base, wm * C::TM + i * 32 + (lane & 31), ch);
+#pragma unroll
+        for (int h = 0; h < C::HALVES; ++h)
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j)
+            wf[buf][h][j] = lds_frag(base, BM + h * BN + wn * C::TN + j * 32 + (lane & 31), ch);
+      };
+      read_frags(0, 0);
 #pragma unroll
       for (int kk = 0; kk < BK / 16; ++kk) {
-        const int ch = kk * 2 + (lane >> 5);
-        bf16x8 xf[C::FM];
+        const int cur = kk & 1;
+        if (kk + 1 < BK / 16) read_frags(kk + 1, cur ^ 1);
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i) xf[i] = lds_frag(base, wm * C::TM + i * 32 + (lane & 31), ch);
+        for (int h = 0; h < C::HALVES; ++h)
 #pragma unroll
-        for (int h = 0; h < C::HALVES; ++h) {
-#pragma unroll
-          for (int j = 0; j < C::FN; ++j) {
-            const bf16x8 wf = lds_frag(base, BM + h * BN + wn * C::TN + j * 32 + (lane & 31), ch);
+          for (int j = 0; j < C::FN; ++j)
 #pragma unroll
             for (int i = 0; i < C::FM; ++i)
-              acc[h][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, xf[i], acc[h][i][j], 0, 0, 0);
+              acc[h][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][h][j], xf[cur][i], acc[h][i][j], 0, 0, 0);
+      }
+      // pin the interleave: the reads of substep 0, then per substep one
+      // fragment read of the next substep after each MFMA
+      constexpr int READS = C::FM + C::HALVES * C::FN, MFMAS = C::HALVES * C::FN * C::FM;
+      constexpr int PAIRS = READS < MFMAS ? READS : MFMAS;
+      __builtin_amdgcn_sched_group_barrier(0x100, READS, 0);
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        if (kk + 1 < BK / 16) {
+#pragma unroll
+          for (int q = 0; q < PAIRS; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           }
+          if (MFMAS > PAIRS) __builtin_amdgcn_sched_group_barrier(0x008, MFMAS - PAIRS, 0);
+          if (READS > PAIRS) __builtin_amdgcn_sched_group_barrier(0x100, READS - PAIRS, 0);
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x008, MFMAS, 0);
         }
       }
     };
