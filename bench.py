@@ -117,8 +117,9 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str, copy_mib: int, 
     print(json.dumps(out))
 
 
-def stats_markdown(csv_path: str, title: str, command: str, out_path: str):
-    """A short markdown table of a rocprofv3 --stats kernel summary."""
+def stats_markdown(csv_path: str, title: str, command: str, out_path: str, bench_log: str = ""):
+    """A short markdown table of a rocprofv3 --stats kernel summary, with the
+    bench line the same profiled run printed (its HIP-event stage times)."""
     import csv
 
     def short(n):
@@ -137,6 +138,15 @@ def stats_markdown(csv_path: str, title: str, command: str, out_path: str):
     for r in csv.DictReader(open(csv_path)):
         lines.append(f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+    if bench_log:
+        recs = [json.loads(l) for l in open(bench_log) if l.startswith("{")]
+        if recs:
+            r = recs[-1]
+            lines += ["", f"The same run's bench line: {r['value']} {r['unit']}, {r['steps']} timed steps after "
+                      f"{r['warmup']} warm-up steps; average time of each stage over the timed steps, from HIP "
+                      "events on the launch stream (us):", "",
+                      "| stage | us |", "|---|---|"]
+            lines += [f"| {k} | {v} |" for k, v in r["stages_us"].items()]
     with open(out_path, "w") as fh:
         fh.write("\n".join(lines) + "\n")
 
@@ -218,10 +228,11 @@ def main(argv=None):
                     help="time the backward of the BF16 SwiGLU layer instead of the forward")
     ap.add_argument("--stats-md", nargs=3, metavar=("STATS_CSV", "TITLE", "OUT_MD"),
                     help="write a markdown summary of a rocprofv3 --stats kernel table and exit")
+    ap.add_argument("--bench-log", default="", help="with --stats-md: the profiled run's output (its bench line)")
     a = ap.parse_args(argv)
 
     if a.stats_md:
-        stats_markdown(a.stats_md[0], a.stats_md[1], a.traffic_command, a.stats_md[2])
+        stats_markdown(a.stats_md[0], a.stats_md[1], a.traffic_command, a.stats_md[2], a.bench_log)
         return 0
     if a.write_traffic:
         write_traffic(a.workload, a.write_traffic[0], a.write_traffic[1], a.copy_probe_mib or 1024,
