@@ -166,8 +166,8 @@ struct Params {
   int E, H, I, k;
 };
 
-template <int BM, int BN, int WM, int WN, bool GEMM1, int MODE, int NST>
-__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_scaled_kernel(Params p) {
+template <int BM, int BN, int WM, int WN, bool GEMM1, int MODE, int NST, int OCC>
+__global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_scaled_kernel(Params p) {
   using C = Cfg<BM, BN, WM, WN, GEMM1, MODE, NST>;
   constexpr int WB = C::W_BYTES;
   // one LDS array per stage, so that the compiler can tell the stages being
@@ -536,9 +536,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_scaled_kernel(Params p) 
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool GEMM1, int MODE, int NST = 2>
+// OCC workgroups per CU: the 32-row tiles of small token counts are bound by
+// the weight stream, and a second workgroup per CU fills the gaps one
+// workgroup's pipeline leaves between tasks (LDS and registers must fit OCC)
+template <int BM, int BN, int WM, int WN, bool GEMM1, int MODE, int NST = 2, int OCC = 1>
 hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   using C = Cfg<BM, BN, WM, WN, GEMM1, MODE, NST>;
+  static_assert(OCC * (NST * C::STAGE + WN * BM * 4 + (NST > 2 ? 1024 : 0)) <= 160 * 1024, "OCC workgroups fit in LDS");
   Params p;
   p.a = static_cast<const uint8_t*>(g.a);
   p.a_scale = g.a_scale;
@@ -557,10 +561,10 @@ hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   p.k = g.k;
   const int N = GEMM1 ? g.I : g.H;
   const int64_t max_tasks = (g.cap / BM) * ((N + BN - 1) / BN);
-  int64_t grid = dev.num_cus;
+  int64_t grid = static_cast<int64_t>(dev.num_cus) * OCC;
   if (grid > max_tasks) grid = max_tasks;
   if (grid < 1) grid = 1;
-  gemm_scaled_kernel<BM, BN, WM, WN, GEMM1, MODE, NST><<<static_cast<unsigned>(grid), C::THREADS, 0, s>>>(p);
+  gemm_scaled_kernel<BM, BN, WM, WN, GEMM1, MODE, NST, OCC><<<static_cast<unsigned>(grid), C::THREADS, 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -579,7 +583,7 @@ hipError_t launch_gemm2_mx_tiles(const GemmArgs& g, const DeviceInfo& dev, hipSt
     case 256: return launch<256, 256, 4, 2, false, kMx>(g, dev, s);
     case 128: return launch<128, 512, 2, 4, false, kMx>(g, dev, s);
     case 64: return launch<64, 512, 1, 8, false, kMx>(g, dev, s);
-    case 32: return launch<32, 512, 1, 8, false, kMx, 4>(g, dev, s);
+    case 32: return launch<32, 512, 1, 8, false, kMx, 2, 2>(g, dev, s);
     default: return hipErrorInvalidValue;
   }
 }
