@@ -15,16 +15,23 @@
 //     lane ends up with four consecutive output columns of one token, which
 //     become one 8-byte store);
 //   * 8 waves per workgroup (two per SIMD, so one wave's MFMAs cover the other's
-//     waits); a workgroup tile is 128 sorted rows x 512 weight rows and each
-//     wave owns 8 32x32 accumulator tiles (64 tokens x 128 weight rows), which
-//     keeps both the L2->LDS traffic and the LDS reads per MFMA low;
-//   * software pipeline of depth two: the global loads for k-step s+2 are in
-//     flight in one register set while k-step s+1 waits in the other and the
-//     MFMAs consume k-step s from LDS (double buffered); one barrier per step;
+//     waits); the workgroup tile is 256 sorted rows x 256 weight rows (128 gate
+//     + 128 up in GEMM1) when experts average >= 384 rows, else 128 x 512 (or
+//     narrower for 64- and 32-row tiles); each wave holds 128 accumulator
+//     registers, the most the register file leaves room for;
+//   * operands reach LDS by direct-to-LDS buffer loads (16 bytes a lane, 1 KB
+//     a wave instruction); two LDS stages: the loads of k-step s+1 are issued
+//     before the MFMAs of k-step s, and one barrier ends each step;
+//   * inside a k-step the MFMA fragments of the next 16-K substep are read
+//     from LDS while the current substep's MFMAs run (order pinned with
+//     scheduling-group barriers);
 //   * LDS rows of BK bf16 with the 16-byte chunk index XOR-swizzled by row, so
 //     the fragment reads of 8 consecutive rows fall on distinct banks;
 //   * GEMM1 keeps the gate rows n and up rows I + n of the same output column
-//     in one workgroup, so SwiGLU runs in registers in the epilogue.
+//     in one workgroup, so SwiGLU runs in registers in the epilogue;
+//   * what bounds it: the L2 -> LDS stream, limited per CU by the requests in
+//     flight over the L1 -> L2 latency (about 0.12 lines per clock at 66% L2
+//     hits on the Qwen3-30B-A3B shape), not by MFMA issue.
 #include "moe_common.cuh"
 #include "moe_launch.h"
 
