@@ -114,14 +114,15 @@ def test_backward_deterministic():
         assert torch.equal(getattr(a, name), getattr(b, name)), name
 
 
-def test_backward_full_size_sampled():
-    """The Qwen3-30B-A3B-shaped layer at T = 8192, in the launch configuration
-    the backward benchmark times: routing and layout compared in full; dx,
-    dw and dlogits on sampled tokens, and dW1 / dW2 of the most and the least
-    loaded expert, each from the oracle run on just the tokens that
-    determine them (a token's gradients depend on that token alone; an
-    expert's weight gradients on the tokens routed to it)."""
-    cfg = get_config("qwen3_30b_a3b_bf16")
+@pytest.mark.parametrize("name", ["qwen3_30b_a3b_bf16", "llama4_scout_bf16"])
+def test_backward_full_size_sampled(name):
+    """The Qwen3-30B-A3B- and Llama 4 Scout-shaped layers at T = 8192, in the
+    launch configuration the backward benchmark times: routing and layout
+    compared in full; dx, dw and dlogits on sampled tokens, and dW1 / dW2 of
+    the most and the least loaded expert, each from the oracle run on just
+    the tokens that determine them (a token's gradients depend on that token
+    alone; an expert's weight gradients on the tokens routed to it)."""
+    cfg = get_config(name)
     inp = make_inputs(cfg)
     dout = make_dout(cfg, 0)
     say("backward full-size sampled", cfg.name)
