@@ -375,18 +375,19 @@ moe_status_t moe_grouped_gemm_swiglu_save(const void* x, const void* w1,
 
 /*
  * moe_backward_combine -- backward of moe_combine, per sorted row.
- *   For each sorted row r < cap with a = sorted_ids[r] (t = a / k):
+ *   For each sorted row r < num_tiles * block_m with a = sorted_ids[r]
+ *   (t = a / k):
  *     dy[r, c] = bf16( topk_w[a] * dout[t, c] ) if a < A, else 0;
  *     dw[a]    = sum_c dout[t, c] * y[a, c] (fp32, each real a once).
  *   dout [T, H] bf16; topk_w [T, k] fp32; y [T*k, H] bf16 (the forward's
- *   GEMM2 rows); sorted_ids [cap] int32 from moe_align_sort; dy [cap, H]
- *   bf16 out; dw [T, k] fp32 out.
- * Rows of sorted_ids at or past num_tiles * block_m must hold ids >= A (the
- * moe_align_sort layout fills them so). Requires H % 8 == 0.
+ *   GEMM2 rows); sorted_ids [cap] int32, num_tiles (device int32) from
+ *   moe_align_sort with the same block_m; dy [cap, H] bf16 out (rows past
+ *   num_tiles * block_m are not written); dw [T, k] fp32 out.
+ * Requires H % 8 == 0.
  */
 moe_status_t moe_backward_combine(const uint16_t* dout, const float* topk_w, const uint16_t* y,
-                                  const int32_t* sorted_ids, int64_t T, int32_t k, int32_t H, int64_t cap,
-                                  uint16_t* dy, float* dw, void* stream);
+                                  const int32_t* sorted_ids, const int32_t* num_tiles, int64_t T, int32_t k,
+                                  int32_t H, int32_t block_m, int64_t cap, uint16_t* dy, float* dw, void* stream);
 
 /*
  * moe_route_backward -- gradient of the router logits from the gradient of
@@ -406,12 +407,13 @@ moe_status_t moe_route_backward(const float* topk_w, const int32_t* topk_ids, co
 /*
  * moe_gather_rows -- the tokens in sorted-row order (the token operand of the
  * W1 weight gradient): x_sorted[r, :] = x[sorted_ids[r] / k, :] for real rows,
- * 0 for pad rows, every r < cap.
- *   x [T, H] bf16; sorted_ids [cap] int32; x_sorted [cap, H] bf16 out.
+ * 0 for pad rows, every r < num_tiles * block_m (later rows are not written).
+ *   x [T, H] bf16; sorted_ids [cap] int32 and num_tiles (device int32) from
+ *   moe_align_sort with the same block_m; x_sorted [cap, H] bf16 out.
  * Requires H % 8 == 0.
  */
-moe_status_t moe_gather_rows(const uint16_t* x, const int32_t* sorted_ids, int64_t T, int32_t k, int32_t H,
-                             int64_t cap, uint16_t* x_sorted, void* stream);
+moe_status_t moe_gather_rows(const uint16_t* x, const int32_t* sorted_ids, const int32_t* num_tiles, int64_t T,
+                             int32_t k, int32_t H, int32_t block_m, int64_t cap, uint16_t* x_sorted, void* stream);
 
 /*
  * moe_grouped_gemm_dh -- gradient through GEMM2 and the SwiGLU, per sorted

@@ -54,9 +54,9 @@ SIGNATURES = {
                                              _I32, _I64, _P, _P, _P, _P, _SZ, _P]),
     "moe_grouped_gemm_swiglu_save": (_I32, [_P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I64,
                                             _P, _P, _P]),
-    "moe_backward_combine": (_I32, [_P, _P, _P, _P, _I64, _I32, _I32, _I64, _P, _P, _P]),
+    "moe_backward_combine": (_I32, [_P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I64, _P, _P, _P]),
     "moe_route_backward": (_I32, [_P, _P, _P, _I64, _I32, _I32, _I32, _I32, _P, _P]),
-    "moe_gather_rows": (_I32, [_P, _P, _I64, _I32, _I32, _I64, _P, _P]),
+    "moe_gather_rows": (_I32, [_P, _P, _P, _I64, _I32, _I32, _I32, _I64, _P, _P]),
     "moe_grouped_gemm_dh": (_I32, [_P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I64, _P, _P]),
     "moe_grouped_gemm_dx": (_I32, [_P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32, _I32, _I64, _P, _P]),
     "moe_grouped_gemm_wgrad": (_I32, [_P, _P, _I32, _I32, _P, _I64, _I32, _I32, _I32, _I64, _P, _P]),
@@ -312,7 +312,8 @@ def moe_backward_combine(dout, topk_w, y, sort: SortResult, dy=None, dw=None, st
     if dw is None:
         dw = torch.empty((T, k), dtype=torch.float32, device=dout.device)
     _check("moe_backward_combine", lib().moe_backward_combine(
-        _p(dout), _p(topk_w), _p(y), _p(sort.sorted_ids), T, k, H, sort.cap, _p(dy), _p(dw), _s(stream)))
+        _p(dout), _p(topk_w), _p(y), _p(sort.sorted_ids), _p(sort.num_tiles), T, k, H, sort.block_m, sort.cap,
+        _p(dy), _p(dw), _s(stream)))
     return dy, dw
 
 
@@ -336,8 +337,8 @@ def moe_gather_rows(x, sort: SortResult, out=None, stream=None):
     H = x.shape[1]
     if out is None:
         out = torch.empty((max(sort.cap, 1), H), dtype=torch.bfloat16, device=x.device)
-    _check("moe_gather_rows", lib().moe_gather_rows(_p(x), _p(sort.sorted_ids), sort.T, sort.k, H, sort.cap,
-                                                    _p(out), _s(stream)))
+    _check("moe_gather_rows", lib().moe_gather_rows(_p(x), _p(sort.sorted_ids), _p(sort.num_tiles), sort.T, sort.k,
+                                                    H, sort.block_m, sort.cap, _p(out), _s(stream)))
     return out
 
 

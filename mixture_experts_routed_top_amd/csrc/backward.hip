@@ -2,6 +2,7 @@
 // the pages' follow-up work: Liger-Kernel PR #1463, MoEBenchmark results,
 // forward and backward).
 //
+//   (both per-row kernels cover the rows of the num_tiles tiles only)
 //   combine backward: for each sorted row r holding assignment a = (t, j):
 //     dY[r, :] = bf16( w[t, j] * dout[t, :] )          (pad rows: 0)
 //     dw[t, j] = sum_c dout[t, c] * Y[a, c]             (fp32, one wave per row)
@@ -22,11 +23,12 @@ __global__ __launch_bounds__(256) void backward_combine_kernel(const uint16_t* _
                                                                const float* __restrict__ w,
                                                                const uint16_t* __restrict__ y,
                                                                const int32_t* __restrict__ sorted_ids,
-                                                               int64_t A, int kk, int H, int64_t rows,
+                                                               const int32_t* __restrict__ num_tiles,
+                                                               int block_m, int64_t A, int kk, int H,
                                                                uint16_t* __restrict__ dy, float* __restrict__ dw) {
   const int lane = threadIdx.x & 63;
   const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (r >= rows) return;
+  if (r >= static_cast<int64_t>(*num_tiles) * block_m) return;   // rows no tile covers
   const int a = sorted_ids[r];
   uint16_t* dyr = dy + r * H;
   if (a >= A) {
@@ -38,6 +40,8 @@ __global__ __launch_bounds__(256) void backward_combine_kernel(const uint16_t* _
   const uint16_t* dr = dout + t * H;
   const uint16_t* yr = y + static_cast<int64_t>(a) * H;
   float dot = 0.0f;
+  // unrolled so that several 16-byte loads per lane are in flight
+#pragma unroll 4
   for (int c = lane * 8; c < H; c += 512) {
     const uint4 dq = *reinterpret_cast<const uint4*>(dr + c);
     const uint4 yq = *reinterpret_cast<const uint4*>(yr + c);
@@ -87,12 +91,12 @@ __global__ __launch_bounds__(256) void route_backward_kernel(const float* __rest
 
 // one wave per sorted row
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __restrict__ x,
-                                                          const int32_t* __restrict__ sorted_ids, int64_t A,
-                                                          int kk, int H, int64_t rows,
-                                                          uint16_t* __restrict__ out) {
+                                                          const int32_t* __restrict__ sorted_ids,
+                                                          const int32_t* __restrict__ num_tiles, int block_m,
+                                                          int64_t A, int kk, int H, uint16_t* __restrict__ out) {
   const int lane = threadIdx.x & 63;
   const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (r >= rows) return;
+  if (r >= static_cast<int64_t>(*num_tiles) * block_m) return;   // rows no tile covers
   const int a = sorted_ids[r];
   uint16_t* o = out + r * H;
   if (a >= A) {
@@ -100,6 +104,7 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __rest
     return;
   }
   const uint16_t* src = x + static_cast<int64_t>(a / kk) * H;
+#pragma unroll 4
   for (int c = lane * 8; c < H; c += 512)
     *reinterpret_cast<uint4*>(o + c) = *reinterpret_cast<const uint4*>(src + c);
 }
@@ -107,10 +112,10 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t* __rest
 }  // namespace
 
 hipError_t launch_backward_combine(const uint16_t* dout, const float* w, const uint16_t* y,
-                                   const int32_t* sorted_ids, int64_t A, int kk, int H, int64_t rows,
-                                   uint16_t* dy, float* dw, hipStream_t s) {
-  backward_combine_kernel<<<static_cast<unsigned>((rows + 3) / 4), 256, 0, s>>>(dout, w, y, sorted_ids, A, kk, H,
-                                                                                rows, dy, dw);
+                                   const int32_t* sorted_ids, const int32_t* num_tiles, int block_m, int64_t A,
+                                   int kk, int H, int64_t cap, uint16_t* dy, float* dw, hipStream_t s) {
+  backward_combine_kernel<<<static_cast<unsigned>((cap + 3) / 4), 256, 0, s>>>(dout, w, y, sorted_ids, num_tiles,
+                                                                               block_m, A, kk, H, dy, dw);
   return hipGetLastError();
 }
 
@@ -122,9 +127,10 @@ hipError_t launch_route_backward(const float* w, const int32_t* ids, const float
   return hipGetLastError();
 }
 
-hipError_t launch_gather_rows(const uint16_t* x, const int32_t* sorted_ids, int64_t A, int kk, int H, int64_t rows,
-                              uint16_t* out, hipStream_t s) {
-  gather_rows_kernel<<<static_cast<unsigned>((rows + 3) / 4), 256, 0, s>>>(x, sorted_ids, A, kk, H, rows, out);
+hipError_t launch_gather_rows(const uint16_t* x, const int32_t* sorted_ids, const int32_t* num_tiles, int block_m,
+                              int64_t A, int kk, int H, int64_t cap, uint16_t* out, hipStream_t s) {
+  gather_rows_kernel<<<static_cast<unsigned>((cap + 3) / 4), 256, 0, s>>>(x, sorted_ids, num_tiles, block_m, A, kk,
+                                                                          H, out);
   return hipGetLastError();
 }
 

@@ -340,18 +340,18 @@ moe_status_t check_bwd(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k, in
 }  // namespace
 
 moe_status_t moe_backward_combine(const uint16_t* dout, const float* topk_w, const uint16_t* y,
-                                  const int32_t* sorted_ids, int64_t T, int32_t k, int32_t H, int64_t cap,
-                                  uint16_t* dy, float* dw, void* stream) {
-  if (T < 0 || k < 1 || k > MOE_MAX_TOPK || H <= 0 || cap < 0) return MOE_ERR_INVALID_ARG;
+                                  const int32_t* sorted_ids, const int32_t* num_tiles, int64_t T, int32_t k,
+                                  int32_t H, int32_t block_m, int64_t cap, uint16_t* dy, float* dw, void* stream) {
+  if (T < 0 || k < 1 || k > MOE_MAX_TOPK || H <= 0 || cap < 0 || !valid_block_m(block_m)) return MOE_ERR_INVALID_ARG;
   if (H % 8) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (T == 0 || cap == 0) return MOE_OK;
-  if (!dout || !topk_w || !y || !sorted_ids || !dy || !dw) return MOE_ERR_INVALID_ARG;
+  if (!dout || !topk_w || !y || !sorted_ids || !num_tiles || !dy || !dw) return MOE_ERR_INVALID_ARG;
   if (!aligned(dout, 16) || !aligned(y, 16) || !aligned(dy, 16) || !aligned(topk_w, 4) || !aligned(dw, 4))
     return MOE_ERR_INVALID_ARG;
   moe::DeviceInfo dev;
   if (moe_status_t st = current_device(&dev)) return st;
-  return launched(moe::launch_backward_combine(dout, topk_w, y, sorted_ids, T * k, k, H, cap, dy, dw,
-                                               static_cast<hipStream_t>(stream)));
+  return launched(moe::launch_backward_combine(dout, topk_w, y, sorted_ids, num_tiles, block_m, T * k, k, H, cap,
+                                               dy, dw, static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_route_backward(const float* topk_w, const int32_t* topk_ids, const float* dw, int64_t T,
@@ -367,15 +367,17 @@ moe_status_t moe_route_backward(const float* topk_w, const int32_t* topk_ids, co
                                              static_cast<hipStream_t>(stream)));
 }
 
-moe_status_t moe_gather_rows(const uint16_t* x, const int32_t* sorted_ids, int64_t T, int32_t k, int32_t H,
-                             int64_t cap, uint16_t* x_sorted, void* stream) {
-  if (T < 0 || k < 1 || H <= 0 || cap < 0) return MOE_ERR_INVALID_ARG;
+moe_status_t moe_gather_rows(const uint16_t* x, const int32_t* sorted_ids, const int32_t* num_tiles, int64_t T,
+                             int32_t k, int32_t H, int32_t block_m, int64_t cap, uint16_t* x_sorted, void* stream) {
+  if (T < 0 || k < 1 || H <= 0 || cap < 0 || !valid_block_m(block_m)) return MOE_ERR_INVALID_ARG;
   if (H % 8) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (T == 0 || cap == 0) return MOE_OK;
-  if (!x || !sorted_ids || !x_sorted || !aligned(x, 16) || !aligned(x_sorted, 16)) return MOE_ERR_INVALID_ARG;
+  if (!x || !sorted_ids || !num_tiles || !x_sorted || !aligned(x, 16) || !aligned(x_sorted, 16))
+    return MOE_ERR_INVALID_ARG;
   moe::DeviceInfo dev;
   if (moe_status_t st = current_device(&dev)) return st;
-  return launched(moe::launch_gather_rows(x, sorted_ids, T * k, k, H, cap, x_sorted, static_cast<hipStream_t>(stream)));
+  return launched(moe::launch_gather_rows(x, sorted_ids, num_tiles, block_m, T * k, k, H, cap, x_sorted,
+                                          static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_grouped_gemm_dh(const void* dy, const void* w2, const void* gu, const int32_t* sorted_ids,

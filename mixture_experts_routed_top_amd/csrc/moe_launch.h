@@ -86,12 +86,12 @@ hipError_t launch_bwd_dx(const BwdArgs& g, const DeviceInfo& dev, hipStream_t s)
 hipError_t launch_bwd_wgrad(const void* pm, const void* qn, int M, int N, const BwdArgs& g, float* dw,
                             const DeviceInfo& dev, hipStream_t s);
 hipError_t launch_backward_combine(const uint16_t* dout, const float* w, const uint16_t* y,
-                                   const int32_t* sorted_ids, int64_t A, int kk, int H, int64_t rows,
-                                   uint16_t* dy, float* dw, hipStream_t s);
+                                   const int32_t* sorted_ids, const int32_t* num_tiles, int block_m, int64_t A,
+                                   int kk, int H, int64_t cap, uint16_t* dy, float* dw, hipStream_t s);
 hipError_t launch_route_backward(const float* w, const int32_t* ids, const float* dw, int64_t T, int E, int k,
                                  int kk, int score, float* dlogits, hipStream_t s);
-hipError_t launch_gather_rows(const uint16_t* x, const int32_t* sorted_ids, int64_t A, int kk, int H, int64_t rows,
-                              uint16_t* out, hipStream_t s);
+hipError_t launch_gather_rows(const uint16_t* x, const int32_t* sorted_ids, const int32_t* num_tiles, int block_m,
+                              int64_t A, int kk, int H, int64_t cap, uint16_t* out, hipStream_t s);
 
 bool gemm_fp8_supports(int block_m);
 hipError_t launch_gemm1_fp8(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s);

@@ -173,14 +173,16 @@ def test_backward_host_validation():
     save = lambda h=FAKE, gu=FAKE, T=T, cap=cap: L.moe_grouped_gemm_swiglu_save(
         FAKE, FAKE, FAKE, FAKE, FAKE, T, H, I, E, k, 256, cap, h, gu, NULL)
     assert save(gu=NULL) == 1 and save(gu=MIS) == 1 and save(T=0, cap=0, gu=NULL) == 0
-    assert L.moe_backward_combine(FAKE, FAKE, FAKE, FAKE, T, k, 100, cap, FAKE, FAKE, NULL) == 2
-    assert L.moe_backward_combine(FAKE, FAKE, MIS, FAKE, T, k, H, cap, FAKE, FAKE, NULL) == 1
-    assert L.moe_backward_combine(NULL, NULL, NULL, NULL, 0, k, H, cap, NULL, NULL, NULL) == 0
+    bc = lambda y=FAKE, nt=FAKE, T=T, H=H, bm=256: L.moe_backward_combine(FAKE, FAKE, y, FAKE, nt, T, k, H, bm, cap,
+                                                                          FAKE, FAKE, NULL)
+    assert bc(H=100) == 2 and bc(y=MIS) == 1 and bc(nt=NULL) == 1 and bc(bm=48) == 1
+    assert L.moe_backward_combine(NULL, NULL, NULL, NULL, NULL, 0, k, H, 256, cap, NULL, NULL, NULL) == 0
     assert L.moe_route_backward(FAKE, FAKE, FAKE, T, E, 5, 0, 0, FAKE, NULL) == 1     # k > E
     assert L.moe_route_backward(FAKE, FAKE, FAKE, T, E, 2, 0, 7, FAKE, NULL) == 1     # unknown score
     assert L.moe_route_backward(FAKE, FAKE, NULL, T, E, 2, 0, 0, FAKE, NULL) == 1
-    assert L.moe_gather_rows(FAKE, FAKE, T, k, 100, cap, FAKE, NULL) == 2
-    assert L.moe_gather_rows(FAKE, FAKE, T, k, H, cap, MIS, NULL) == 1
+    assert L.moe_gather_rows(FAKE, FAKE, FAKE, T, k, 100, 256, cap, FAKE, NULL) == 2
+    assert L.moe_gather_rows(FAKE, FAKE, FAKE, T, k, H, 256, cap, MIS, NULL) == 1
+    assert L.moe_gather_rows(FAKE, FAKE, NULL, T, k, H, 256, cap, FAKE, NULL) == 1
 
 
 def test_down_combine_host_validation():
