@@ -35,7 +35,11 @@
 // (E4M3) or 64-byte (E2M1) weight row, and one 32-bit scale word per row
 // (the fp32 1x128 token scale, or four E8M0 bytes). LDS is double buffered;
 // 16-byte chunks are XOR-swizzled per row so that the fragment reads of 8
-// consecutive rows fall on distinct banks.
+// consecutive rows fall on distinct banks. The 32-row MX GEMM1 tile (small
+// token counts, bound by the weight stream) stages two such k-steps at once:
+// a 64-byte E2M1 slice is half an L2 line, and the number of requests a CU
+// keeps in flight, not their size, limits the stream, so whole 128-byte
+// weight slices carry twice the bytes per request.
 #include "moe_common.cuh"
 #include "moe_launch.h"
 
@@ -47,19 +51,24 @@ constexpr int kXcds = 8;
 constexpr int kFp8Block = 1;
 constexpr int kMx = 2;
 
-template <int BM, int BN, int WM, int WN, bool GEMM1, int MODE, int NST_ = 2>
+template <int BM, int BN, int WM, int WN, bool GEMM1, int MODE, int NST_ = 2, int KSUB_ = 1>
 struct Cfg {
   static constexpr int NST = NST_;                          // LDS stages (2 or 4)
-  static constexpr int W_BYTES = MODE == kMx ? 64 : 128;   // weight row bytes per k-step
+  // 128-K substeps per stage. MX stages two, so that a weight row's slice is
+  // 128 bytes (256 E2M1): one whole L2 line per request instead of two halves
+  static constexpr int KSUB = KSUB_;
+  static constexpr int W_BYTES = MODE == kMx ? 64 * KSUB : 128;   // weight row bytes per stage
   static constexpr int B_ROWS = GEMM1 ? 2 * BN : BN;
   static constexpr int TM = BM / WM, TN = BN / WN;
   static constexpr int FM = TM / 32, FN = TN / 32;
   static constexpr int HALVES = GEMM1 ? 2 : 1;
   static constexpr int WAVES = WM * WN;
   static constexpr int THREADS = 64 * WAVES;
-  static constexpr int A_REGION = BM * 128;
+  static constexpr int A_SUB = BM * 128;                      // token rows of one substep
+  static constexpr int A_REGION = A_SUB * KSUB;
   static constexpr int W_REGION = B_ROWS * W_BYTES;
-  static constexpr int A_GROUPS = BM / 8;                     // 1 KB direct-to-LDS loads of token rows
+  static constexpr int A_GROUPS_SUB = BM / 8;                 // 1 KB direct-to-LDS loads of token rows
+  static constexpr int A_GROUPS = A_GROUPS_SUB * KSUB;
   static constexpr int W_GROUPS = W_REGION / 1024;            // ... of weight rows
   static constexpr int GROUPS = A_GROUPS + W_GROUPS;
   static constexpr int GPW = (GROUPS + WAVES - 1) / WAVES;    // data loads per wave per k-step
@@ -67,13 +76,15 @@ struct Cfg {
   // one load never mixes the two operands), then (MX) weight rows
   static constexpr int S_TOK = (BM + 63) / 64 * 64;
   static constexpr int S_ROWS = S_TOK + (MODE == kMx ? B_ROWS : 0);
-  static constexpr int S_GROUPS = (S_ROWS + 63) / 64;         // 256 B direct-to-LDS loads of scale words
+  static constexpr int S_GROUPS_SUB = (S_ROWS + 63) / 64;     // 256 B direct-to-LDS loads of scale words
+  static constexpr int S_GROUPS = S_GROUPS_SUB * KSUB;
   static constexpr int SPW = (S_GROUPS + WAVES - 1) / WAVES;
   static constexpr int STAGE = A_REGION + W_REGION + S_GROUPS * 256;
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile is a multiple of 32");
   static_assert(BM % 8 == 0 && W_REGION % 1024 == 0, "whole 1 KB load groups");
   static_assert(MODE != kFp8Block || TN <= 128, "a wave's weight rows share one 128x128 scale block");
   static_assert(NST == 2 || NST == 4, "double or quadruple buffering");
+  static_assert(KSUB == 1 || (KSUB == 2 && MODE == kMx && NST == 2), "two substeps: MX, double buffered");
   static_assert(NST * STAGE + WN * BM * 4 + (NST > 2 ? 1024 : 0) <= 160 * 1024, "the stages fit in LDS");
   static_assert((NST - 2) * (GPW + SPW) < 64, "outstanding loads fit the counter");
 };
@@ -120,10 +131,11 @@ typedef __attribute__((address_space(4))) const float* const_f32_ptr;   // read-
 // that one wait count fits all: a slot without a group loads zeros into
 // `sink`, an LDS area nobody reads.
 template <class C>
-__device__ __forceinline__ void issue_loads(char* stage, char* sink, int kt, int nk, int wave,
+__device__ __forceinline__ void issue_loads(char* stage, char* sink, int kt, int nk, int nk128, int wave,
                                             __amdgpu_buffer_rsrc_t a_rsrc, __amdgpu_buffer_rsrc_t w_rsrc,
                                             __amdgpu_buffer_rsrc_t as_rsrc, __amdgpu_buffer_rsrc_t ws_rsrc,
-                                            const uint32_t (&doff)[C::GPW], const uint32_t (&soff)[C::SPW]) {
+                                            const uint32_t (&doff)[C::GPW], const uint32_t (&soff)[C::SPW],
+                                            const uint32_t (&dsub)[C::GPW]) {
   constexpr bool kUniform = C::NST > 2;
   const bool live = kt < nk;
 #pragma unroll
@@ -131,10 +143,14 @@ __device__ __forceinline__ void issue_loads(char* stage, char* sink, int kt, int
     const int g = wave * C::GPW + q;
     const bool real = C::GROUPS % C::WAVES == 0 || g < C::GROUPS;
     if (real || kUniform) {
-      const __amdgpu_buffer_rsrc_t rsrc = g < C::A_GROUPS ? a_rsrc : w_rsrc;
+      const bool tok = g < C::A_GROUPS;
+      const int ks = kt * C::KSUB + (tok ? g / C::A_GROUPS_SUB : 0);   // 128-K substep of a token group
+      const __amdgpu_buffer_rsrc_t rsrc = tok ? a_rsrc : w_rsrc;
       char* const dst = real ? stage + g * 1024 : sink;
-      const uint32_t voff = live && real ? doff[q] : kOob;
-      const uint32_t soffset = static_cast<uint32_t>(kt) * (g < C::A_GROUPS ? 128 : C::W_BYTES);
+      // a weight chunk of the second substep past K (K ends inside the stage) is not fetched
+      const bool ok = tok ? ks < nk128 : live && (C::KSUB == 1 || kt * C::KSUB + static_cast<int>(dsub[q]) < nk128);
+      const uint32_t voff = ok && real ? doff[q] : kOob;
+      const uint32_t soffset = tok ? static_cast<uint32_t>(ks) * 128 : static_cast<uint32_t>(kt) * C::W_BYTES;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)dst, 16, voff, soffset, 0, 0);
     }
   }
@@ -143,10 +159,11 @@ __device__ __forceinline__ void issue_loads(char* stage, char* sink, int kt, int
     const int g = wave + q * C::WAVES;
     const bool real = g < C::S_GROUPS;
     if (real || kUniform) {
-      const __amdgpu_buffer_rsrc_t rsrc = g * 64 < C::S_TOK ? as_rsrc : ws_rsrc;
+      const int gs = g % C::S_GROUPS_SUB, ks = kt * C::KSUB + g / C::S_GROUPS_SUB;
+      const __amdgpu_buffer_rsrc_t rsrc = gs * 64 < C::S_TOK ? as_rsrc : ws_rsrc;
       char* const dst = real ? stage + C::A_REGION + C::W_REGION + g * 256 : sink;
-      const uint32_t voff = live && real ? soff[q] : kOob;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)dst, 4, voff, static_cast<uint32_t>(kt) * 4, 0, 0);
+      const uint32_t voff = ks < nk128 && real ? soff[q] : kOob;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)dst, 4, voff, static_cast<uint32_t>(ks) * 4, 0, 0);
     }
   }
 }
@@ -166,9 +183,9 @@ struct Params {
   int E, H, I, k;
 };
 
-template <int BM, int BN, int WM, int WN, bool GEMM1, int MODE, int NST, int OCC>
+template <int BM, int BN, int WM, int WN, bool GEMM1, int MODE, int NST, int OCC, int KSUB>
 __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_scaled_kernel(Params p) {
-  using C = Cfg<BM, BN, WM, WN, GEMM1, MODE, NST>;
+  using C = Cfg<BM, BN, WM, WN, GEMM1, MODE, NST, KSUB>;
   constexpr int WB = C::W_BYTES;
   // one LDS array per stage, so that the compiler can tell the stages being
   // filled by direct-to-LDS loads from the one being read
@@ -187,7 +204,8 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_scaled_kernel(Params p
   const int K = GEMM1 ? p.H : p.I;
   const int ntn = (N + BN - 1) / BN;
   const int total = *p.num_tiles * ntn;
-  const int nk = K / 128;
+  const int nk128 = K / 128;                         // 128-K substeps
+  const int nk = (nk128 + KSUB - 1) / KSUB;          // stages
   const int wrows = GEMM1 ? 2 * p.I : p.H;           // weight rows of one expert
   const int wrow_bytes = MODE == kMx ? K / 2 : K;
   const int srow_bytes = MODE == kMx ? K / 32 : (K / 128) * 4;   // scale bytes per token row
@@ -237,12 +255,14 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_scaled_kernel(Params p
     // data loads: group g (1 KB) fills 8 token rows (g < A_GROUPS) or 1 KB of
     // weight rows; lane l writes the 16 bytes at l * 16 of the group
     uint32_t doff[C::GPW];
+    uint32_t dsub[C::GPW];   // substep of this lane's weight chunk (two-substep stages)
 #pragma unroll
     for (int q = 0; q < C::GPW; ++q) {
       const int g = wave * C::GPW + q;
       doff[q] = kOob;
+      dsub[q] = 0;
       if (g < C::A_GROUPS) {
-        const int row = g * 8 + (lane >> 3), pc = lane & 7;
+        const int row = (g % C::A_GROUPS_SUB) * 8 + (lane >> 3), pc = lane & 7;
         const int64_t src = token_row(row);
         if (src >= 0) doff[q] = static_cast<uint32_t>(src * K + ((pc ^ (row & 7)) << 4));
       } else if (g < C::GROUPS) {
@@ -251,6 +271,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_scaled_kernel(Params p
         const int lc = WB == 128 ? (pc ^ (br & 7)) : (pc ^ ((br >> 2) & 3));
         const int wr = weight_row(br);
         if (wr >= 0) doff[q] = static_cast<uint32_t>(wr) * wrow_bytes + (lc << 4);
+        dsub[q] = static_cast<uint32_t>(lc * 16 / 64) % C::KSUB;
       }
     }
     // scale-word loads: group g (256 B) holds the k-step's scale word of 64
@@ -258,7 +279,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_scaled_kernel(Params p
     uint32_t soff_[C::SPW];
 #pragma unroll
     for (int q = 0; q < C::SPW; ++q) {
-      const int r = (wave + q * C::WAVES) * 64 + lane;
+      const int r = ((wave + q * C::WAVES) % C::S_GROUPS_SUB) * 64 + lane;
       soff_[q] = kOob;
       if (r < BM) {
         const int64_t src = token_row(r);
@@ -279,7 +300,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_scaled_kernel(Params p
     }
 
     auto load = [&](char* stage, int kt) {
-      issue_loads<C>(stage, sink, kt, nk, wave, a_rsrc, w_rsrc, as_rsrc, ws_rsrc, doff, soff_);
+      issue_loads<C>(stage, sink, kt, nk, nk128, wave, a_rsrc, w_rsrc, as_rsrc, ws_rsrc, doff, soff_, dsub);
     };
 
     f32x16 acc[C::HALVES][C::FM][C::FN];
@@ -297,38 +318,48 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_scaled_kernel(Params p
       for (int i = 0; i < C::FM; ++i) fprev[h][i] = 0.0f;
 
     auto compute = [&](const char* base, int kt) {
-      const uint32_t* sc = reinterpret_cast<const uint32_t*>(base + C::A_REGION + C::W_REGION);
       const int hl = lane >> 5;   // which 32-deep half of a 64-deep MFMA step this lane holds
-      uint32_t tsc[C::FM];
-#pragma unroll
-      for (int i = 0; i < C::FM; ++i) tsc[i] = sc[wm * C::TM + i * 32 + (lane & 31)];
       if (MODE == kMx) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const int blk = 2 * s + hl;                 // 32-element K block of this lane's scales
-          i32x8 xf[C::FM];
-          int xs[C::FM];
+        for (int sub = 0; sub < C::KSUB; ++sub) {
+          if (C::KSUB > 1 && kt * C::KSUB + sub >= nk128) break;   // K ends inside the stage
+          const char* abase = base + sub * C::A_SUB;
+          const uint32_t* sc =
+              reinterpret_cast<const uint32_t*>(base + C::A_REGION + C::W_REGION + sub * C::S_GROUPS_SUB * 256);
+          uint32_t tsc[C::FM];
 #pragma unroll
-          for (int i = 0; i < C::FM; ++i) {
-            const int r = wm * C::TM + i * 32 + (lane & 31);
-            xf[i] = frag32(base + a_off(r, s * 4 + hl), base + a_off(r, s * 4 + 2 + hl));
-            xs[i] = static_cast<int>((tsc[i] >> (8 * blk)) & 0xFF);
-          }
+          for (int i = 0; i < C::FM; ++i) tsc[i] = sc[wm * C::TM + i * 32 + (lane & 31)];
 #pragma unroll
-          for (int h = 0; h < C::HALVES; ++h) {
+          for (int s = 0; s < 2; ++s) {
+            const int blk = 2 * s + hl;               // 32-element K block of this lane's scales
+            i32x8 xf[C::FM];
+            int xs[C::FM];
 #pragma unroll
-            for (int j = 0; j < C::FN; ++j) {
-              const int r = h * BN + wn * C::TN + j * 32 + (lane & 31);
-              const i32x8 wf = frag16(base + C::A_REGION + w_off<WB>(r, s * 2 + hl));
-              const int ws = static_cast<int>((sc[C::S_TOK + r] >> (8 * blk)) & 0xFF);
+            for (int i = 0; i < C::FM; ++i) {
+              const int r = wm * C::TM + i * 32 + (lane & 31);
+              xf[i] = frag32(abase + a_off(r, s * 4 + hl), abase + a_off(r, s * 4 + 2 + hl));
+              xs[i] = static_cast<int>((tsc[i] >> (8 * blk)) & 0xFF);
+            }
 #pragma unroll
-              for (int i = 0; i < C::FM; ++i)
-                acc[h][i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf, xf[i], acc[h][i][j], 4, 0, 0, ws,
-                                                                             0, xs[i]);
+            for (int h = 0; h < C::HALVES; ++h) {
+#pragma unroll
+              for (int j = 0; j < C::FN; ++j) {
+                const int r = h * BN + wn * C::TN + j * 32 + (lane & 31);
+                const i32x8 wf = frag16(base + C::A_REGION + w_off<WB>(r, sub * 4 + s * 2 + hl));
+                const int ws = static_cast<int>((sc[C::S_TOK + r] >> (8 * blk)) & 0xFF);
+#pragma unroll
+                for (int i = 0; i < C::FM; ++i)
+                  acc[h][i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf, xf[i], acc[h][i][j], 4, 0, 0,
+                                                                               ws, 0, xs[i]);
+              }
             }
           }
         }
       } else {
+        const uint32_t* sc = reinterpret_cast<const uint32_t*>(base + C::A_REGION + C::W_REGION);
+        uint32_t tsc[C::FM];
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i) tsc[i] = sc[wm * C::TM + i * 32 + (lane & 31)];
         float wsc[C::HALVES];
 #pragma unroll
         for (int h = 0; h < C::HALVES; ++h)
@@ -539,9 +570,9 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_scaled_kernel(Params p
 // OCC workgroups per CU: the 32-row tiles of small token counts are bound by
 // the weight stream, and a second workgroup per CU fills the gaps one
 // workgroup's pipeline leaves between tasks (LDS and registers must fit OCC)
-template <int BM, int BN, int WM, int WN, bool GEMM1, int MODE, int NST = 2, int OCC = 1>
+template <int BM, int BN, int WM, int WN, bool GEMM1, int MODE, int NST = 2, int OCC = 1, int KSUB = 1>
 hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
-  using C = Cfg<BM, BN, WM, WN, GEMM1, MODE, NST>;
+  using C = Cfg<BM, BN, WM, WN, GEMM1, MODE, NST, KSUB>;
   static_assert(OCC * (NST * C::STAGE + WN * BM * 4 + (NST > 2 ? 1024 : 0)) <= 160 * 1024, "OCC workgroups fit in LDS");
   Params p;
   p.a = static_cast<const uint8_t*>(g.a);
@@ -564,7 +595,7 @@ hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   int64_t grid = static_cast<int64_t>(dev.num_cus) * OCC;
   if (grid > max_tasks) grid = max_tasks;
   if (grid < 1) grid = 1;
-  gemm_scaled_kernel<BM, BN, WM, WN, GEMM1, MODE, NST, OCC><<<static_cast<unsigned>(grid), C::THREADS, 0, s>>>(p);
+  gemm_scaled_kernel<BM, BN, WM, WN, GEMM1, MODE, NST, OCC, KSUB><<<static_cast<unsigned>(grid), C::THREADS, 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -573,7 +604,7 @@ hipError_t launch_gemm1_mx_tiles(const GemmArgs& g, const DeviceInfo& dev, hipSt
     case 256: return launch<256, 128, 4, 2, true, kMx>(g, dev, s);
     case 128: return launch<128, 256, 4, 2, true, kMx>(g, dev, s);
     case 64: return launch<64, 256, 1, 8, true, kMx>(g, dev, s);
-    case 32: return launch<32, 256, 1, 8, true, kMx, 4>(g, dev, s);
+    case 32: return launch<32, 256, 1, 8, true, kMx, 2, 1, 2>(g, dev, s);
     default: return hipErrorInvalidValue;
   }
 }

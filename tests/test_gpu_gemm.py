@@ -230,6 +230,7 @@ SCALED_SHAPES = [  # T, H, E, k, I, block_m
     (300, 1024, 32, 8, 512, 128),
     (1, 256, 4, 2, 128, 32),
     (700, 1024, 8, 4, 384, 256),   # 256-row tiles: full and ragged tiles, partial column tiles
+    (200, 640, 8, 2, 384, 32),     # 32-row tiles with an odd number of 128-K steps in both GEMMs
 ]
 
 
