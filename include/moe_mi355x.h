@@ -1,11 +1,16 @@
 /*
- * moe_mi355x.h -- C ABI of the routed-expert MoE MLP forward for MI355X (gfx950).
+ * moe_mi355x.h -- C ABI of the routed-expert MoE MLP for MI355X (gfx950).
  *
  * The forward of a routed-expert MoE MLP layer, split into the calls below and
  * run on one GPU:
  *
  *   moe_route -> moe_align_sort -> [moe_quantize_fp8 | moe_quantize_mxfp8 (x)]
  *     -> moe_grouped_gemm_swiglu -> moe_grouped_gemm_down -> moe_combine
+ *
+ * with variants for shared experts (moe_route_shared), the squared-ReLU
+ * expert (moe_grouped_gemm_relu2) and GEMM2 with the combine fused
+ * (moe_grouped_gemm_down_combine), and the BF16 backward at the end of the
+ * file.
  *
  * What is computed follows the pages that describe the method:
  *   - TileScale PR #70 "SM90 FP8 distributed MegaMoE example", Design section:
