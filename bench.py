@@ -338,12 +338,23 @@ def measure(cfg, inp, steps: int, warmup: int, block_m=None, data=None, fused_co
     dom = max((g1, g2), key=lambda n: stage_us[n])
     fl_mult = {"gemm1_swiglu": 4, "gemm1_relu2": 2, "gemm2_down": 2, "gemm2_down_combine": 2}[dom]
     dom_flops = fl_mult * cfg.T * (cfg.k + cfg.n_shared) * cfg.H * cfg.I   # rows the kernel computes
-    achieved = dom_flops / (stage_us[dom] * 1e-6) / 1e12
     peak = PEAK_TFLOPS[cfg.dtype]
-    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": _traffic(cfg.name, dom, cfg.dtype),
-                "avg_launch_us": stage_us[dom],
-                "algorithmic": f"{fl_mult}*T*(k+shared)*H*I = {dom_flops} FLOP per launch"}
+    e_used = int((plan.sort.counts > 0).sum().item())
+    dom_bytes, bytes_note = gemm_algorithmic_bytes(cfg, dom, e_used)
+    # the binding resource: MFMA time of the FLOPs at peak, or HBM time of the
+    # bytes the kernel must move at least once (small token counts stream the
+    # weights of every expert used and do little arithmetic on them)
+    if dom_bytes / (PEAK_HBM_GBS * 1e9) > dom_flops / (peak * 1e12):
+        achieved = dom_bytes / (stage_us[dom] * 1e-6) / 1e9
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    else:
+        achieved = dom_flops / (stage_us[dom] * 1e-6) / 1e12
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
+    roofline.update({"traffic": _traffic(cfg.name, dom, cfg.dtype), "avg_launch_us": stage_us[dom],
+                     "algorithmic": f"{fl_mult}*T*(k+shared)*H*I = {dom_flops} FLOP per launch; "
+                                    f"{bytes_note} = {dom_bytes} B per launch"})
 
     rec = {
         "metric": "routed MoE-MLP forward TFLOP/s on 1 MI355X (+% of dtype MFMA peak)",
@@ -363,6 +374,32 @@ def measure(cfg, inp, steps: int, warmup: int, block_m=None, data=None, fused_co
     if cfg.dtype == 2:
         rec["pct_of_fp4_peak"] = round(100 * value / PEAK_FP4_TFLOPS, 2)
     return rec
+
+
+def gemm_algorithmic_bytes(cfg, kernel: str, e_used: int):
+    """Bytes a grouped GEMM of the forward must move at least once per launch:
+    the weights (and block scales) of the e_used experts that received rows,
+    the token operand read once, and its output written once (GEMM1: the
+    intermediate h of the A = T*(k+shared) real rows; GEMM2: h read, Y
+    written in bf16). Pad rows are not counted."""
+    A, H, I = cfg.T * (cfg.k + cfg.n_shared), cfg.H, cfg.I
+    if cfg.dtype == 0:                      # bf16 everywhere
+        val, scale_w, scale_a = 2.0, 0.0, 0.0
+    elif cfg.dtype == 1:                    # E4M3, fp32 per 128x128 (weights) / 1x128 (tokens)
+        val, scale_w, scale_a = 1.0, 4.0 / (128 * 128), 4.0 / 128
+    else:                                   # E2M1 weights / E4M3 tokens, one E8M0 byte per 32
+        val, scale_w, scale_a = 1.0, 1.0 / 32, 1.0 / 32
+    wval = 0.5 if cfg.dtype == 2 else val   # weight element bytes
+    if kernel.startswith("gemm1"):
+        rows = cfg.w1_rows
+        w = e_used * rows * H * (wval + scale_w)
+        x = cfg.T * H * (val + scale_a)
+        h = A * I * (val + scale_a)
+        return int(w + x + h), f"{e_used} experts x W1 ({rows}x{H}) + x (T x H) + h (A x I)"
+    w = e_used * H * I * (wval + scale_w)
+    h = A * I * (val + scale_a)
+    y = A * H * 2
+    return int(w + h + y), f"{e_used} experts x W2 ({H}x{I}) + h (A x I) + Y (A x H, bf16)"
 
 
 # FLOPs per launch of each backward GEMM, in units of T*(k+shared)*H*I

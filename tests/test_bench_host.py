@@ -1,0 +1,72 @@
+"""Host-side logic of bench.py (no GPU): the one-GPU refusal, the algorithmic
+bytes behind the HBM roofline, and the rocprofv3 summary writer."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from workloads import get_config  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "4"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_algorithmic_bytes_bf16():
+    cfg = get_config("qwen3_30b_a3b_bf16")
+    A = cfg.T * cfg.k
+    b1, _ = bench.gemm_algorithmic_bytes(cfg, "gemm1_swiglu", cfg.E)
+    assert b1 == cfg.E * 2 * cfg.I * cfg.H * 2 + cfg.T * cfg.H * 2 + A * cfg.I * 2
+    b2, _ = bench.gemm_algorithmic_bytes(cfg, "gemm2_down", 100)
+    assert b2 == 100 * cfg.H * cfg.I * 2 + A * cfg.I * 2 + A * cfg.H * 2
+
+
+def test_algorithmic_bytes_block_scaled():
+    # MX: half a byte per E2M1 weight, one E8M0 byte per 32 elements on both operands
+    cfg = get_config("mxfp4_moe_t128")
+    A = cfg.T * cfg.k
+    b1, _ = bench.gemm_algorithmic_bytes(cfg, "gemm1_swiglu", 7)
+    w = 7 * 2 * cfg.I * cfg.H * (0.5 + 1 / 32)
+    assert b1 == int(w + cfg.T * cfg.H * (1 + 1 / 32) + A * cfg.I * (1 + 1 / 32))
+    # FP8: one fp32 per 128x128 weight block and per 1x128 token block
+    cfg = get_config("fp8_block128_share")
+    b2, _ = bench.gemm_algorithmic_bytes(cfg, "gemm2_down", cfg.E)
+    A = cfg.T * cfg.k
+    w = cfg.E * cfg.H * cfg.I * (1 + 4 / (128 * 128))
+    assert b2 == int(w + A * cfg.I * (1 + 4 / 128) + A * cfg.H * 2)
+
+
+def test_small_token_counts_are_hbm_bound():
+    # the weights of every expert used dominate at T = 128: HBM time > MFMA time
+    cfg = get_config("mxfp4_moe_t128")
+    flops = 4 * cfg.T * cfg.k * cfg.H * cfg.I
+    b, _ = bench.gemm_algorithmic_bytes(cfg, "gemm1_swiglu", cfg.E)
+    assert b / (bench.PEAK_HBM_GBS * 1e9) > flops / (bench.PEAK_TFLOPS[cfg.dtype] * 1e12)
+    cfg = get_config("qwen3_30b_a3b_bf16")
+    flops = 4 * cfg.T * cfg.k * cfg.H * cfg.I
+    b, _ = bench.gemm_algorithmic_bytes(cfg, "gemm1_swiglu", cfg.E)
+    assert b / (bench.PEAK_HBM_GBS * 1e9) < flops / (bench.PEAK_TFLOPS[cfg.dtype] * 1e12)
+
+
+def test_stats_markdown(tmp_path):
+    csv_path = tmp_path / "kt_kernel_stats.csv"
+    csv_path.write_text('"Name","Calls","TotalDurationNs","AverageNs","Percentage","MinNs","MaxNs"\n'
+                        '"void moe::(anonymous namespace)::gemm_bf16_kernel<256, 128, 4, 2, true, 0, false>'
+                        '(moe::(anonymous namespace)::Params)",7,3500000,500000.0,60.0,480000,520000\n')
+    log = tmp_path / "run.log"
+    log.write_text("noise\n" + json.dumps({"value": 1.0, "unit": "TFLOP/s", "steps": 5, "warmup": 2,
+                                           "stages_us": {"gemm1_swiglu": 499.0}}) + "\n")
+    out = tmp_path / "summary.md"
+    bench.stats_markdown(str(csv_path), "title", "the command", str(out), str(log))
+    text = out.read_text()
+    assert "`gemm_bf16_kernel<256, 128, 4, 2, true, 0, false>` | 7 | 500.0 |" in text
+    assert "| gemm1_swiglu | 499.0 |" in text and "the command" in text
