@@ -61,6 +61,13 @@ class MoeLayer:
     For the FP8 path the weights are quantised here to E4M3 with 128x128 fp32
     block scales, for the MX path to E2M1 with E8M0 per 32 along K (weight
     preparation, outside the timed forward).
+
+    fused_combine=True (BF16) runs GEMM2 with the weighted combine in its
+    epilogue (same result, bit for bit, but slower on MI355X: the device-scope
+    fences between the workgroups of different XCDs flush the L2 weight reuse).
+    plan(T, train=True) prepares the BF16 SwiGLU training step:
+    forward_train() keeps the pre-activations and backward() returns dx,
+    dlogits and the fp32 weight gradients dw1, dw2.
     """
 
     def __init__(self, dtype: int, w1: torch.Tensor, w2: torch.Tensor, k: int, score: int = B.SCORE_SOFTMAX,
