@@ -324,7 +324,7 @@ moe_status_t moe_grouped_gemm_down_combine(int32_t dtype, const void* h, const v
 namespace {
 
 moe_status_t check_bwd(int64_t T, int32_t H, int32_t I, int32_t E, int32_t k, int32_t block_m, int64_t cap) {
-  if (T < 0 || H <= 0 || I <= 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > MOE_MAX_TOPK)
+  if (T < 0 || H <= 0 || I <= 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > E || k > MOE_MAX_TOPK)
     return MOE_ERR_INVALID_ARG;
   if (!valid_block_m(block_m)) return MOE_ERR_INVALID_ARG;
   if (T > (int64_t{1} << 31) / k) return MOE_ERR_INVALID_ARG;

@@ -167,6 +167,8 @@ def test_backward_host_validation():
         assert f(cap=cap + 256) == 1
         assert f(T=0, cap=0) == 0
     assert dh(dy=NULL) == 1 and dh(gu=MIS) == 1 and dx(dgu=MIS) == 1
+    assert L.moe_grouped_gemm_dh(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, T, H, I, 2, 3, 256,
+                                 O.sorted_capacity(T, 3, 2, 256), FAKE, NULL) == 1     # k > E
     assert wg(M=100) == 2 and wg(N=36) == 2 and wg(M=0) == 1
     assert wg(bm=128, cap=O.sorted_capacity(T, k, E, 128)) == 2
     assert wg(p=NULL) == 1 and wg(dw=MIS) == 1
