@@ -39,10 +39,15 @@ GEMM1_STAGE = {0: "gemm1_swiglu", 1: "gemm1_relu2"}     # by activation
 
 
 def _src_hash(fname: str) -> str:
+    """Hash of a kernel source and the common header, comments and blank lines
+    left out (a comment edit does not change what the counters measured)."""
+    import re
     path = os.path.join(ROOT, "mixture_experts_routed_top_amd", "csrc", fname)
     h = hashlib.sha256()
     for f in (path, os.path.join(os.path.dirname(path), "moe_common.cuh")):
-        h.update(open(f, "rb").read())
+        text = re.sub(r"/\*.*?\*/", "", open(f).read(), flags=re.S)
+        lines = [re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines()]
+        h.update("\n".join(ln for ln in lines if ln.strip()).encode())
     return h.hexdigest()[:16]
 
 

@@ -29,9 +29,11 @@
 //     the fragment reads of 8 consecutive rows fall on distinct banks;
 //   * GEMM1 keeps the gate rows n and up rows I + n of the same output column
 //     in one workgroup, so SwiGLU runs in registers in the epilogue;
-//   * what bounds it: the L2 -> LDS stream, limited per CU by the requests in
-//     flight over the L1 -> L2 latency (about 0.12 lines per clock at 66% L2
-//     hits on the Qwen3-30B-A3B shape), not by MFMA issue.
+//   * what bounds it: the operand stream into LDS, held back by the latency of
+//     the third of its requests that miss L2 (66% hits on the Qwen3-30B-A3B
+//     shape; the same loads stream about 4x faster from L2-resident data):
+//     each k-step waits for its whole tile and the pipeline looks one k-step
+//     ahead. Not MFMA issue, and neither HBM nor L2 bandwidth.
 #include "moe_common.cuh"
 #include "moe_launch.h"
 

@@ -70,3 +70,16 @@ def test_stats_markdown(tmp_path):
     text = out.read_text()
     assert "`gemm_bf16_kernel<256, 128, 4, 2, true, 0, false>` | 7 | 500.0 |" in text
     assert "| gemm1_swiglu | 499.0 |" in text and "the command" in text
+
+
+def test_src_hash_ignores_comments(tmp_path, monkeypatch):
+    csrc = tmp_path / "mixture_experts_routed_top_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    (csrc / "moe_common.cuh").write_text("int common;\n")
+    (csrc / "k.hip").write_text("// header\nint a = 1;  // note\n/* block\n comment */\nint b = 2;\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    h0 = bench._src_hash("k.hip")
+    (csrc / "k.hip").write_text("// other header\n\nint a = 1;\nint b = 2;  /* x */\n")
+    assert bench._src_hash("k.hip") == h0
+    (csrc / "k.hip").write_text("int a = 1;\nint b = 3;\n")
+    assert bench._src_hash("k.hip") != h0
