@@ -407,6 +407,20 @@ def gemm_algorithmic_bytes(cfg, kernel: str, e_used: int):
     return int(w + h + y), f"{e_used} experts x W2 ({H}x{I}) + h (A x I) + Y (A x H, bf16)"
 
 
+def bwd_algorithmic_bytes(cfg, kernel: str, e_used: int):
+    """Bytes a backward GEMM must move at least once per launch (bf16 rows of
+    the A = T*(k+shared) real assignments, weights of the experts that
+    received rows, fp32 weight gradients of every expert)."""
+    A, H, I, E = cfg.T * (cfg.k + cfg.n_shared), cfg.H, cfg.I, cfg.E_total
+    if kernel == "gemm_dh":
+        return A * H * 2 + e_used * H * I * 2 + 2 * A * 2 * I * 2, "dY + W2 (experts used) + gu + dGU"
+    if kernel == "gemm_dx":
+        return A * 2 * I * 2 + e_used * 2 * I * H * 2 + A * H * 2, "dGU + W1 (experts used) + dx rows"
+    if kernel == "wgrad_w2":
+        return A * I * 2 + A * H * 2 + E * H * I * 4, "h + dY + dW2 (fp32)"
+    return A * H * 2 + A * 2 * I * 2 + E * 2 * I * H * 4, "x rows + dGU + dW1 (fp32)"
+
+
 # FLOPs per launch of each backward GEMM, in units of T*(k+shared)*H*I
 BWD_GEMM_FLOPS = {"gemm_dh": 2, "gemm_dx": 4, "wgrad_w2": 2, "wgrad_w1": 4}
 
@@ -447,8 +461,17 @@ def measure_backward(cfg, inp, steps: int, warmup: int, data=None) -> dict:
     value = flops / (ms / 1e3) / 1e12
     dom = max(BWD_GEMM_FLOPS, key=lambda n: stage_us[n])
     dom_flops = BWD_GEMM_FLOPS[dom] * unit
-    achieved = dom_flops / (stage_us[dom] * 1e-6) / 1e12
     peak = PEAK_TFLOPS[0]
+    e_used = int((p.sort.counts > 0).sum().item())
+    dom_bytes, bytes_note = bwd_algorithmic_bytes(cfg, dom, e_used)
+    if dom_bytes / (PEAK_HBM_GBS * 1e9) > dom_flops / (peak * 1e12):
+        achieved = dom_bytes / (stage_us[dom] * 1e-6) / 1e9
+        rl = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+              "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    else:
+        achieved = dom_flops / (stage_us[dom] * 1e-6) / 1e12
+        rl = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+              "frac": round(achieved / peak, 4)}
     gemm_tflops = {n: round(BWD_GEMM_FLOPS[n] * unit / (stage_us[n] * 1e-6) / 1e12, 2) for n in BWD_GEMM_FLOPS}
     return {
         "metric": "routed MoE-MLP backward TFLOP/s on 1 MI355X (+% of dtype MFMA peak)",
@@ -460,10 +483,9 @@ def measure_backward(cfg, inp, steps: int, warmup: int, data=None) -> dict:
         "config": _config(cfg, p),
         "pct_of_dtype_peak": round(100 * value / peak, 2),
         "step_ms": step_stats, "stages_us": stage_us, "gemm_tflops": gemm_tflops, "wall_s_timed": round(wall, 4),
-        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
-                     "avg_launch_us": stage_us[dom],
-                     "algorithmic": f"{BWD_GEMM_FLOPS[dom]}*T*(k+shared)*H*I = {dom_flops} FLOP per launch"},
+        "roofline": {"kernel": dom, **rl, "traffic": None, "avg_launch_us": stage_us[dom],
+                     "algorithmic": f"{BWD_GEMM_FLOPS[dom]}*T*(k+shared)*H*I = {dom_flops} FLOP per launch; "
+                                    f"{bytes_note} = {dom_bytes} B per launch"},
     }
 
 

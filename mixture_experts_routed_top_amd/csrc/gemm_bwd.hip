@@ -226,8 +226,12 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_bwd_kernel(Params p) {
         for (int j = 0; j < FN; ++j) {
           const bf16x8 bf = WGRAD ? t_frag(tb, lane, wn * TN + j * 32, kk * 16)
                                   : n_frag(tb, wn * TN + j * 32 + (lane & 31), kk * 2 + (lane >> 5));
+          // the weight gradient takes its N side as the MFMA A operand, so
+          // that each lane holds one M index (contiguous in dW) of 16 N rows
 #pragma unroll
-          for (int i = 0; i < FM; ++i) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf, acc[i][j], 0, 0, 0);
+          for (int i = 0; i < FM; ++i)
+            acc[i][j] = WGRAD ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf, af[i], acc[i][j], 0, 0, 0)
+                              : __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf, acc[i][j], 0, 0, 0);
         }
       }
     };
@@ -245,6 +249,24 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_bwd_kernel(Params p) {
       __syncthreads();
     }
 
+    if constexpr (WGRAD) {
+      // lane holds M index lane % 32 of N indices 8 (v / 4) + 4 (lane / 32) + v % 4:
+      // each store writes 2 x 128 contiguous bytes of dW
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int m = m0 + wm * TM + i * 32 + (lane & 31);
+        if (m >= p.M) continue;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int n = n0 + wn * TN + j * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            if (n < p.N)
+              static_cast<float*>(p.out)[(static_cast<int64_t>(e) * p.N + n) * p.M + m] = acc[i][j][v];
+          }
+      }
+      continue;
+    }
     // epilogue: lane holds M indices 8 (v / 4) + 4 (lane / 32) + v % 4 of N index lane % 32
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
@@ -256,14 +278,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_bwd_kernel(Params p) {
           const int m = m0 + wm * TM + i * 32 + g * 8 + (lane >> 5) * 4;
           if (m >= p.M) continue;
           const float a4[4] = {acc[i][j][g * 4], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2], acc[i][j][g * 4 + 3]};
-          if (MODE == kWgrad) {
-            const int n = n0 + nl;
-            if (n < p.N) {
-              float4 st = make_float4(a4[0], a4[1], a4[2], a4[3]);
-              *reinterpret_cast<float4*>(static_cast<float*>(p.out) +
-                                         (static_cast<int64_t>(e) * p.N + n) * p.M + m) = st;
-            }
-          } else if (MODE == kDh) {
+          if (MODE == kDh) {
             const int64_t r = row0 + nl;
             const uint2 gq = *reinterpret_cast<const uint2*>(p.gu + r * 2 * p.M + m);
             const uint2 uq = *reinterpret_cast<const uint2*>(p.gu + r * 2 * p.M + p.M + m);
