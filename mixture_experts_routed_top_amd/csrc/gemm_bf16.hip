@@ -29,11 +29,11 @@
 //     the fragment reads of 8 consecutive rows fall on distinct banks;
 //   * GEMM1 keeps the gate rows n and up rows I + n of the same output column
 //     in one workgroup, so SwiGLU runs in registers in the epilogue;
-//   * what bounds it: the operand stream into LDS, held back by the latency of
-//     the third of its requests that miss L2 (66% hits on the Qwen3-30B-A3B
-//     shape; the same loads stream about 4x faster from L2-resident data):
-//     each k-step waits for its whole tile and the pipeline looks one k-step
-//     ahead. Not MFMA issue, and neither HBM nor L2 bandwidth.
+//   * what bounds it: on the Qwen3-30B-A3B shape the operand loads alone and
+//     the MFMAs with their LDS fragment reads alone each take most of the
+//     kernel time, and they overlap only partly; no single bandwidth is
+//     saturated (a third of the loads miss L2; HBM runs at half of what a
+//     pure stream reaches), and more lookahead does not help.
 #include "moe_common.cuh"
 #include "moe_launch.h"
 
