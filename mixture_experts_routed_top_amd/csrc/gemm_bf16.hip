@@ -188,7 +188,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
   const int N = GEMM1 ? p.I : p.H;      // output columns
   const int K = GEMM1 ? p.H : p.I;      // reduction length
   const int ntn = (N + BN - 1) / BN;
-  const int total = *p.num_tiles * ntn;
+  const int num_tiles = *p.num_tiles;
+  const int total = num_tiles * ntn;
   const int nk = (K + BK - 1) / BK;
   // this lane's place in a direct-to-LDS load: the load writes 64 x 16 bytes
   // contiguously, i.e. 8 LDS rows; lane l fills physical chunk l % 8 of row l / 8
@@ -204,7 +205,17 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
                      ((xcd + 1) * (G / kXcds) + (xcd + 1 < G % kXcds ? xcd + 1 : G % kXcds)) / G;
 
   for (int64_t task = t0 + local; task < t1; task += per_xcd) {
-    const int mt = static_cast<int>(task / ntn), nt = static_cast<int>(task - static_cast<int64_t>(mt) * ntn);
+    // When the weight slices one m-tile walks through exceed an XCD's 4 MB
+    // L2, tasks walk the n-tiles with two m-tiles side by side (m fastest),
+    // so that the m-tiles of an expert, which read the same weight slice, run
+    // together and share it in L2; otherwise one m-tile's n-tiles come in a
+    // row and the slices are still in L2 when the next m-tile reads them.
+    // (Token tiles are shared along n either way.)
+    const int MC = static_cast<int64_t>(ntn) * C::B_ROWS * K * 2 > (int64_t{4} << 20) ? 2 : 1;
+    const int chunk = static_cast<int>(task / (MC * ntn));
+    const int mcount = num_tiles - chunk * MC < MC ? num_tiles - chunk * MC : MC;
+    const int r = static_cast<int>(task - static_cast<int64_t>(chunk) * MC * ntn);
+    const int nt = r / mcount, mt = chunk * MC + r % mcount;
     const int e = p.tile_expert[mt];
     const int64_t row0 = static_cast<int64_t>(mt) * BM;
     const int n0 = nt * BN;
