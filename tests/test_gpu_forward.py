@@ -52,6 +52,15 @@ def test_bf16_forward_edge_shapes(T, H, E, k, I):
     _full_compare(cfg, make_inputs(cfg, seed=T))
 
 
+def test_bf16_forward_paired_m_tiles():
+    """256-row tiles whose weight slices per m-tile exceed 4 MB (GEMM1: 16
+    n-tiles of 256 rows x 2048; GEMM2: 8 n-tiles of 256 rows x 2048), so the
+    tasks pair m-tiles along n in both GEMMs; 5 experts with one m-tile each
+    leave the last pair with a single m-tile."""
+    cfg = get_config("tiny_bf16").with_(T=700, H=2048, E=5, k=1, I=2048, w_std=0.02)
+    _full_compare(cfg, make_inputs(cfg, seed=21), block_m=256)
+
+
 def test_bf16_forward_one_expert_takes_all():
     cfg = get_config("tiny_bf16").with_(T=300, E=8, k=1)
     inp = make_inputs(cfg, seed=3)
