@@ -82,7 +82,11 @@ struct Cfg {
   static constexpr int STAGE = A_REGION + W_REGION + S_GROUPS * 256;
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile is a multiple of 32");
   static_assert(BM % 8 == 0 && W_REGION % 1024 == 0, "whole 1 KB load groups");
-  static_assert(MODE != kFp8Block || TN <= 128, "a wave's weight rows share one 128x128 scale block");
+  // FP8: a wave's weight rows must lie in one 128-row scale block: tiles start
+  // on multiples of BN, so BN a multiple of 128 (or 128 a multiple of BN) and
+  // TN dividing 128 keep every wave's rows inside one block
+  static_assert(MODE != kFp8Block || (TN <= 128 && 128 % TN == 0 && (BN % 128 == 0 || 128 % BN == 0)),
+                "a wave's weight rows share one 128x128 scale block");
   static_assert(NST == 2 || NST == 4, "double or quadruple buffering");
   static_assert(KSUB == 1 || (KSUB == 2 && MODE == kMx && NST == 2), "two substeps: MX, double buffered");
   static_assert(NST * STAGE + WN * BM * 4 + (NST > 2 ? 1024 : 0) <= 160 * 1024, "the stages fit in LDS");
