@@ -26,7 +26,7 @@
 //     from LDS while the current substep's MFMAs run (order pinned with
 //     scheduling-group barriers);
 //   * LDS rows of BK bf16 with the 16-byte chunk index XOR-swizzled by row, so
-//     the fragment reads of 8 consecutive rows fall on distinct banks;
+//     the fragment reads of 16 consecutive rows fall on distinct banks;
 //   * GEMM1 keeps the gate rows n and up rows I + n of the same output column
 //     in one workgroup, so SwiGLU runs in registers in the epilogue;
 //   * what bounds it: on the Qwen3-30B-A3B shape the operand loads alone and
@@ -65,10 +65,16 @@ struct Cfg {
   static_assert(2 * STAGE <= 160 * 1024, "two stages fit in LDS");
 };
 
-// Byte offset of 16-byte chunk c of LDS row `row`: the XOR swizzle spreads 8
-// consecutive rows reading the same logical chunk over distinct banks.
+// The XOR swizzle of the 16-byte chunks of LDS row `row`. gfx950's LDS has
+// 64 four-byte banks (256 bytes), so the 16 lanes of one 16-byte fragment
+// read, 16 consecutive rows at the same logical chunk, cover two 128-byte rows
+// per bank sweep: rows 2j and 2j + 1 share the swizzle j, which sends the 8
+// even (and the 8 odd) rows to 8 distinct chunks.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+// Byte offset of 16-byte chunk c of LDS row `row`.
 __device__ __forceinline__ uint32_t lds_off(int row, int c) {
-  return static_cast<uint32_t>(row * 128 + ((c ^ (row & 7)) << 4));
+  return static_cast<uint32_t>(row * 128 + ((c ^ swz(row)) << 4));
 }
 
 __device__ __forceinline__ bf16x8 lds_frag(const char* base, int row, int chunk) {
@@ -258,7 +264,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
 #pragma unroll
     for (int q = 0; q < C::GPW; ++q) {
       const int row = (wave * C::GPW + q) * 8 + g_row;
-      const int lc = g_pc ^ (row & 7);                  // logical chunk stored at this place
+      const int lc = g_pc ^ swz(row);                   // logical chunk stored at this place
       kcol[q] = lc * 8;
       const uint32_t base = row_src(row);
       off[q] = base == kOob ? kOob : base + lc * 16;

@@ -68,9 +68,11 @@ __device__ __forceinline__ uint32_t t_off(int k, int c) {
   return static_cast<uint32_t>(k * (BO * 2) + ((c ^ ((k & 3) << 2)) << 4));
 }
 // K-contiguous tile: row r (one output column of the N side), 16-byte chunk c
-// of its BK elements, swizzled by r & 7 as in the forward kernels.
+// of its BK elements, swizzled by (r / 2) % 8 as in the forward kernels: the
+// 16 consecutive rows of one fragment read fill the 64 banks once.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ uint32_t n_off(int r, int c) {
-  return static_cast<uint32_t>(r * (BK * 2) + ((c ^ (r & 7)) << 4));
+  return static_cast<uint32_t>(r * (BK * 2) + ((c ^ swz(r)) << 4));
 }
 
 // Fragment of 8 consecutive K (k0 + 8 (lane / 32) ...) for column m_base +
@@ -179,7 +181,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_bwd_kernel(Params p) {
       } else {
         // K-contiguous rows of the sorted operand: row r = 8 gl + lane / 8
         const int r = 8 * gl + (lane >> 3), pc = lane & 7;
-        const int lc = pc ^ (r & 7);
+        const int lc = pc ^ swz(r);
         krow[q] = lc * 8;
         off[q] = static_cast<uint32_t>((row0 + r) * p.K + lc * 8) * 2;
       }

@@ -34,7 +34,7 @@
 // One k-step stages 128 K elements: a 128-byte token row (E4M3), a 128-byte
 // (E4M3) or 64-byte (E2M1) weight row, and one 32-bit scale word per row
 // (the fp32 1x128 token scale, or four E8M0 bytes). LDS is double buffered;
-// 16-byte chunks are XOR-swizzled per row so that the fragment reads of 8
+// 16-byte chunks are XOR-swizzled per row so that the fragment reads of 16
 // consecutive rows fall on distinct banks. The 32-row MX GEMM1 tile (small
 // token counts, bound by the weight stream) stages two such k-steps at once:
 // a 64-byte E2M1 slice is half an L2 line, and the number of requests a CU
@@ -93,14 +93,22 @@ struct Cfg {
   static_assert((NST - 2) * (GPW + SPW) < 64, "outstanding loads fit the counter");
 };
 
+// XOR swizzles of the 16-byte chunks of an LDS row. gfx950's LDS has 64
+// four-byte banks (256 bytes), and a 16-byte fragment read serves 16 lanes,
+// 16 consecutive rows at one logical chunk, per bank sweep. 128-byte rows:
+// rows 2j and 2j + 1 share the swizzle j (the even and the odd rows each
+// reach 8 distinct chunks); 64-byte rows: rows 4j .. 4j + 3 share j.
+__device__ __forceinline__ int swz128(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int swz64(int row) { return (row >> 2) & 3; }
+
 __device__ __forceinline__ uint32_t a_off(int row, int c) {
-  return static_cast<uint32_t>(row * 128 + ((c ^ (row & 7)) << 4));
+  return static_cast<uint32_t>(row * 128 + ((c ^ swz128(row)) << 4));
 }
 
 template <int W_BYTES>
 __device__ __forceinline__ uint32_t w_off(int row, int c) {
-  if (W_BYTES == 128) return static_cast<uint32_t>(row * 128 + ((c ^ (row & 7)) << 4));
-  return static_cast<uint32_t>(row * 64 + ((c ^ ((row >> 2) & 3)) << 4));
+  if (W_BYTES == 128) return static_cast<uint32_t>(row * 128 + ((c ^ swz128(row)) << 4));
+  return static_cast<uint32_t>(row * 64 + ((c ^ swz64(row)) << 4));
 }
 
 __device__ __forceinline__ i32x8 frag32(const char* p0, const char* p1) {
@@ -268,11 +276,11 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_scaled_kernel(Params p
       if (g < C::A_GROUPS) {
         const int row = (g % C::A_GROUPS_SUB) * 8 + (lane >> 3), pc = lane & 7;
         const int64_t src = token_row(row);
-        if (src >= 0) doff[q] = static_cast<uint32_t>(src * K + ((pc ^ (row & 7)) << 4));
+        if (src >= 0) doff[q] = static_cast<uint32_t>(src * K + ((pc ^ swz128(row)) << 4));
       } else if (g < C::GROUPS) {
         const int byte = (g - C::A_GROUPS) * 1024 + lane * 16;
         const int br = byte / WB, pc = (byte % WB) / 16;
-        const int lc = WB == 128 ? (pc ^ (br & 7)) : (pc ^ ((br >> 2) & 3));
+        const int lc = WB == 128 ? (pc ^ swz128(br)) : (pc ^ swz64(br));
         const int wr = weight_row(br);
         if (wr >= 0) doff[q] = static_cast<uint32_t>(wr) * wrow_bytes + (lc << 4);
         dsub[q] = static_cast<uint32_t>(lc * 16 / 64) % C::KSUB;
