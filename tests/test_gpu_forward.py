@@ -52,13 +52,52 @@ def test_bf16_forward_edge_shapes(T, H, E, k, I):
     _full_compare(cfg, make_inputs(cfg, seed=T))
 
 
-def test_bf16_forward_paired_m_tiles():
+def test_bf16_forward_grouped_m_tiles():
     """256-row tiles whose weight slices per m-tile exceed 4 MB (GEMM1: 16
     n-tiles of 256 rows x 2048; GEMM2: 8 n-tiles of 256 rows x 2048), so the
-    tasks pair m-tiles along n in both GEMMs; 5 experts with one m-tile each
-    leave the last pair with a single m-tile."""
+    tasks walk the n-tiles with each expert's m-tiles side by side in both
+    GEMMs; 5 experts with one m-tile each make groups of one."""
     cfg = get_config("tiny_bf16").with_(T=700, H=2048, E=5, k=1, I=2048, w_std=0.02)
     _full_compare(cfg, make_inputs(cfg, seed=21), block_m=256)
+
+
+def test_bf16_forward_expert_groups_long_runs():
+    """Weight slices per m-tile above 4 MB in both GEMMs (GEMM1: 16 n-tiles of
+    256 rows x 1536; GEMM2: 6 n-tiles of 256 rows x 2048), so each expert's
+    m-tiles walk the n-tiles in groups of up to four; one expert holds 37
+    m-tiles (runs of more than 32 tiles on both sides of most of its tiles,
+    and a last group of one), the others 3 and 2. Routing and layout are
+    compared in full, Y on rows from every m-tile."""
+    cfg = get_config("tiny_bf16").with_(T=10300, H=1536, E=3, k=1, I=2048, w_std=0.02)
+    inp = make_inputs(cfg, seed=5)
+    inp.logits[:] = -1.0
+    inp.logits[:9300, 0] = 2.0
+    inp.logits[9300:10000, 1] = 2.0
+    inp.logits[10000:, 2] = 2.0
+    say("forward expert groups", cfg.T, cfg.H, cfg.E, cfg.I)
+    layer, plan, out = _run(cfg, inp, block_m=256)
+    rid, rw = O.route_with_shared(inp.logits.numpy(), cfg.k, cfg.score, 0)
+    np.testing.assert_array_equal(plan.ids.cpu().numpy(), rid)
+    counts, offsets, sorted_ids, tile_expert, num_tiles = O.align_sort(rid, cfg.E, 256)
+    assert list(np.bincount(tile_expert[:num_tiles], minlength=3)) == [37, 3, 2]
+    np.testing.assert_array_equal(plan.sort.sorted_ids.cpu().numpy()[:len(sorted_ids)], sorted_ids)
+    np.testing.assert_array_equal(plan.sort.tile_expert.cpu().numpy()[:len(tile_expert)], tile_expert)
+    rng = np.random.default_rng(1)
+    assigned, refs = [], []
+    for e in range(cfg.E):
+        seg = sorted_ids[offsets[e]:offsets[e] + counts[e]]
+        # the first and last row of every 256-row tile, and one more in each
+        pick = np.unique(np.concatenate([seg[0::256], seg[255::256], [seg[-1]],
+                                         seg[np.minimum(np.arange(0, len(seg), 256) + 97, len(seg) - 1)]]))
+        w1e, w2e = to_f64(inp.w1[e]), to_f64(inp.w2[e])
+        xr = to_f64(inp.x[torch.from_numpy(pick)])
+        refs += [O.assignment_forward(xr[i], w1e, w2e, cfg.dtype, cfg.act) for i in range(len(pick))]
+        assigned += list(pick)
+    got = f64(plan.y[torch.from_numpy(np.array(assigned)).to(out.device)])
+    ref = np.stack(refs)
+    assert rel_fro(got, ref) <= TOL_FRO[cfg.dtype]
+    assert min_row_cos(got, ref) >= TOL_COS
+    assert torch.isfinite(out.float()).all()
 
 
 def test_bf16_forward_one_expert_takes_all():
