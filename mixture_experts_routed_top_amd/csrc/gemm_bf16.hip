@@ -213,54 +213,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
 
   for (int64_t task = t0 + local; task < t1; task += per_xcd) {
     // When the weight slices one m-tile walks through exceed an XCD's 4 MB
-    // L2, tasks walk the n-tiles with the m-tiles of one expert side by side
-    // (groups of up to kGroup m-tiles, m fastest), so that the m-tiles that
-    // read the same weight slice run together and share it in L2; otherwise
-    // one m-tile's n-tiles come in a row and the slices are still in L2 when
-    // the next m-tile reads them. (Token tiles are shared along n either way.)
-    // A group of c m-tiles owns the c * ntn tasks from its first tile times
-    // ntn, so the tile q = task / ntn lies in the task's group.
+    // L2, the m-tiles of one expert walk the n-tiles side by side (groups of
+    // up to kGroup, m fastest), so that the m-tiles that read the same weight
+    // slice run together and share it in L2; otherwise one m-tile's n-tiles
+    // come in a row and the slices are still in L2 when the next m-tile reads
+    // them. (Token tiles are shared along n either way.)
     int nt, mt, e;
     if (static_cast<int64_t>(ntn) * C::B_ROWS * K * 2 > (int64_t{4} << 20)) {
-      const int q = static_cast<int>(task / ntn);
-      // expert e of tile q and its tiles [f, l) around q (tiles are in expert
-      // order): one load, lane 0 at q, lanes 1..31 behind it, lanes 32..63
-      // after it; runs longer than that continue 64 tiles at a time
-      int f, l;
-      {
-        const int i = lane < 32 ? q - lane : q + lane - 31;
-        const int v = p.tile_expert[i < 0 ? 0 : (i < num_tiles ? i : q)];
-        e = __builtin_amdgcn_readfirstlane(v);
-        const uint64_t m = __ballot(i >= 0 && i < num_tiles && v == e);
-        const uint32_t mb = static_cast<uint32_t>(m), ma = static_cast<uint32_t>(m >> 32);
-        const int rb = ~mb == 0 ? 32 : __builtin_ctz(~mb);      // tiles q, q-1, .. of expert e
-        const int ra = ~ma == 0 ? 32 : __builtin_ctz(~ma);      // tiles q+1, q+2, .. of expert e
-        f = q + 1 - rb;
-        l = q + 1 + ra;
-        if (rb == 32) {
-          for (;;) {
-            const int j = f - 1 - lane;
-            const uint64_t mm = __ballot(j >= 0 && p.tile_expert[j >= 0 ? j : 0] == e);
-            const int run = ~mm == 0 ? 64 : __builtin_ctzll(~mm);
-            f -= run;
-            if (run < 64) break;
-          }
-        }
-        if (ra == 32) {
-          for (;;) {
-            const int j = l + lane;
-            const uint64_t mm = __ballot(j < num_tiles && p.tile_expert[j < num_tiles ? j : 0] == e);
-            const int run = ~mm == 0 ? 64 : __builtin_ctzll(~mm);
-            l += run;
-            if (run < 64) break;
-          }
-        }
-      }
-      const int gs = f + (q - f) / kGroup * kGroup;
-      const int gc = l - gs < kGroup ? l - gs : kGroup;
-      const int r = static_cast<int>(task - static_cast<int64_t>(gs) * ntn);
-      nt = r / gc;
-      mt = gs + r % gc;
+      grouped_task<kGroup>(task, ntn, num_tiles, p.tile_expert, lane, nt, mt, e);
     } else {
       mt = static_cast<int>(task / ntn);
       nt = static_cast<int>(task - static_cast<int64_t>(mt) * ntn);

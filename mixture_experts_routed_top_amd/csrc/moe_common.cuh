@@ -125,5 +125,54 @@ __device__ __forceinline__ void wait_vmcnt() {
 // every outstanding load would also wait for the later pipeline stages.
 __device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
 
+// ------------------------------------------------------------------ grouped task order
+// Task order of the grouped GEMMs over the expert-sorted m-tiles when one
+// m-tile's walk over the n-tiles reads more weight bytes than an XCD's L2
+// holds: the m-tiles of one expert (groups of up to GROUP, from the expert's
+// first tile) go side by side along n, m fastest, so the tasks that read the
+// same weight slice run together and share it in L2. A group of c m-tiles
+// owns the c * ntn tasks from its first tile times ntn, so tile task / ntn
+// lies in the task's group; one 64-lane load around that tile (lane 0 at it,
+// lanes 1..31 behind, lanes 32..63 after) finds the expert's first and last
+// tile, and longer runs continue 64 tiles at a time. Tiles are in expert
+// order (tile_expert is non-decreasing over [0, num_tiles)). Called by whole
+// waves with wave-uniform arguments; returns the task's n-tile, m-tile and
+// expert.
+template <int GROUP>
+__device__ __forceinline__ void grouped_task(int64_t task, int ntn, int num_tiles, const int32_t* tile_expert,
+                                             int lane, int& nt, int& mt, int& e) {
+  const int q = static_cast<int>(task / ntn);
+  const int i = lane < 32 ? q - lane : q + lane - 31;
+  const int v = tile_expert[i < 0 ? 0 : (i < num_tiles ? i : q)];
+  e = __builtin_amdgcn_readfirstlane(v);
+  const uint64_t m = __ballot(i >= 0 && i < num_tiles && v == e);
+  const uint32_t mb = static_cast<uint32_t>(m), ma = static_cast<uint32_t>(m >> 32);
+  const int rb = ~mb == 0 ? 32 : __builtin_ctz(~mb);      // tiles q, q-1, .. of expert e
+  const int ra = ~ma == 0 ? 32 : __builtin_ctz(~ma);      // tiles q+1, q+2, .. of expert e
+  int f = q + 1 - rb, l = q + 1 + ra;
+  if (rb == 32) {
+    for (;;) {
+      const int j = f - 1 - lane;
+      const uint64_t mm = __ballot(j >= 0 && tile_expert[j >= 0 ? j : 0] == e);
+      const int run = ~mm == 0 ? 64 : __builtin_ctzll(~mm);
+      f -= run;
+      if (run < 64) break;
+    }
+  }
+  if (ra == 32) {
+    for (;;) {
+      const int j = l + lane;
+      const uint64_t mm = __ballot(j < num_tiles && tile_expert[j < num_tiles ? j : 0] == e);
+      const int run = ~mm == 0 ? 64 : __builtin_ctzll(~mm);
+      l += run;
+      if (run < 64) break;
+    }
+  }
+  const int gs = f + (q - f) / GROUP * GROUP;
+  const int gc = l - gs < GROUP ? l - gs : GROUP;
+  const int r = static_cast<int>(task - static_cast<int64_t>(gs) * ntn);
+  nt = r / gc;
+  mt = gs + r % gc;
+}
 
 }  // namespace moe
