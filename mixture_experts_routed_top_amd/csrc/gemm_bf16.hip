@@ -26,7 +26,7 @@
 //     from LDS while the current substep's MFMAs run (order pinned with
 //     scheduling-group barriers);
 //   * LDS rows of BK bf16 with the 16-byte chunk index XOR-swizzled by row, so
-//     the fragment reads of 16 consecutive rows fall on distinct banks;
+//     the fragment reads of 8 consecutive rows fall on distinct chunks;
 //   * GEMM1 keeps the gate rows n and up rows I + n of the same output column
 //     in one workgroup, so SwiGLU runs in registers in the epilogue;
 //   * what bounds it: on the Qwen3-30B-A3B shape the operand loads alone and
@@ -66,12 +66,14 @@ struct Cfg {
   static_assert(2 * STAGE <= 160 * 1024, "two stages fit in LDS");
 };
 
-// The XOR swizzle of the 16-byte chunks of LDS row `row`. gfx950's LDS has
-// 64 four-byte banks (256 bytes), so the 16 lanes of one 16-byte fragment
-// read, 16 consecutive rows at the same logical chunk, cover two 128-byte rows
-// per bank sweep: rows 2j and 2j + 1 share the swizzle j, which sends the 8
-// even (and the 8 odd) rows to 8 distinct chunks.
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+// The XOR swizzle of the 16-byte chunks of LDS row `row`: row & 7, which
+// spreads 8 consecutive rows over distinct chunks. gfx950's LDS has 64
+// four-byte banks and a 16-byte read serves 16 lanes (16 rows) per sweep, so
+// rows r and r + 8 still meet (two-way conflicts, half of the LDS-active
+// cycles); the conflict-free (row >> 1) & 7 measured 1-2% slower on these
+// kernels (same-process medians, Qwen3-30B-A3B and Nemotron shapes) and is
+// used by the FP8 / MX and backward kernels, where it is neutral.
+__device__ __forceinline__ int swz(int row) { return row & 7; }
 
 // Byte offset of 16-byte chunk c of LDS row `row`.
 __device__ __forceinline__ uint32_t lds_off(int row, int c) {
@@ -211,16 +213,19 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
   const int64_t t1 = static_cast<int64_t>(total) *
                      ((xcd + 1) * (G / kXcds) + (xcd + 1 < G % kXcds ? xcd + 1 : G % kXcds)) / G;
 
+  // When the weight slices one m-tile walks through exceed an XCD's 4 MB L2,
+  // the m-tiles of one expert walk the n-tiles side by side (groups of up to
+  // kGroup, m fastest), so that the m-tiles that read the same weight slice
+  // run together and share it in L2; otherwise one m-tile's n-tiles come in
+  // a row and the slices are still in L2 when the next m-tile reads them.
+  // (Token tiles are shared along n either way.)
+  const bool grouped = static_cast<int64_t>(ntn) * C::B_ROWS * K * 2 > (int64_t{4} << 20);
+  int probe = grouped && t0 + local < t1 ? grouped_probe(t0 + local, ntn, num_tiles, p.tile_expert, lane) : 0;
   for (int64_t task = t0 + local; task < t1; task += per_xcd) {
-    // When the weight slices one m-tile walks through exceed an XCD's 4 MB
-    // L2, the m-tiles of one expert walk the n-tiles side by side (groups of
-    // up to kGroup, m fastest), so that the m-tiles that read the same weight
-    // slice run together and share it in L2; otherwise one m-tile's n-tiles
-    // come in a row and the slices are still in L2 when the next m-tile reads
-    // them. (Token tiles are shared along n either way.)
     int nt, mt, e;
-    if (static_cast<int64_t>(ntn) * C::B_ROWS * K * 2 > (int64_t{4} << 20)) {
-      grouped_task<kGroup>(task, ntn, num_tiles, p.tile_expert, lane, nt, mt, e);
+    if (grouped) {
+      grouped_task<kGroup>(task, ntn, num_tiles, p.tile_expert, lane, probe, nt, mt, e);
+      if (task + per_xcd < t1) probe = grouped_probe(task + per_xcd, ntn, num_tiles, p.tile_expert, lane);
     } else {
       mt = static_cast<int>(task / ntn);
       nt = static_cast<int>(task - static_cast<int64_t>(mt) * ntn);

@@ -235,16 +235,19 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_scaled_kernel(Params p
   const __amdgpu_buffer_rsrc_t a_rsrc = make_rsrc(p.a, p.a_rows * static_cast<uint32_t>(K));
   const __amdgpu_buffer_rsrc_t as_rsrc = make_rsrc(p.a_scale, p.a_rows * static_cast<uint32_t>(srow_bytes));
 
+  // the m-tiles of one expert walk the n-tiles side by side when one
+  // m-tile's walk reads more weight bytes than an XCD's 4 MB L2 holds and
+  // a task stages at least as many weight rows as token rows (FP8 GEMM1:
+  // 2463 -> 2265 us on the 64-expert H 7168 shape; its GEMM2, 256 token
+  // rows against 128 weight rows, got 6% slower: there the m-tile walk,
+  // whose 32 concurrent tasks on an XCD share one token tile, wins)
+  const bool grouped = C::B_ROWS >= BM && static_cast<int64_t>(ntn) * C::B_ROWS * wrow_bytes > (int64_t{4} << 20);
+  int probe = grouped && t0 + local < t1 ? grouped_probe(t0 + local, ntn, num_tiles, p.tile_expert, lane) : 0;
   for (int64_t task = t0 + local; task < t1; task += per_xcd) {
-    // the m-tiles of one expert walk the n-tiles side by side when one
-    // m-tile's walk reads more weight bytes than an XCD's 4 MB L2 holds and
-    // a task stages at least as many weight rows as token rows (FP8 GEMM1:
-    // 2463 -> 2265 us on the 64-expert H 7168 shape; its GEMM2, 256 token
-    // rows against 128 weight rows, got 6% slower: there the m-tile walk,
-    // whose 32 concurrent tasks on an XCD share one token tile, wins)
     int nt, mt, e;
-    if (C::B_ROWS >= BM && static_cast<int64_t>(ntn) * C::B_ROWS * wrow_bytes > (int64_t{4} << 20)) {
-      grouped_task<kGroup>(task, ntn, num_tiles, p.tile_expert, lane, nt, mt, e);
+    if (grouped) {
+      grouped_task<kGroup>(task, ntn, num_tiles, p.tile_expert, lane, probe, nt, mt, e);
+      if (task + per_xcd < t1) probe = grouped_probe(task + per_xcd, ntn, num_tiles, p.tile_expert, lane);
     } else {
       mt = static_cast<int>(task / ntn);
       nt = static_cast<int>(task - static_cast<int64_t>(mt) * ntn);

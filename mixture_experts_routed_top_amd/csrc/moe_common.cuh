@@ -137,13 +137,21 @@ __device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::
 // tile, and longer runs continue 64 tiles at a time. Tiles are in expert
 // order (tile_expert is non-decreasing over [0, num_tiles)). Called by whole
 // waves with wave-uniform arguments; returns the task's n-tile, m-tile and
-// expert.
-template <int GROUP>
-__device__ __forceinline__ void grouped_task(int64_t task, int ntn, int num_tiles, const int32_t* tile_expert,
-                                             int lane, int& nt, int& mt, int& e) {
+// expert. The 64-lane load is grouped_probe, issued ahead (a task loads the
+// next task's probe, so that its latency hides behind the k-loop) and passed
+// in as v.
+__device__ __forceinline__ int grouped_probe(int64_t task, int ntn, int num_tiles, const int32_t* tile_expert,
+                                             int lane) {
   const int q = static_cast<int>(task / ntn);
   const int i = lane < 32 ? q - lane : q + lane - 31;
-  const int v = tile_expert[i < 0 ? 0 : (i < num_tiles ? i : q)];
+  return tile_expert[i < 0 ? 0 : (i < num_tiles ? i : q)];
+}
+
+template <int GROUP>
+__device__ __forceinline__ void grouped_task(int64_t task, int ntn, int num_tiles, const int32_t* tile_expert,
+                                             int lane, int v, int& nt, int& mt, int& e) {
+  const int q = static_cast<int>(task / ntn);
+  const int i = lane < 32 ? q - lane : q + lane - 31;
   e = __builtin_amdgcn_readfirstlane(v);
   const uint64_t m = __ballot(i >= 0 && i < num_tiles && v == e);
   const uint32_t mb = static_cast<uint32_t>(m), ma = static_cast<uint32_t>(m >> 32);
