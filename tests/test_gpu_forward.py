@@ -53,18 +53,18 @@ def test_bf16_forward_edge_shapes(T, H, E, k, I):
 
 
 def test_bf16_forward_grouped_m_tiles():
-    """256-row tiles whose weight slices per m-tile exceed 4 MB (GEMM1: 16
-    n-tiles of 256 rows x 2048; GEMM2: 8 n-tiles of 256 rows x 2048), so the
-    tasks walk the n-tiles with each expert's m-tiles side by side in both
-    GEMMs; 5 experts with one m-tile each make groups of one."""
+    """256-row tiles (GEMM1: 16 n-tiles of 256 rows x 2048; GEMM2: 8 n-tiles
+    of 256 rows x 2048); the tasks walk the n-tiles with each expert's m-tiles
+    side by side in both GEMMs, and 5 experts with one m-tile each make groups
+    of one."""
     cfg = get_config("tiny_bf16").with_(T=700, H=2048, E=5, k=1, I=2048, w_std=0.02)
     _full_compare(cfg, make_inputs(cfg, seed=21), block_m=256)
 
 
 def test_bf16_forward_expert_groups_long_runs():
-    """Weight slices per m-tile above 4 MB in both GEMMs (GEMM1: 16 n-tiles of
-    256 rows x 1536; GEMM2: 6 n-tiles of 256 rows x 2048), so each expert's
-    m-tiles walk the n-tiles in groups of up to four; one expert holds 37
+    """Each expert's m-tiles walk the n-tiles in groups of up to four (GEMM1:
+    16 n-tiles of 256 rows x 1536; GEMM2: 6 n-tiles of 256 rows x 2048, above
+    the 4 MB walk the FP8 / MX kernels group from too); one expert holds 37
     m-tiles (runs of more than 32 tiles on both sides of most of its tiles,
     and a last group of one), the others 3 and 2. Routing and layout are
     compared in full, Y on rows from every m-tile."""
