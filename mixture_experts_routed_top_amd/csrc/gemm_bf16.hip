@@ -9,7 +9,8 @@
 //     from device memory, so the host never waits for the router. The list is
 //     cut into one contiguous slice per XCD (workgroup b runs on XCD b % 8), so
 //     the workgroups that run together on one XCD work on neighbouring tasks of
-//     the same expert and share its weight slices in that XCD's L2;
+//     the same expert and share its weight slices in that XCD's L2; within the
+//     list an expert's m-tiles go side by side along n (grouped_task);
 //   * MFMA v_mfma_f32_32x32x16_bf16 with the weight rows as the MFMA "A"
 //     operand and the token rows as "B" (output transposed in registers: each
 //     lane ends up with four consecutive output columns of one token, which

@@ -126,11 +126,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
 
 // ------------------------------------------------------------------ grouped task order
-// Task order of the grouped GEMMs over the expert-sorted m-tiles when one
-// m-tile's walk over the n-tiles reads more weight bytes than an XCD's L2
-// holds: the m-tiles of one expert (groups of up to GROUP, from the expert's
-// first tile) go side by side along n, m fastest, so the tasks that read the
-// same weight slice run together and share it in L2. A group of c m-tiles
+// Task order of the grouped GEMMs over the expert-sorted m-tiles (the BF16
+// kernels always, the FP8 / MX kernels when one m-tile's walk over the
+// n-tiles reads more weight bytes than an XCD's L2 holds): the m-tiles of one
+// expert (groups of up to GROUP, from the expert's first tile) go side by
+// side along n, m fastest, so the tasks that read the same weight slice run
+// together and share it in L2. A group of c m-tiles
 // owns the c * ntn tasks from its first tile times ntn, so tile task / ntn
 // lies in the task's group; one 64-lane load around that tile (lane 0 at it,
 // lanes 1..31 behind, lanes 32..63 after) finds the expert's first and last
