@@ -21,8 +21,14 @@
 //     narrower for 64- and 32-row tiles); each wave holds 128 accumulator
 //     registers, the most the register file leaves room for;
 //   * operands reach LDS by direct-to-LDS buffer loads (16 bytes a lane, 1 KB
-//     a wave instruction); two LDS stages: the loads of k-step s+1 are issued
-//     before the MFMAs of k-step s, and one barrier ends each step;
+//     a wave instruction). The 256-row tiles split each k-step's LDS stage:
+//     token rows in one of two buffers, weight rows in one of three (exactly
+//     the 160 KB of LDS), so the weight rows, most of the L2 misses, stream
+//     two k-steps ahead; every wave issues the same number of each kind of
+//     load, and one exact wait count per step lets the newest weight loads
+//     stay in flight across the barrier. The other tiles keep two whole
+//     stages: the loads of k-step s+1 are issued before the MFMAs of k-step
+//     s, and one barrier ends each step;
 //   * inside a k-step the MFMA fragments of the next 16-K substep are read
 //     from LDS while the current substep's MFMAs run (order pinned with
 //     scheduling-group barriers);
@@ -34,7 +40,8 @@
 //     the MFMAs with their LDS fragment reads alone each take most of the
 //     kernel time, and they overlap only partly; no single bandwidth is
 //     saturated (a third of the loads miss L2; HBM runs at half of what a
-//     pure stream reaches), and more lookahead does not help.
+//     pure stream reaches); the loads are bound by how far ahead they are
+//     issued (a step waits on its slowest requests).
 #include "moe_common.cuh"
 #include "moe_launch.h"
 
@@ -62,6 +69,16 @@ struct Cfg {
   static constexpr int GROUPS = ROWS / 8;             // 8 rows = one 1 KB direct-to-LDS load
   static constexpr int GPW = (GROUPS + WAVES - 1) / WAVES;   // loads per wave per k-step
   static constexpr int STAGE = ROWS * 128;
+  // Split pipeline, where it fits: the token rows of a k-step in one of two
+  // LDS buffers and its weight rows in one of three, so the weight rows
+  // (most of the L2 misses) stream two k-steps ahead and the token rows one.
+  // Every wave issues the same number of token and of weight loads per step,
+  // which makes one wait count exact for all of them.
+  static constexpr int T_BYTES = BM * 128, W_BYTES = B_ROWS * 128;
+  static constexpr int T_GROUPS = BM / 8, W_GROUPS = B_ROWS / 8;
+  static constexpr bool SPLIT = 2 * T_BYTES + 3 * W_BYTES <= 160 * 1024 && T_GROUPS % WAVES == 0 &&
+                                W_GROUPS % WAVES == 0;
+  static constexpr int GPW_T = SPLIT ? T_GROUPS / WAVES : 0;   // token loads per wave per k-step
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile is a multiple of 32");
   static_assert(BM % 8 == 0, "token rows fill whole 8-row groups");
   static_assert(2 * STAGE <= 160 * 1024, "two stages fit in LDS");
@@ -186,10 +203,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
   using C = Cfg<BM, BN, WM, WN, GEMM1, ACT>;
   static_assert(!FUSE || !GEMM1, "the combine fuses into GEMM2");
   constexpr int BK = C::BK;
-  // two separate LDS arrays, so the compiler can tell the stage being filled
-  // by the direct-to-LDS loads from the stage being read
-  __shared__ __attribute__((aligned(1024))) char stage0[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) char stage1[C::STAGE];
+  // separate LDS arrays, so the compiler can tell the stage being filled by
+  // the direct-to-LDS loads from the stage being read: two whole stages, or
+  // (split pipeline) two token buffers and three weight buffers
+  __shared__ __attribute__((aligned(1024))) char stage0[C::SPLIT ? C::T_BYTES : C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage1[C::SPLIT ? C::T_BYTES : C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char wst0[C::SPLIT ? C::W_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char wst1[C::SPLIT ? C::W_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char wst2[C::SPLIT ? C::W_BYTES : 16];
 
   // the wave index is uniform across the wave: keep it in a scalar register so
   // that the LDS destinations and descriptors of the loads are scalar too
@@ -238,12 +259,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
     // byte offset of the start of LDS row `row`'s source row: a token row
     // (gathered by sorted id in GEMM1) or a weight row of expert e; kOob for
     // pad rows, rows past N and rows past the tile
-    auto row_src = [&](int row) -> uint32_t {
+    // (`sid`: the sorted id of a GEMM1 token row, loaded beforehand)
+    auto row_src = [&](int row, int sid) -> uint32_t {
       if (row >= C::ROWS) return kOob;
       if (row < BM) {
         int64_t src_row = -1;
         if (GEMM1) {
-          const int sid = p.sorted_ids[row0 + row];
           if (sid < p.A) src_row = sid / p.k;
         } else {
           src_row = row0 + row;
@@ -264,12 +285,29 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
     };
     uint32_t off[C::GPW];
     int kcol[C::GPW];                                   // first K column of this lane's chunk
+    // load q of this wave fills the 8 LDS rows of group grp_of(q): in the
+    // split pipeline the first GPW_T are token groups, the rest weight groups
+    // (numbered from the first weight row)
+    auto grp_of = [&](int q) -> int {
+      if (!C::SPLIT) return wave * C::GPW + q;
+      return q < C::GPW_T ? wave * C::GPW_T + q : wave * (C::GPW - C::GPW_T) + (q - C::GPW_T);
+    };
+    auto row_of = [&](int q) -> int { return grp_of(q) * 8 + g_row + (C::SPLIT && q >= C::GPW_T ? BM : 0); };
+    // GEMM1 gathers its token rows by sorted id: every id this lane needs is
+    // loaded before any is used, so the loads overlap instead of each one
+    // waiting for the last (a weight row loads a harmless id too)
+    int sid[C::GPW];
 #pragma unroll
     for (int q = 0; q < C::GPW; ++q) {
-      const int row = (wave * C::GPW + q) * 8 + g_row;
+      const int row = row_of(q);
+      sid[q] = GEMM1 ? p.sorted_ids[row0 + (row < BM ? row : 0)] : 0;
+    }
+#pragma unroll
+    for (int q = 0; q < C::GPW; ++q) {
+      const int row = row_of(q);
       const int lc = g_pc ^ swz(row);                   // logical chunk stored at this place
       kcol[q] = lc * 8;
-      const uint32_t base = row_src(row);
+      const uint32_t base = row_src(row, sid[q]);
       off[q] = base == kOob ? kOob : base + lc * 16;
     }
     // issue the direct-to-LDS loads of k-step kt into `stage`
@@ -286,6 +324,23 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
                                                    soff, 0, 0);
       }
     };
+    // split pipeline: the token loads of k-step kt into `tb`, the weight loads into `wb`
+    auto load_t = [&](char* tb, int kt) {
+      const uint32_t soff = static_cast<uint32_t>(kt) * BK * 2;
+#pragma unroll
+      for (int q = 0; q < C::GPW_T; ++q) {
+        const uint32_t o = kt * BK + kcol[q] < K ? off[q] : kOob;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr_t)(tb + grp_of(q) * 1024), 16, o, soff, 0, 0);
+      }
+    };
+    auto load_w = [&](char* wb, int kt) {
+      const uint32_t soff = static_cast<uint32_t>(kt) * BK * 2;
+#pragma unroll
+      for (int q = C::GPW_T; q < C::GPW; ++q) {
+        const uint32_t o = kt * BK + kcol[q] < K ? off[q] : kOob;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lds_ptr_t)(wb + grp_of(q) * 1024), 16, o, soff, 0, 0);
+      }
+    };
 
     f32x16 acc[C::HALVES][C::FM][C::FN];
 #pragma unroll
@@ -298,17 +353,18 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
     // the fragments of 16-K substep kk + 1 are read from LDS into the other
     // register set while the MFMAs of substep kk run, so the LDS latency
     // hides behind MFMA work instead of stalling the matrix pipe
-    auto compute = [&](const char* base) {
+    // `tbase`: the k-step's token rows; `wbase`: its weight rows
+    auto compute = [&](const char* tbase, const char* wbase) {
       bf16x8 xf[2][C::FM], wf[2][C::HALVES][C::FN];
       auto read_frags = [&](int kk, int buf) {
         const int ch = kk * 2 + (lane >> 5);
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i) xf[buf][i] = lds_frag(base, wm * C::TM + i * 32 + (lane & 31), ch);
+        for (int i = 0; i < C::FM; ++i) xf[buf][i] = lds_frag(tbase, wm * C::TM + i * 32 + (lane & 31), ch);
 #pragma unroll
         for (int h = 0; h < C::HALVES; ++h)
 #pragma unroll
           for (int j = 0; j < C::FN; ++j)
-            wf[buf][h][j] = lds_frag(base, BM + h * BN + wn * C::TN + j * 32 + (lane & 31), ch);
+            wf[buf][h][j] = lds_frag(wbase, h * BN + wn * C::TN + j * 32 + (lane & 31), ch);
       };
       read_frags(0, 0);
 #pragma unroll
@@ -347,17 +403,56 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
     // k-step s+1 streams into one stage while the MFMAs consume k-step s from
     // the other; the loads are issued first (the scheduling barrier keeps them
     // there) and must have landed at the barrier that ends the step
-    load(stage0, 0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; kt += 2) {
-      load(stage1, kt + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(stage0);
+    if constexpr (C::SPLIT) {
+      // k-step s reads tokens from buffer s % 2 and weights from buffer s % 3.
+      // Issue order per step: tokens of s + 1, then weights of s + 2; so when
+      // step s starts, everything but the newest GPW - GPW_T loads (the
+      // weights of s + 1) has landed, tokens and weights of s included. The
+      // barrier after that wait also means every wave has finished step
+      // s - 1, whose buffers step s refills. Six steps repeat the buffer
+      // pattern; the k-steps past the end load zeros and are not computed.
+      auto step = [&](char* tb, char* wb, char* tb_next, char* wb_next2, int s) {
+        wait_vmcnt<C::GPW - C::GPW_T>();
+        barrier_no_fence();
+        load_t(tb_next, s + 1);
+        load_w(wb_next2, s + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(tb, wb);
+      };
+      load_t(stage0, 0);
+      load_w(wst0, 0);
+      load_w(wst1, 1);
+      for (int kt = 0;; kt += 6) {
+        step(stage0, wst0, stage1, wst2, kt);
+        if (kt + 1 >= nk) break;
+        step(stage1, wst1, stage0, wst0, kt + 1);
+        if (kt + 2 >= nk) break;
+        step(stage0, wst2, stage1, wst1, kt + 2);
+        if (kt + 3 >= nk) break;
+        step(stage1, wst0, stage0, wst2, kt + 3);
+        if (kt + 4 >= nk) break;
+        step(stage0, wst1, stage1, wst0, kt + 4);
+        if (kt + 5 >= nk) break;
+        step(stage1, wst2, stage0, wst1, kt + 5);
+        if (kt + 6 >= nk) break;
+      }
+      // the loads issued past the end have landed and every wave is done
+      // with LDS before the next task refills it
+      wait_vmcnt<0>();
+      barrier_no_fence();
+    } else {
+      load(stage0, 0);
       __syncthreads();
-      load(stage0, kt + 2);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(stage1);
-      __syncthreads();
+      for (int kt = 0; kt < nk; kt += 2) {
+        load(stage1, kt + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(stage0, stage0 + BM * 128);
+        __syncthreads();
+        load(stage0, kt + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(stage1, stage1 + BM * 128);
+        __syncthreads();
+      }
     }
 
     // epilogue: lane holds output columns 8*(v/4) + 4*(lane/32) + v%4 of token lane%32
