@@ -50,7 +50,8 @@ constexpr int STAGE = T_TILE + N_TILE;   // both tiles have the same size
 constexpr int GROUPS = STAGE / 1024;     // 1 KB direct-to-LDS loads per step
 constexpr int GPW = GROUPS / WAVES;
 static_assert(T_TILE == N_TILE && GROUPS % WAVES == 0, "uniform loads per wave");
-static_assert(2 * STAGE <= 160 * 1024, "two stages fit in LDS");
+static_assert(2 * STAGE <= 160 * 1024 && 3 * T_TILE + 2 * N_TILE <= 160 * 1024 && GPW % 2 == 0,
+              "two whole stages, or the split stages, fit in LDS");
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -111,8 +112,21 @@ struct Params {
 template <int MODE>
 __global__ __launch_bounds__(THREADS, 1) void gemm_bwd_kernel(Params p) {
   constexpr bool WGRAD = MODE == kWgrad;
-  __shared__ __attribute__((aligned(1024))) char stage0[STAGE];
-  __shared__ __attribute__((aligned(1024))) char stage1[STAGE];
+  // Weight gradients: the A tile of a step in one of three LDS buffers, the
+  // B tile in one of two (160 KB), so A (the P rows the m-tiles walk, most of
+  // the L2 misses) streams two steps ahead and B one. The dgrad kernels keep
+  // two whole stages (A and B buffers 0 and 1): at 252-255 registers they
+  // spill with the split pipeline's extra LDS addresses and ran 5-10% slower.
+  // Separate arrays, so the compiler can tell the buffers being filled from
+  // the ones being read.
+  // (two stages: abuf0 / abuf1 hold a whole stage each, the A tile then the
+  // B tile)
+  constexpr bool SPLIT = WGRAD;
+  __shared__ __attribute__((aligned(1024))) char abuf0[SPLIT ? T_TILE : STAGE];
+  __shared__ __attribute__((aligned(1024))) char abuf1[SPLIT ? T_TILE : STAGE];
+  __shared__ __attribute__((aligned(1024))) char abuf2[SPLIT ? T_TILE : 16];
+  __shared__ __attribute__((aligned(1024))) char bbuf0[SPLIT ? N_TILE : 16];
+  __shared__ __attribute__((aligned(1024))) char bbuf1[SPLIT ? N_TILE : 16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
@@ -154,13 +168,19 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_bwd_kernel(Params p) {
     const __amdgpu_buffer_rsrc_t b_rsrc = make_rsrc(p.b, p.b_bytes);
 
     // per-lane source of each 1 KB group: groups [0, GROUPS/2) fill the A
-    // tile, the rest the B tile. A transposed tile row is BO * 2 = 512 bytes,
-    // so a group covers 2 rows; a K-contiguous row is 128 bytes, 8 per group.
+    // tile, the rest the B tile; every wave loads GPW/2 of each (load q < GPW/2
+    // is an A group). A transposed tile row is BO * 2 = 512 bytes, so a group
+    // covers 2 rows; a K-contiguous row is 128 bytes, 8 per group.
+    // (two-stage pipeline: waves 0 .. WAVES/2 - 1 load A, the others B)
+    auto grp_of = [&](int q) -> int {
+      if (!SPLIT) return wave * GPW + q;
+      return q < GPW / 2 ? wave * (GPW / 2) + q : GROUPS / 2 + wave * (GPW / 2) + (q - GPW / 2);
+    };
     uint32_t off[GPW];
     int krow[GPW];                 // K row (transposed tiles) or K column of the chunk (K-contiguous tile)
 #pragma unroll
     for (int q = 0; q < GPW; ++q) {
-      const int grp = wave * GPW + q;
+      const int grp = grp_of(q);
       off[q] = kOob;
       krow[q] = 0;
       const bool in_a = grp < GROUPS / 2;
@@ -186,12 +206,14 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_bwd_kernel(Params p) {
         off[q] = static_cast<uint32_t>((row0 + r) * p.K + lc * 8) * 2;
       }
     }
-    // issue the loads of step kt into `stage`; rows / columns past the end
-    // (and steps past the end) read zeros
-    auto load = [&](char* stage, int kt) {
+    // issue the loads of step kt: with the split pipeline the A loads
+    // (q < GPW/2, a_side) or the B loads into `buf`; with two stages every
+    // load of the wave, A groups into `buf`, B groups into `bbuf`. Rows /
+    // columns past the end (and steps past the end) read zeros.
+    auto load = [&](char* buf, int kt, bool a_side, char* bbuf = nullptr) {
 #pragma unroll
-      for (int q = 0; q < GPW; ++q) {
-        const int grp = wave * GPW + q;
+      for (int q = SPLIT ? (a_side ? 0 : GPW / 2) : 0; q < (SPLIT ? (a_side ? GPW / 2 : GPW) : GPW); ++q) {
+        const int grp = grp_of(q);
         const bool in_a = grp < GROUPS / 2;
         uint32_t o, soff;
         if (in_a || WGRAD) {
@@ -205,7 +227,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_bwd_kernel(Params p) {
           soff = static_cast<uint32_t>(kt) * BK * 2;
         }
         const __amdgpu_buffer_rsrc_t rsrc = in_a ? a_rsrc : b_rsrc;
-        char* const dst = stage + grp * 1024;
+        char* const dst = (in_a || SPLIT ? buf : bbuf) + (in_a ? grp : grp - GROUPS / 2) * 1024;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)dst, 16, o, soff, 0, 0);
       }
     };
@@ -216,9 +238,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_bwd_kernel(Params p) {
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
 
-    auto compute = [&](const char* base) {
-      const char* ta = base;
-      const char* tb = base + T_TILE;
+    auto compute = [&](const char* ta, const char* tb) {
 #pragma unroll
       for (int kk = 0; kk < BK / 16; ++kk) {
         bf16x8 af[FM];
@@ -238,17 +258,56 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_bwd_kernel(Params p) {
       }
     };
 
-    load(stage0, 0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; kt += 2) {
-      load(stage1, kt + 1);
+    // Step s reads A from buffer s % 3 and B from buffer s % 2. Issue order
+    // per step: B of s + 1, then A of s + 2; so when step s starts, all but
+    // the newest GPW/2 loads (A of s + 1) have landed, A and B of s
+    // included, and after the barrier every wave is done with step s - 1,
+    // whose buffers step s refills. Six steps repeat the buffer pattern; the
+    // steps past the end load zeros and are not computed.
+    auto step = [&](char* a, char* b, char* b_next, char* a_next2, int st) {
+      wait_vmcnt<GPW / 2>();
+      barrier_no_fence();
+      load(b_next, st + 1, false);
+      load(a_next2, st + 2, true);
       __builtin_amdgcn_sched_barrier(0);
-      compute(stage0);
+      compute(a, b);
+    };
+    if constexpr (SPLIT) {
+    load(bbuf0, 0, false);
+    load(abuf0, 0, true);
+    load(abuf1, 1, true);
+    for (int kt = 0;; kt += 6) {
+      step(abuf0, bbuf0, bbuf1, abuf2, kt);
+      if (kt + 1 >= nk) break;
+      step(abuf1, bbuf1, bbuf0, abuf0, kt + 1);
+      if (kt + 2 >= nk) break;
+      step(abuf2, bbuf0, bbuf1, abuf1, kt + 2);
+      if (kt + 3 >= nk) break;
+      step(abuf0, bbuf1, bbuf0, abuf2, kt + 3);
+      if (kt + 4 >= nk) break;
+      step(abuf1, bbuf0, bbuf1, abuf0, kt + 4);
+      if (kt + 5 >= nk) break;
+      step(abuf2, bbuf1, bbuf0, abuf1, kt + 5);
+      if (kt + 6 >= nk) break;
+    }
+    // the loads issued past the end have landed and every wave is done with
+    // LDS before the next task refills it
+    wait_vmcnt<0>();
+    barrier_no_fence();
+    } else {
+      // two stages: step s+1 streams into one while the MFMAs read the other
+      load(abuf0, 0, true, abuf0 + T_TILE);
       __syncthreads();
-      load(stage0, kt + 2);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(stage1);
-      __syncthreads();
+      for (int kt = 0; kt < nk; kt += 2) {
+        load(abuf1, kt + 1, true, abuf1 + T_TILE);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(abuf0, abuf0 + T_TILE);
+        __syncthreads();
+        load(abuf0, kt + 2, true, abuf0 + T_TILE);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(abuf1, abuf1 + T_TILE);
+        __syncthreads();
+      }
     }
 
     if constexpr (WGRAD) {
