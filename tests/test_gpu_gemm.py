@@ -81,6 +81,11 @@ SHAPES = [  # T, H, E, k, I, block_m
     (200, 200, 8, 3, 40, 64),      # K tails of one 8-column chunk
     (700, 2048, 8, 4, 768, 256),   # 256-row tiles: several full tiles per expert, ragged last tiles
     (300, 384, 16, 4, 136, 256),   # 256-row tiles with partial column tiles and a K tail
+    # 256-row tiles run a six-step pipeline loop: k-step counts 1, 4 / 2, 5 / 7, 1
+    # (GEMM1 K = H, GEMM2 K = I; 64 K a step) end it at every position
+    (260, 64, 4, 2, 200, 256),
+    (300, 120, 4, 2, 312, 256),
+    (280, 448, 4, 2, 64, 256),
 ]
 
 
