@@ -542,11 +542,17 @@ hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s, const
 
 bool gemm_bf16_supports(int block_m) { return block_m == 32 || block_m == 64 || block_m == 128 || block_m == 256; }
 
+// Tiles: 256 rows x 128 output columns (128 gate + 128 up weight rows) where
+// experts average >= 384 rows; 128- and 64-row tiles keep 256 weight rows a
+// task too, so that their stages split (tokens double, weights triple
+// buffered): wider tiles (512 weight rows, two whole stages) staged fewer
+// bytes per MFMA but ran 3-18% slower (Qwen3-30B-A3B and Scout shapes at
+// T = 1024 .. 4096); 32-row tiles (small T) keep 512 weight rows.
 hipError_t launch_gemm1_bf16(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   switch (g.block_m) {
     case 256: return launch<256, 128, 4, 2, true>(g, dev, s);
-    case 128: return launch<128, 256, 2, 4, true>(g, dev, s);
-    case 64: return launch<64, 256, 1, 8, true>(g, dev, s);
+    case 128: return launch<128, 128, 2, 4, true>(g, dev, s);
+    case 64: return launch<64, 128, 2, 4, true>(g, dev, s);
     case 32: return launch<32, 256, 1, 8, true>(g, dev, s);
     default: return hipErrorInvalidValue;
   }
@@ -556,8 +562,8 @@ hipError_t launch_gemm1_bf16(const GemmArgs& g, const DeviceInfo& dev, hipStream
 hipError_t launch_gemm1_relu2_bf16(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   switch (g.block_m) {
     case 256: return launch<256, 256, 4, 2, true, kActRelu2>(g, dev, s);
-    case 128: return launch<128, 512, 2, 4, true, kActRelu2>(g, dev, s);
-    case 64: return launch<64, 512, 1, 8, true, kActRelu2>(g, dev, s);
+    case 128: return launch<128, 256, 2, 4, true, kActRelu2>(g, dev, s);
+    case 64: return launch<64, 256, 2, 4, true, kActRelu2>(g, dev, s);
     case 32: return launch<32, 512, 1, 8, true, kActRelu2>(g, dev, s);
     default: return hipErrorInvalidValue;
   }
@@ -566,8 +572,8 @@ hipError_t launch_gemm1_relu2_bf16(const GemmArgs& g, const DeviceInfo& dev, hip
 hipError_t launch_gemm2_bf16(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   switch (g.block_m) {
     case 256: return launch<256, 256, 4, 2, false>(g, dev, s);
-    case 128: return launch<128, 512, 2, 4, false>(g, dev, s);
-    case 64: return launch<64, 512, 1, 8, false>(g, dev, s);
+    case 128: return launch<128, 256, 2, 4, false>(g, dev, s);
+    case 64: return launch<64, 256, 2, 4, false>(g, dev, s);
     case 32: return launch<32, 512, 1, 8, false>(g, dev, s);
     default: return hipErrorInvalidValue;
   }
@@ -576,8 +582,8 @@ hipError_t launch_gemm2_bf16(const GemmArgs& g, const DeviceInfo& dev, hipStream
 hipError_t launch_gemm2_combine_bf16(const GemmArgs& g, const CombineArgs& c, const DeviceInfo& dev, hipStream_t s) {
   switch (g.block_m) {
     case 256: return launch<256, 256, 4, 2, false, kActSwiglu, true>(g, dev, s, &c);
-    case 128: return launch<128, 512, 2, 4, false, kActSwiglu, true>(g, dev, s, &c);
-    case 64: return launch<64, 512, 1, 8, false, kActSwiglu, true>(g, dev, s, &c);
+    case 128: return launch<128, 256, 2, 4, false, kActSwiglu, true>(g, dev, s, &c);
+    case 64: return launch<64, 256, 2, 4, false, kActSwiglu, true>(g, dev, s, &c);
     case 32: return launch<32, 512, 1, 8, false, kActSwiglu, true>(g, dev, s, &c);
     default: return hipErrorInvalidValue;
   }
