@@ -547,13 +547,15 @@ bool gemm_bf16_supports(int block_m) { return block_m == 32 || block_m == 64 || 
 // task too, so that their stages split (tokens double, weights triple
 // buffered): wider tiles (512 weight rows, two whole stages) staged fewer
 // bytes per MFMA but ran 3-18% slower (Qwen3-30B-A3B and Scout shapes at
-// T = 1024 .. 4096); 32-row tiles (small T) keep 512 weight rows.
+// T = 1024 .. 4096). 32-row tiles run four waves (a token stage of 32 rows
+// is four 1 KB loads, one a wave), which lets them split too (2-17% faster
+// at T = 256 .. 512 than eight waves over 512 weight rows).
 hipError_t launch_gemm1_bf16(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   switch (g.block_m) {
     case 256: return launch<256, 128, 4, 2, true>(g, dev, s);
     case 128: return launch<128, 128, 2, 4, true>(g, dev, s);
     case 64: return launch<64, 128, 2, 4, true>(g, dev, s);
-    case 32: return launch<32, 256, 1, 8, true>(g, dev, s);
+    case 32: return launch<32, 128, 1, 4, true>(g, dev, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -564,7 +566,7 @@ hipError_t launch_gemm1_relu2_bf16(const GemmArgs& g, const DeviceInfo& dev, hip
     case 256: return launch<256, 256, 4, 2, true, kActRelu2>(g, dev, s);
     case 128: return launch<128, 256, 2, 4, true, kActRelu2>(g, dev, s);
     case 64: return launch<64, 256, 2, 4, true, kActRelu2>(g, dev, s);
-    case 32: return launch<32, 512, 1, 8, true, kActRelu2>(g, dev, s);
+    case 32: return launch<32, 256, 1, 4, true, kActRelu2>(g, dev, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -574,7 +576,7 @@ hipError_t launch_gemm2_bf16(const GemmArgs& g, const DeviceInfo& dev, hipStream
     case 256: return launch<256, 256, 4, 2, false>(g, dev, s);
     case 128: return launch<128, 256, 2, 4, false>(g, dev, s);
     case 64: return launch<64, 256, 2, 4, false>(g, dev, s);
-    case 32: return launch<32, 512, 1, 8, false>(g, dev, s);
+    case 32: return launch<32, 256, 1, 4, false>(g, dev, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -584,7 +586,7 @@ hipError_t launch_gemm2_combine_bf16(const GemmArgs& g, const CombineArgs& c, co
     case 256: return launch<256, 256, 4, 2, false, kActSwiglu, true>(g, dev, s, &c);
     case 128: return launch<128, 256, 2, 4, false, kActSwiglu, true>(g, dev, s, &c);
     case 64: return launch<64, 256, 2, 4, false, kActSwiglu, true>(g, dev, s, &c);
-    case 32: return launch<32, 512, 1, 8, false, kActSwiglu, true>(g, dev, s, &c);
+    case 32: return launch<32, 256, 1, 4, false, kActSwiglu, true>(g, dev, s, &c);
     default: return hipErrorInvalidValue;
   }
 }
