@@ -100,6 +100,18 @@ def test_bf16_forward_expert_groups_long_runs():
     assert torch.isfinite(out.float()).all()
 
 
+def test_bf16_forward_expert_groups_very_long_run():
+    """One expert with 117 m-tiles of 256 rows: the 64-tile continuation of the
+    grouped order's expert-run search takes several rounds in both
+    directions; small H and I keep the full oracle comparison cheap."""
+    cfg = get_config("tiny_bf16").with_(T=30000, H=64, E=2, k=1, I=64, w_std=0.05)
+    inp = make_inputs(cfg, seed=6)
+    inp.logits[:] = -1.0
+    inp.logits[:29900, 0] = 2.0
+    inp.logits[29900:, 1] = 2.0
+    _full_compare(cfg, inp, block_m=256)
+
+
 def test_bf16_forward_one_expert_takes_all():
     cfg = get_config("tiny_bf16").with_(T=300, E=8, k=1)
     inp = make_inputs(cfg, seed=3)
