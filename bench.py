@@ -27,9 +27,9 @@ PEAK_HBM_GBS = 8000.0
 DTYPE_NAME = {0: "bf16", 1: "fp8_e4m3 (128-block scales)", 2: "mxfp4 weights x mxfp8 activations"}
 # The pages' own 1-GPU forward figure for this workload (other hardware, context only):
 # Liger-Kernel PR #1463, MoEBenchmark results, H200, Qwen3-30B-A3B, T=8192, BF16 forward.
-PAGE_BASELINE = {"qwen3_30b_a3b_bf16": (354.38, "H200 1-GPU BF16 forward, Liger-Kernel PR #1463 MoEBenchmark"),
+PAGE_FIGURES = {"qwen3_30b_a3b_bf16": (354.38, "H200 1-GPU BF16 forward, Liger-Kernel PR #1463 MoEBenchmark"),
                  "llama4_scout_bf16": (511.36, "H200 1-GPU BF16 forward, Liger-Kernel PR #1463 MoEBenchmark")}
-PAGE_BASELINE_BWD = {
+PAGE_FIGURES_BWD = {
     "qwen3_30b_a3b_bf16": (199.28, "H200 1-GPU BF16 backward, Liger-Kernel PR #1463 MoEBenchmark"),
     "llama4_scout_bf16": (299.54, "H200 1-GPU BF16 backward, Liger-Kernel PR #1463 MoEBenchmark")}
 KERNEL_SRC = {"gemm1_swiglu": {0: "gemm_bf16.hip", 1: "gemm_scaled.hip", 2: "gemm_scaled.hip"},
@@ -264,10 +264,10 @@ def main(argv=None):
     inp = make_inputs(cfg)
     if a.backward:
         rec = measure_backward(cfg, inp, a.steps, a.warmup)
-        base = PAGE_BASELINE_BWD.get(cfg.name) if not a.tokens else None
+        base = PAGE_FIGURES_BWD.get(cfg.name) if not a.tokens else None
     else:
         rec = measure(cfg, inp, a.steps, a.warmup, a.block_m, fused_combine=a.fused_combine)
-        base = PAGE_BASELINE.get(cfg.name) if not a.tokens else None
+        base = PAGE_FIGURES.get(cfg.name) if not a.tokens else None
     rec["vs_baseline"] = round(rec["value"] / base[0], 4) if base else None
     rec["baseline_ref"] = f"{base[0]} TFLOP/s, {base[1]} (other hardware, context only)" if base else None
     if not a.no_cpu_baseline:

@@ -17,7 +17,7 @@ projection, SwiGLU and a down projection; the k expert outputs are summed
 with the top-k weights. Implemented as: route -> expert-sorted padded
 permutation -> grouped GEMM1 + SwiGLU -> grouped GEMM2 -> weighted combine.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
   * top-k ties go to the lower expert index; slots are in descending score;
   * weights are softmax over the k selected logits (== softmax over all E,
     renormalised over the top k), or sigmoid(logit) without renormalisation;
@@ -440,7 +440,7 @@ __all__ = [n for n in dir() if not n.startswith("_") and n not in ("math", "np",
 
 # ============================================================================ backward
 # The backward of the BF16 SwiGLU routed forward, for a given output gradient
-# dout (training). Readings (the design doc lists them): the top-k selection is
+# dout (training). Readings where the pages are silent: the top-k selection is
 # piecewise constant (no gradient through the choice); the forward saves the
 # gate/up pre-activations in bf16 beside h; storage points of the backward:
 # dY and dGU (the operands of the next GEMMs) and the per-assignment dx rows
