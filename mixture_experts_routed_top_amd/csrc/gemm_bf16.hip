@@ -21,14 +21,12 @@
 //     narrower for 64- and 32-row tiles); each wave holds 128 accumulator
 //     registers, the most the register file leaves room for;
 //   * operands reach LDS by direct-to-LDS buffer loads (16 bytes a lane, 1 KB
-//     a wave instruction). The 256-row tiles split each k-step's LDS stage:
-//     token rows in one of two buffers, weight rows in one of three (exactly
-//     the 160 KB of LDS), so the weight rows, most of the L2 misses, stream
-//     two k-steps ahead; every wave issues the same number of each kind of
-//     load, and one exact wait count per step lets the newest weight loads
-//     stay in flight across the barrier. The other tiles keep two whole
-//     stages: the loads of k-step s+1 are issued before the MFMAs of k-step
-//     s, and one barrier ends each step;
+//     a wave instruction), each k-step's LDS stage split: token rows in one
+//     of two buffers, weight rows in one of three (the 256-row tiles take
+//     exactly the 160 KB of LDS), so the weight rows, most of the L2 misses,
+//     stream two k-steps ahead; every wave issues the same number of each
+//     kind of load, and one exact wait count per step lets the newest weight
+//     loads stay in flight across the barrier that starts the step;
 //   * inside a k-step the MFMA fragments of the next 16-K substep are read
 //     from LDS while the current substep's MFMAs run (order pinned with
 //     scheduling-group barriers);
@@ -65,23 +63,18 @@ struct Cfg {
   static constexpr int FN = TN / 32;
   static constexpr int WAVES = WM * WN;
   static constexpr int THREADS = 64 * WAVES;
-  static constexpr int ROWS = BM + B_ROWS;            // LDS rows per stage
-  static constexpr int GROUPS = ROWS / 8;             // 8 rows = one 1 KB direct-to-LDS load
-  static constexpr int GPW = (GROUPS + WAVES - 1) / WAVES;   // loads per wave per k-step
-  static constexpr int STAGE = ROWS * 128;
-  // Split pipeline, where it fits: the token rows of a k-step in one of two
-  // LDS buffers and its weight rows in one of three, so the weight rows
-  // (most of the L2 misses) stream two k-steps ahead and the token rows one.
-  // Every wave issues the same number of token and of weight loads per step,
-  // which makes one wait count exact for all of them.
+  // Split pipeline: the token rows of a k-step in one of two LDS buffers and
+  // its weight rows in one of three, so the weight rows (most of the L2
+  // misses) stream two k-steps ahead and the token rows one. Every wave
+  // issues the same number of token and of weight loads per step (1 KB
+  // direct-to-LDS loads, 8 rows each), which makes one wait count exact.
   static constexpr int T_BYTES = BM * 128, W_BYTES = B_ROWS * 128;
   static constexpr int T_GROUPS = BM / 8, W_GROUPS = B_ROWS / 8;
-  static constexpr bool SPLIT = 2 * T_BYTES + 3 * W_BYTES <= 160 * 1024 && T_GROUPS % WAVES == 0 &&
-                                W_GROUPS % WAVES == 0;
-  static constexpr int GPW_T = SPLIT ? T_GROUPS / WAVES : 0;   // token loads per wave per k-step
+  static constexpr int GPW_T = T_GROUPS / WAVES;       // token loads per wave per k-step
+  static constexpr int GPW = GPW_T + W_GROUPS / WAVES;  // loads per wave per k-step
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile is a multiple of 32");
-  static_assert(BM % 8 == 0, "token rows fill whole 8-row groups");
-  static_assert(2 * STAGE <= 160 * 1024, "two stages fit in LDS");
+  static_assert(BM % 8 == 0 && T_GROUPS % WAVES == 0 && W_GROUPS % WAVES == 0, "uniform loads per wave");
+  static_assert(2 * T_BYTES + 3 * W_BYTES <= 160 * 1024, "the split stages fit in LDS");
 };
 
 // The XOR swizzle of the 16-byte chunks of LDS row `row`: row & 7, which
@@ -203,14 +196,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
   using C = Cfg<BM, BN, WM, WN, GEMM1, ACT>;
   static_assert(!FUSE || !GEMM1, "the combine fuses into GEMM2");
   constexpr int BK = C::BK;
-  // separate LDS arrays, so the compiler can tell the stage being filled by
-  // the direct-to-LDS loads from the stage being read: two whole stages, or
-  // (split pipeline) two token buffers and three weight buffers
-  __shared__ __attribute__((aligned(1024))) char stage0[C::SPLIT ? C::T_BYTES : C::STAGE];
-  __shared__ __attribute__((aligned(1024))) char stage1[C::SPLIT ? C::T_BYTES : C::STAGE];
-  __shared__ __attribute__((aligned(1024))) char wst0[C::SPLIT ? C::W_BYTES : 16];
-  __shared__ __attribute__((aligned(1024))) char wst1[C::SPLIT ? C::W_BYTES : 16];
-  __shared__ __attribute__((aligned(1024))) char wst2[C::SPLIT ? C::W_BYTES : 16];
+  // separate LDS arrays, so the compiler can tell the buffer being filled by
+  // the direct-to-LDS loads from the one being read: two token buffers and
+  // three weight buffers
+  __shared__ __attribute__((aligned(1024))) char stage0[C::T_BYTES];
+  __shared__ __attribute__((aligned(1024))) char stage1[C::T_BYTES];
+  __shared__ __attribute__((aligned(1024))) char wst0[C::W_BYTES];
+  __shared__ __attribute__((aligned(1024))) char wst1[C::W_BYTES];
+  __shared__ __attribute__((aligned(1024))) char wst2[C::W_BYTES];
 
   // the wave index is uniform across the wave: keep it in a scalar register so
   // that the LDS destinations and descriptors of the loads are scalar too
@@ -261,7 +254,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
     // pad rows, rows past N and rows past the tile
     // (`sid`: the sorted id of a GEMM1 token row, loaded beforehand)
     auto row_src = [&](int row, int sid) -> uint32_t {
-      if (row >= C::ROWS) return kOob;
+      if (row >= BM + C::B_ROWS) return kOob;
       if (row < BM) {
         int64_t src_row = -1;
         if (GEMM1) {
@@ -289,10 +282,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
     // split pipeline the first GPW_T are token groups, the rest weight groups
     // (numbered from the first weight row)
     auto grp_of = [&](int q) -> int {
-      if (!C::SPLIT) return wave * C::GPW + q;
       return q < C::GPW_T ? wave * C::GPW_T + q : wave * (C::GPW - C::GPW_T) + (q - C::GPW_T);
     };
-    auto row_of = [&](int q) -> int { return grp_of(q) * 8 + g_row + (C::SPLIT && q >= C::GPW_T ? BM : 0); };
+    auto row_of = [&](int q) -> int { return grp_of(q) * 8 + g_row + (q >= C::GPW_T ? BM : 0); };
     // GEMM1 gathers its token rows by sorted id: every id this lane needs is
     // loaded before any is used, so the loads overlap instead of each one
     // waiting for the last (a weight row loads a harmless id too)
@@ -310,20 +302,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
       const uint32_t base = row_src(row, sid[q]);
       off[q] = base == kOob ? kOob : base + lc * 16;
     }
-    // issue the direct-to-LDS loads of k-step kt into `stage`
-    auto load = [&](char* stage, int kt) {
-      const uint32_t soff = static_cast<uint32_t>(kt) * BK * 2;
-#pragma unroll
-      for (int q = 0; q < C::GPW; ++q) {
-        const int grp = wave * C::GPW + q;
-        // chunks past K (the K tail, and the k-steps past the end that the
-        // branch-free pipeline still issues) read as zeros
-        const uint32_t o = kt * BK + kcol[q] < K ? off[q] : kOob;
-        if (C::GROUPS % C::WAVES == 0 || grp < C::GROUPS)   // wave-uniform
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(grp * 8 < BM ? a_rsrc : b_rsrc, (lds_ptr_t)(stage + grp * 1024), 16, o,
-                                                   soff, 0, 0);
-      }
-    };
     // split pipeline: the token loads of k-step kt into `tb`, the weight loads into `wb`
     auto load_t = [&](char* tb, int kt) {
       const uint32_t soff = static_cast<uint32_t>(kt) * BK * 2;
@@ -400,60 +378,44 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
       }
     };
 
-    // k-step s+1 streams into one stage while the MFMAs consume k-step s from
-    // the other; the loads are issued first (the scheduling barrier keeps them
-    // there) and must have landed at the barrier that ends the step
-    if constexpr (C::SPLIT) {
-      // k-step s reads tokens from buffer s % 2 and weights from buffer s % 3.
-      // Issue order per step: tokens of s + 1, then weights of s + 2; so when
-      // step s starts, everything but the newest GPW - GPW_T loads (the
-      // weights of s + 1) has landed, tokens and weights of s included. The
-      // barrier after that wait also means every wave has finished step
-      // s - 1, whose buffers step s refills. Six steps repeat the buffer
-      // pattern; the k-steps past the end load zeros and are not computed.
-      auto step = [&](char* tb, char* wb, char* tb_next, char* wb_next2, int s) {
-        wait_vmcnt<C::GPW - C::GPW_T>();
-        barrier_no_fence();
-        load_t(tb_next, s + 1);
-        load_w(wb_next2, s + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(tb, wb);
-      };
-      load_t(stage0, 0);
-      load_w(wst0, 0);
-      load_w(wst1, 1);
-      for (int kt = 0;; kt += 6) {
-        step(stage0, wst0, stage1, wst2, kt);
-        if (kt + 1 >= nk) break;
-        step(stage1, wst1, stage0, wst0, kt + 1);
-        if (kt + 2 >= nk) break;
-        step(stage0, wst2, stage1, wst1, kt + 2);
-        if (kt + 3 >= nk) break;
-        step(stage1, wst0, stage0, wst2, kt + 3);
-        if (kt + 4 >= nk) break;
-        step(stage0, wst1, stage1, wst0, kt + 4);
-        if (kt + 5 >= nk) break;
-        step(stage1, wst2, stage0, wst1, kt + 5);
-        if (kt + 6 >= nk) break;
-      }
-      // the loads issued past the end have landed and every wave is done
-      // with LDS before the next task refills it
-      wait_vmcnt<0>();
+    // k-step s reads tokens from buffer s % 2 and weights from buffer s % 3.
+    // Issue order per step: tokens of s + 1, then weights of s + 2; so when
+    // step s starts, everything but the newest GPW - GPW_T loads (the
+    // weights of s + 1) has landed, tokens and weights of s included. The
+    // barrier after that wait also means every wave has finished step
+    // s - 1, whose buffers step s refills; the loads are issued ahead of the
+    // MFMAs (the scheduling barrier keeps them there). Six steps repeat the
+    // buffer pattern; the k-steps past the end load zeros and are not computed.
+    auto step = [&](char* tb, char* wb, char* tb_next, char* wb_next2, int s) {
+      wait_vmcnt<C::GPW - C::GPW_T>();
       barrier_no_fence();
-    } else {
-      load(stage0, 0);
-      __syncthreads();
-      for (int kt = 0; kt < nk; kt += 2) {
-        load(stage1, kt + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(stage0, stage0 + BM * 128);
-        __syncthreads();
-        load(stage0, kt + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(stage1, stage1 + BM * 128);
-        __syncthreads();
-      }
+      load_t(tb_next, s + 1);
+      load_w(wb_next2, s + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(tb, wb);
+    };
+    load_t(stage0, 0);
+    load_w(wst0, 0);
+    load_w(wst1, 1);
+    for (int kt = 0;; kt += 6) {
+      step(stage0, wst0, stage1, wst2, kt);
+      if (kt + 1 >= nk) break;
+      step(stage1, wst1, stage0, wst0, kt + 1);
+      if (kt + 2 >= nk) break;
+      step(stage0, wst2, stage1, wst1, kt + 2);
+      if (kt + 3 >= nk) break;
+      step(stage1, wst0, stage0, wst2, kt + 3);
+      if (kt + 4 >= nk) break;
+      step(stage0, wst1, stage1, wst0, kt + 4);
+      if (kt + 5 >= nk) break;
+      step(stage1, wst2, stage0, wst1, kt + 5);
+      if (kt + 6 >= nk) break;
     }
+    // the loads issued past the end have landed and every wave is done
+    // with LDS before the next task refills it
+    wait_vmcnt<0>();
+    barrier_no_fence();
+
 
     // epilogue: lane holds output columns 8*(v/4) + 4*(lane/32) + v%4 of token lane%32
 #pragma unroll
