@@ -16,10 +16,11 @@
 //     lane ends up with four consecutive output columns of one token, which
 //     become one 8-byte store);
 //   * 8 waves per workgroup (two per SIMD, so one wave's MFMAs cover the other's
-//     waits); the workgroup tile is 256 sorted rows x 256 weight rows (128 gate
-//     + 128 up in GEMM1) when experts average >= 384 rows, else 128 x 512 (or
-//     narrower for 64- and 32-row tiles); each wave holds 128 accumulator
-//     registers, the most the register file leaves room for;
+//     waits; 4 for 32-row tiles); every tile stages 256 weight rows (128 gate
+//     + 128 up in GEMM1) against 256, 128, 64 or 32 sorted rows, the row-tile
+//     size moe_pick_block_m chooses from the mean rows per expert; a wave holds
+//     up to 128 accumulator registers, the most the register file leaves room
+//     for;
 //   * operands reach LDS by direct-to-LDS buffer loads (16 bytes a lane, 1 KB
 //     a wave instruction), each k-step's LDS stage split: token rows in one
 //     of two buffers, weight rows in one of three (the 256-row tiles take
@@ -504,8 +505,8 @@ hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s, const
 
 bool gemm_bf16_supports(int block_m) { return block_m == 32 || block_m == 64 || block_m == 128 || block_m == 256; }
 
-// Tiles: 256 rows x 128 output columns (128 gate + 128 up weight rows) where
-// experts average >= 384 rows; 128- and 64-row tiles keep 256 weight rows a
+// Tiles: 256 rows x 128 output columns (128 gate + 128 up weight rows) for
+// the largest row tile; 128- and 64-row tiles keep 256 weight rows a
 // task too, so that their stages split (tokens double, weights triple
 // buffered): wider tiles (512 weight rows, two whole stages) staged fewer
 // bytes per MFMA but ran 3-18% slower (Qwen3-30B-A3B and Scout shapes at

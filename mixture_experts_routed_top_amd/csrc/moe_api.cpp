@@ -139,9 +139,18 @@ int32_t moe_pick_block_m(int32_t dtype, int64_t T, int32_t k, int32_t E, int32_t
   if (!valid_dtype(dtype) || T < 0 || k < 1 || E < 1 || k > E || H <= 0 || I <= 0) return -1;
   const int64_t A = T * k;
   const int64_t mean = A / E;  // mean rows per expert
-  // BF16: 256 x 256 workgroup tiles stage the fewest bytes per MFMA once the
-  // experts hold enough rows that the extra padding stays small
-  if (dtype == MOE_DTYPE_BF16 && mean >= 384) return 256;
+  // BF16 (all tiles stream their weight rows two k-steps ahead): 256-row
+  // tiles stage the fewest bytes per MFMA and win from about 160 rows per
+  // expert, 128-row ones from 64, 64-row ones from 24; measured over the
+  // Qwen3-30B-A3B, Scout and Nemotron shapes at T = 256 .. 8192 (the whole
+  // forward, each row-tile size in turn), this picks the fastest or one
+  // within 5%
+  if (dtype == MOE_DTYPE_BF16) {
+    if (mean >= 160) return 256;
+    if (mean >= 64) return 128;
+    if (mean >= 24) return 64;
+    return 32;
+  }
   if (dtype == MOE_DTYPE_FP8_BLOCK128 && mean >= 768) return 256;
   if (mean >= 256) return 128;
   if (mean >= 48) return 64;
