@@ -214,8 +214,8 @@ def cpu_baseline(cfg, inp, budget_s: float = 15.0, backward: bool = False):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen3_30b_a3b_bf16")
     ap.add_argument("--tokens", type=int, default=None, help="override T (parity-size runs)")
     ap.add_argument("--block-m", type=int, default=None)

@@ -22,7 +22,8 @@
  *     them contiguously and scatters back to assignment order, the combine is
  *     unchanged; padded rows feed only dropped output rows.
  *   - FlashInfer PR #6465 (Hopper MXFP4 x FP8 MegaMoE tuning), Benchmark
- *     configuration: MXFP4 weights with K32 scaling, FP8 activations, BF16 I/O.
+ *     configuration: E2M1 weights with one shared E8M0 scale per 32 K elements,
+ *     E4M3 activations, BF16 input and output.
  *   - Liger-Kernel PR #1463, Summary: empty experts or K slices must not stall
  *     the schedule (empty experts own no tiles here).
  *
@@ -196,7 +197,7 @@ moe_status_t moe_quantize_mxfp8(const uint16_t* in, int64_t rows, int64_t cols,
  * moe_quantize_mxfp4 -- bf16 -> MXFP4 along each row: E2M1 codes (values
  * 0, 0.5, 1, 1.5, 2, 3, 4, 6), one E8M0 scale per 32 columns (OCP MX v1.0,
  * X = 2^(floor(log2 amax) - 2)); RN ties to even, saturating at 6. FlashInfer
- * PR #6465, Benchmark configuration (MXFP4 weights with K32 scaling).
+ * PR #6465, Benchmark configuration (E2M1 weights, one scale per 32 along K).
  *
  *   in [rows, cols] bf16; q [rows, cols / 2] uint8, two codes per byte, the
  *   even column in the low nibble; e8m0 [rows, cols / 32] uint8.
@@ -243,6 +244,28 @@ moe_status_t moe_grouped_gemm_swiglu(int32_t dtype, const void* x, const void* x
                                      int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
                                      int32_t block_m, int64_t cap,
                                      void* h, void* h_scale, void* stream);
+
+/*
+ * moe_grouped_gemm_swiglu_h32 -- moe_grouped_gemm_swiglu that also writes
+ * the fp32 intermediate before its storage rounding, for callers that check
+ * that rounding (bf16 RN, or the FP8 / MXFP8 requantisation) bit for bit.
+ *   h32 [cap, I] fp32, out, 16-byte aligned: for every sorted row
+ *       r < num_tiles * block_m, h32[r, n] is the value silu(g_n) * u_n that
+ *       the kernel rounds (BF16) or quantises (FP8_BLOCK128, MXFP4W_MXFP8A)
+ *       into h[r, n] / h_scale (pad rows: 0). Rows past num_tiles * block_m
+ *       are not touched.
+ * h and h_scale are written exactly as moe_grouped_gemm_swiglu writes them
+ * (the same kernels run; only the extra stores are added). Other arguments
+ * and errors as moe_grouped_gemm_swiglu; h32 NULL or misaligned ->
+ * MOE_ERR_INVALID_ARG.
+ */
+moe_status_t moe_grouped_gemm_swiglu_h32(int32_t dtype, const void* x, const void* x_scale,
+                                         const void* w1, const void* w1_scale,
+                                         const int32_t* sorted_ids, const int32_t* tile_expert,
+                                         const int32_t* num_tiles,
+                                         int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
+                                         int32_t block_m, int64_t cap,
+                                         void* h, void* h_scale, float* h32, void* stream);
 
 /*
  * moe_grouped_gemm_relu2 -- GEMM1 of an ungated expert with the squared-ReLU

@@ -27,8 +27,28 @@ FLAGS = [
 ]
 
 
+PROBES = os.path.join(HERE, "probes")
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
+
+
+def build_probes(verbose: bool = False):
+    """The matrix-core measurement probes (probes/*.hip), each a small
+    stand-alone executable next to its source."""
+    out = []
+    for f in sorted(os.listdir(PROBES)):
+        if not f.endswith(".hip"):
+            continue
+        src, exe = os.path.join(PROBES, f), os.path.join(PROBES, f[:-4])
+        r = subprocess.run([HIPCC, *FLAGS, src, "-o", exe], capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+        out.append(exe)
+    if verbose:
+        print(f"built {len(out)} probe(s) in {PROBES}")
+    return out
 
 
 def _compile(src: str) -> str:
@@ -55,6 +75,7 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB} from {len(srcs)} sources")
+    build_probes(verbose)
     return LIB
 
 

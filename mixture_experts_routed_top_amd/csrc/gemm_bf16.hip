@@ -118,6 +118,7 @@ struct Params {
   const int32_t* num_tiles;
   uint16_t* out;           // GEMM1: h [cap, I]; GEMM2: y [A, H]
   uint16_t* gu;            // GEMM1 (SwiGLU), optional: saved pre-activations [cap, 2I] (gate, up)
+  float* h32;              // GEMM1, optional: the fp32 h before its bf16 rounding [cap, I]
   const float* topk_w;     // GEMM2 with the fused combine: gate weights [A]
   uint16_t* comb;          //   combined output [T, H]
   int32_t* counters;       //   [T, ceil(H / BN)] finished slots per (token, column tile); zero between calls
@@ -455,6 +456,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
             st.x = pack_bf16x2(o[0], o[1]);
             st.y = pack_bf16x2(o[2], o[3]);
             *reinterpret_cast<uint2*>(p.out + dst_row * N + n) = st;
+            if (GEMM1 && p.h32 != nullptr)   // the values rounded to bf16 above, for checking that rounding
+              *reinterpret_cast<f32x4*>(p.h32 + dst_row * N + n) = f32x4{o[0], o[1], o[2], o[3]};
             if (GEMM1 && ACT == kActSwiglu && p.gu != nullptr) {
               // training forward: the gate and up pre-activations for the backward
               const float gv[4] = {acc[0][i][j][g * 4], acc[0][i][j][g * 4 + 1], acc[0][i][j][g * 4 + 2],
@@ -487,6 +490,7 @@ hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s, const
   p.num_tiles = g.num_tiles;
   p.out = static_cast<uint16_t*>(g.out);
   p.gu = static_cast<uint16_t*>(g.out_scale);   // BF16 SwiGLU GEMM1: the optional saved pre-activations
+  p.h32 = GEMM1 ? static_cast<float*>(g.h32) : nullptr;
   p.A = g.T * g.k;
   p.a_bytes = static_cast<uint32_t>((GEMM1 ? g.T * g.H : g.cap * g.I) * 2);
   p.H = g.H;

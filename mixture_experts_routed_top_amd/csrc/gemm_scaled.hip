@@ -8,8 +8,8 @@
 //    token's 1x128 scale and the weight's 128x128 block scale (the commit
 //    notes of that PR keep the running sum in fp32: narrower accumulators lose
 //    an order of magnitude of accuracy).
-//  * MXFP4W_MXFP8A (FlashInfer PR #6465, Benchmark configuration: MXFP4
-//    weights with K32 scaling, FP8 activations). The weights are E2M1, the
+//  * MXFP4W_MXFP8A (FlashInfer PR #6465, Benchmark configuration: E2M1
+//    weights carrying one shared scale per 32 K elements, E4M3 activations). The weights are E2M1, the
 //    tokens E4M3, both with one E8M0 scale per 32 along K, which the MFMA
 //    applies itself: each lane passes the scale of the 32-element K block it
 //    holds ("GC-MoE on SM120", Abstract: FP4 weights on one operand, FP8
@@ -191,6 +191,7 @@ struct Params {
   const int32_t* num_tiles;
   void* out;                 // GEMM1: h codes [cap, I]; GEMM2: y bf16 [A, H]
   void* out_scale;           // GEMM1: fp32 [cap, I/128] or E8M0 [cap, I/32]
+  float* h32;                // GEMM1, optional: the fp32 h before its requantisation [cap, I]
   int64_t A;
   uint32_t a_rows;           // rows of the token operand (T for GEMM1, cap for GEMM2)
   int E, H, I, k;
@@ -386,27 +387,38 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_scaled_kernel(Params p
         }
       } else {
         const uint32_t* sc = reinterpret_cast<const uint32_t*>(base + C::A_REGION + C::W_REGION);
-        uint32_t tsc[C::FM];
+        // Per-128 promotion without a second accumulator set. Each scale s
+        // splits into a power of two, which the MFMA applies itself through
+        // its E8M0 operand scales (token: per lane, weight block: per wave),
+        // and a mantissa m (split_e8m0). acc holds the sum in units of the
+        // current step's mantissa product f = m_x * m_w, so each step
+        // rescales acc by f_prev / f and adds the MFMA's products; the
+        // epilogue multiplies by the last f. With the exponents applied
+        // exactly by the MFMA, f_prev / f lies between 1/4 and 4 for normal
+        // scales and between 2^-46 and 2^46 for any finite ones (a ratio of
+        // two whole scale products overflows, or divides by a denormal, for
+        // blocks of very different magnitudes). A pad row has s_x = 0: its
+        // acc stays 0 and its last f is 0.
+        int xb[C::FM];
+        float xm[C::FM];
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i) tsc[i] = sc[wm * C::TM + i * 32 + (lane & 31)];
-        float wsc[C::HALVES];
+        for (int i = 0; i < C::FM; ++i)
+          xm[i] = split_e8m0(__uint_as_float(sc[wm * C::TM + i * 32 + (lane & 31)]), xb[i]);
+        int wb[C::HALVES];
+        float wmn[C::HALVES];
 #pragma unroll
         for (int h = 0; h < C::HALVES; ++h)
           // a scalar load (the index is uniform and the scales are read-only
           // here): it waits on its own counter, not behind the stage loads
-          wsc[h] = ((const_f32_ptr)p.w_scale)[__builtin_amdgcn_readfirstlane(
-              static_cast<int>(wsb[h] * (K / 128) + kt))];
-        // Per-128 promotion without a second accumulator set: acc holds the
-        // sum in units of the current step's scale product f = s_x * s_w, so
-        // each step rescales acc by f_prev / f and adds the unscaled MFMA
-        // products; the epilogue multiplies by the last f. (A pad row has
-        // s_x = 0: its acc stays 0 and its last f is 0.)
+          wmn[h] = split_e8m0(((const_f32_ptr)p.w_scale)[__builtin_amdgcn_readfirstlane(
+                                  static_cast<int>(wsb[h] * (K / 128) + kt))],
+                              wb[h]);
 #pragma unroll
         for (int h = 0; h < C::HALVES; ++h)
 #pragma unroll
           for (int i = 0; i < C::FM; ++i) {
-            const float f = __uint_as_float(tsc[i]) * wsc[h];
-            const float ratio = f > 0.0f ? fprev[h][i] * __builtin_amdgcn_rcpf(f) : 1.0f;
+            const float f = xm[i] * wmn[h];
+            const float ratio = f > 0.0f ? __fdiv_rn(fprev[h][i], f) : 1.0f;
             if (f > 0.0f) fprev[h][i] = f;
 #pragma unroll
             for (int j = 0; j < C::FN; ++j)
@@ -431,7 +443,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_scaled_kernel(Params p
 #pragma unroll
               for (int i = 0; i < C::FM; ++i)
                 acc[h][i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf, xf[i], acc[h][i][j], 0, 0, 0,
-                                                                             127, 0, 127);
+                                                                             wb[h], 0, xb[i]);
             }
           }
         }
@@ -509,6 +521,20 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_scaled_kernel(Params p
             const float u = acc[C::HALVES - 1][i][j][v] * (MODE == kFp8Block ? fprev[C::HALVES - 1][i] : 1.0f);
             hv[i][j][v] = g / (1.0f + expf(-g)) * u;
           }
+      if (p.h32 != nullptr) {
+        // the values the requantisation below reads, for checking it bit for bit
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int n = n0 + wn * C::TN + j * 32 + g * 8 + (lane >> 5) * 4;
+              if (n < N)
+                *reinterpret_cast<f32x4*>(p.h32 + (row0 + wm * C::TM + i * 32 + (lane & 31)) * N + n) =
+                    f32x4{hv[i][j][4 * g], hv[i][j][4 * g + 1], hv[i][j][4 * g + 2], hv[i][j][4 * g + 3]};
+            }
+      }
       uint8_t* hq = static_cast<uint8_t*>(p.out);
       if (MODE == kFp8Block) {
         // one 1x128 block per token row: this workgroup's BN = 128 columns
@@ -613,6 +639,7 @@ hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   p.num_tiles = g.num_tiles;
   p.out = g.out;
   p.out_scale = g.out_scale;
+  p.h32 = GEMM1 ? static_cast<float*>(g.h32) : nullptr;
   p.A = g.T * g.k;
   p.a_rows = static_cast<uint32_t>(GEMM1 ? g.T : g.cap);
   p.E = g.E;

@@ -261,6 +261,31 @@ moe_status_t moe_grouped_gemm_swiglu(int32_t dtype, const void* x, const void* x
   }
 }
 
+moe_status_t moe_grouped_gemm_swiglu_h32(int32_t dtype, const void* x, const void* x_scale, const void* w1,
+                                         const void* w1_scale, const int32_t* sorted_ids,
+                                         const int32_t* tile_expert, const int32_t* num_tiles, int64_t T,
+                                         int32_t H, int32_t I, int32_t E, int32_t k, int32_t block_m, int64_t cap,
+                                         void* h, void* h_scale, float* h32, void* stream) {
+  if (moe_status_t st = check_gemm(dtype, x, x_scale, w1, w1_scale, sorted_ids, tile_expert, num_tiles, T, H,
+                                   I, E, k, block_m, cap, h, h_scale, true))
+    return st;
+  if (T == 0) return MOE_OK;
+  if (!h32 || !aligned(h32, 16)) return MOE_ERR_INVALID_ARG;
+  moe::DeviceInfo dev;
+  if (moe_status_t st = current_device(&dev)) return st;
+  moe::GemmArgs g{x, x_scale, w1, w1_scale, sorted_ids, tile_expert, num_tiles, h, h_scale,
+                  T, H, I, E, k, block_m, cap};
+  g.h32 = h32;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  switch (dtype) {
+    case MOE_DTYPE_BF16:
+      g.out_scale = nullptr;
+      return launched(moe::launch_gemm1_bf16(g, dev, s));
+    case MOE_DTYPE_FP8_BLOCK128: return launched(moe::launch_gemm1_fp8(g, dev, s));
+    default: return launched(moe::launch_gemm1_mx(g, dev, s));
+  }
+}
+
 moe_status_t moe_grouped_gemm_swiglu_save(const void* x, const void* w1, const int32_t* sorted_ids,
                                           const int32_t* tile_expert, const int32_t* num_tiles, int64_t T,
                                           int32_t H, int32_t I, int32_t E, int32_t k, int32_t block_m, int64_t cap,

@@ -90,6 +90,15 @@ __device__ __forceinline__ int mx_scale_exponent(float amax, int emax) {
 // is exact whenever the product is a normal fp32 number.
 __device__ __forceinline__ float mx_inv_scale(int x) { return __builtin_ldexpf(1.0f, -x); }
 
+// Split a finite scale s >= 0 into s = m * 2^(b - 127) with b an E8M0 byte
+// (b in [0, 254]): for a normal s, b is its biased exponent and m in [1, 2);
+// for a subnormal s (or 0), b = 0 and m = s * 2^127, exact and below 1.
+__device__ __forceinline__ float split_e8m0(float s, int& b) {
+  const uint32_t u = __float_as_uint(s);
+  b = static_cast<int>((u >> 23) & 0xFF);
+  return b ? __uint_as_float((u & 0x007FFFFFu) | 0x3F800000u) : s * 0x1p127f;
+}
+
 // ------------------------------------------------------------------ wave reductions
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

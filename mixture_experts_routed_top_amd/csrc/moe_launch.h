@@ -47,6 +47,7 @@ struct GemmArgs {
   int64_t T;
   int H, I, E, k, block_m;
   int64_t cap;
+  void* h32 = nullptr;    // GEMM1, optional: fp32 h [cap, I] before its storage rounding
 };
 
 // GEMM2 with the weighted combine fused: gate weights [T*k] fp32, the

@@ -6,7 +6,7 @@
 // equal to it, and one compaction through LDS puts them in slot order (logit
 // descending, equal logits -> lower expert index). The gate weights are the
 // softmax over the selected logits, summed in slot order, or the sigmoid of
-// each selected logit (TileScale PR #70, Design: routing precedes the expert
+// each selected logit, both in double precision and rounded once to fp32 (TileScale PR #70, Design: routing precedes the expert
 // GEMMs; the renormalised top-k softmax equals a softmax over the k selected
 // logits).
 #include "moe_common.cuh"
@@ -118,15 +118,21 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void route_kernel(const float*
     my_v = s_v[wib][lane];
   }
 
+  // The weights are evaluated in double precision and rounded once to fp32:
+  // the difference of two fp32 logits is exact in double, and the double
+  // exp / sum / division err by a few units in 2^-53, so the fp32 result is
+  // the correctly rounded weight except within that distance of a rounding
+  // midpoint. (k exponentials per token; the kernel is bound by its logit
+  // reads, not by this arithmetic.)
   float wj;
   if (score == 0) {
-    const float l0 = __shfl(my_v, 0);
-    const float z = lane < k ? expf(my_v - l0) : 0.0f;
-    float sum = 0.0f;
+    const double l0 = static_cast<double>(__shfl(my_v, 0));
+    const double z = lane < k ? exp(static_cast<double>(my_v) - l0) : 0.0;
+    double sum = 0.0;
     for (int j = 0; j < k; ++j) sum += __shfl(z, j);
-    wj = __fdiv_rn(z, sum);
+    wj = static_cast<float>(z / sum);
   } else {
-    wj = __fdiv_rn(1.0f, 1.0f + expf(-my_v));
+    wj = static_cast<float>(1.0 / (1.0 + exp(-static_cast<double>(my_v))));
   }
   // slots k .. k + n_shared - 1: the shared experts E .. E + n_shared - 1, weight 1
   const int kk = k + n_shared;

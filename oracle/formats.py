@@ -17,9 +17,10 @@ format definitions, not from any GPU conversion instruction:
   2^(byte-127); byte 255 is NaN and is never produced here.
 
 The pages that describe the method fix only the format names (FP8 E4M3 with
-FP32 per-128 scales in the Design section of TileScale PR #70; MXFP4 weights
-with K32 scaling and FP8 activations in the Benchmark configuration of
-FlashInfer PR #6465); the bit-level rules above come from the OCP documents.
+FP32 per-128 scales in the Design section of TileScale PR #70; E2M1 weights
+sharing one scale per 32 K elements against E4M3 activations in the
+Benchmark configuration of FlashInfer PR #6465); the bit-level rules above
+come from the OCP documents.
 """
 from __future__ import annotations
 

@@ -210,7 +210,7 @@ def quantize_mxfp8(v: np.ndarray):
 def quantize_mxfp4(v: np.ndarray):
     """MXFP4 along the last axis: E2M1 elements, one E8M0 scale per 32.
 
-    [FI6465] Benchmark configuration: MXFP4 weights with K32 scaling.
+    [FI6465] Benchmark configuration (E2M1 weights, one shared scale per 32 along K).
     Rule: OCP MX v1.0 (emax_elem = 2). Two codes per byte, even column in the
     low nibble. v: [R, C], C % 32 == 0.
     Returns packed uint8 [R, C/2], e8m0 uint8 [R, C/32].
@@ -462,6 +462,112 @@ def route_backward(w: np.ndarray, ids: np.ndarray, dw: np.ndarray, E: int, score
     return F.round_fp32(dl).astype(np.float32)
 
 
+def _row_layout(sorted_ids, tile_expert, num_tiles: int, block_m: int, A: int):
+    """Sorted rows r < num_tiles * block_m: assignment ids, real-row mask and
+    the expert of each row."""
+    rows = num_tiles * block_m
+    srt = np.asarray(sorted_ids[:rows], np.int64)
+    real = srt < A
+    e_of = np.repeat(np.asarray(tile_expert[:num_tiles], np.int64), block_m)
+    return rows, srt, real, e_of
+
+
+def _per_expert(e_of, E: int, rows: int, out_cols: int, f):
+    """Rows of expert e (e_of == e) filled by f(e, sel); other rows 0."""
+    out = np.zeros((rows, out_cols))
+    for e in range(E):
+        sel = e_of == e
+        if sel.any():
+            out[sel] = f(e, sel)
+    return out
+
+
+def gate_up_rows(x, w1, sorted_ids, tile_expert, num_tiles: int, block_m: int, kk: int):
+    """GEMM1 of the backward's saved forward, per sorted row: the token row x[a // kk]
+    (0 for pad rows) against its expert's gate rows W1[e, :I] and up rows
+    W1[e, I:]. Returns (xs, g, u): the gathered rows and both projections, float64."""
+    x = np.asarray(x, np.float64)
+    w1 = np.asarray(w1, np.float64)
+    E, twoI, _ = w1.shape
+    I = twoI // 2
+    rows, srt, real, e_of = _row_layout(sorted_ids, tile_expert, num_tiles, block_m, x.shape[0] * kk)
+    tok = np.where(real, srt // kk, 0)
+    xs = np.where(real[:, None], x[tok], 0.0)                       # gathered tokens, sorted rows
+    g = _per_expert(e_of, E, rows, I, lambda e, sel: xs[sel] @ w1[e, :I].T)
+    u = _per_expert(e_of, E, rows, I, lambda e, sel: xs[sel] @ w1[e, I:].T)
+    return xs, g, u
+
+
+def combine_backward(dout, w, y, sorted_ids, num_tiles: int, block_m: int, exact: bool = False):
+    """Backward of the weighted combine out[t] = sum_j w[t, j] y[t*kk + j]:
+    dY of each sorted row, dy[r] = bf16(w[a] * dout[a // kk]) (0 for pad rows),
+    and the gate-weight gradient dw[t, j] = sum_c dout[t, c] y[t*kk + j, c] (float64).
+    w: [T, kk]; y: [T*kk, H] in assignment order."""
+    rb = (lambda v: np.asarray(v, np.float64)) if exact else F.round_bf16
+    dout = np.asarray(dout, np.float64)
+    y = np.asarray(y, np.float64)
+    T, kk = np.asarray(w).shape
+    A = T * kk
+    rows = num_tiles * block_m
+    srt = np.asarray(sorted_ids[:rows], np.int64)
+    real = srt < A
+    tok = np.where(real, srt // kk, 0)
+    wa = np.asarray(w, np.float64).reshape(A)
+    dy = np.where(real[:, None], rb(wa[np.where(real, srt, 0)][:, None] * dout[tok]), 0.0)
+    dw = (dout[np.arange(A) // kk] * y).sum(axis=1).reshape(T, kk)
+    return dy, dw
+
+
+def swiglu_backward(dy, w2, gu, tile_expert, num_tiles: int, block_m: int, exact: bool = False):
+    """Gradient through GEMM2 and the SwiGLU, per sorted row of expert e:
+    dh = dy @ W2[e] (float64); with (g, u) the saved pre-activations gu[r]
+    and s = sigmoid(g): dgu = bf16([dh u s (1 + g (1 - s)), dh g s])."""
+    rb = (lambda v: np.asarray(v, np.float64)) if exact else F.round_bf16
+    dy = np.asarray(dy, np.float64)
+    w2 = np.asarray(w2, np.float64)
+    gu = np.asarray(gu, np.float64)
+    E, H, I = w2.shape
+    rows = num_tiles * block_m
+    e_of = np.repeat(np.asarray(tile_expert[:num_tiles], np.int64), block_m)
+    g_s, u_s = gu[:rows, :I], gu[:rows, I:]
+    dh = _per_expert(e_of, E, rows, I, lambda e, sel: dy[sel] @ w2[e])
+    sg = 1.0 / (1.0 + np.exp(-g_s))
+    dg = dh * u_s * sg * (1.0 + g_s * (1.0 - sg))
+    du = dh * g_s * sg
+    return rb(np.concatenate([dg, du], axis=1))
+
+
+def dx_rows_backward(dgu, w1, sorted_ids, tile_expert, num_tiles: int, block_m: int, A: int,
+                     exact: bool = False):
+    """Gradient through GEMM1 to each assignment's row: dx_rows[a] =
+    bf16(dgu[r] @ W1[e]) for the sorted row r of assignment a, in assignment
+    order [A, H]."""
+    rb = (lambda v: np.asarray(v, np.float64)) if exact else F.round_bf16
+    dgu = np.asarray(dgu, np.float64)
+    w1 = np.asarray(w1, np.float64)
+    E, _, H = w1.shape
+    rows, srt, real, e_of = _row_layout(sorted_ids, tile_expert, num_tiles, block_m, A)
+    dx_sorted = rb(_per_expert(e_of, E, rows, H, lambda e, sel: dgu[sel] @ w1[e]))
+    dx_rows = np.zeros((A, H))
+    dx_rows[srt[real]] = dx_sorted[real]
+    return dx_rows
+
+
+def weight_grad(p_rows, q_rows, sorted_ids, tile_expert, num_tiles: int, block_m: int, A: int, E: int):
+    """Per-expert weight gradient over the expert's real sorted rows:
+    dW[e] = sum_r q_rows[r]^T p_rows[r] (float64) [E, N, M]; dW2 takes
+    p = h, q = dy; dW1 takes p = the gathered token rows, q = dgu."""
+    p_rows = np.asarray(p_rows, np.float64)
+    q_rows = np.asarray(q_rows, np.float64)
+    rows, srt, real, e_of = _row_layout(sorted_ids, tile_expert, num_tiles, block_m, A)
+    dw = np.zeros((E, q_rows.shape[1], p_rows.shape[1]))
+    for e in range(E):
+        sel = (e_of == e) & real
+        if sel.any():
+            dw[e] = q_rows[:rows][sel].T @ p_rows[:rows][sel]
+    return dw
+
+
 def moe_backward(logits, x_bf16, w1_bf16, w2_bf16, dout_bf16, k: int, score: int, block_m: int = 16,
                  n_shared: int = 0, exact: bool = False):
     """Gradients of the BF16 SwiGLU routed forward (moe_forward) for dout.
@@ -479,7 +585,6 @@ def moe_backward(logits, x_bf16, w1_bf16, w2_bf16, dout_bf16, k: int, score: int
     dout = np.asarray(dout_bf16, np.float64)
     T, H = x.shape
     E, twoI, _ = w1.shape
-    I = twoI // 2
     E_routed = E - n_shared
     if n_shared:
         ids, w = route_with_shared(logits, k, score, n_shared)
@@ -488,59 +593,29 @@ def moe_backward(logits, x_bf16, w1_bf16, w2_bf16, dout_bf16, k: int, score: int
     kk = k + n_shared
     A = T * kk
     counts, offsets, sorted_ids, tile_expert, num_tiles = align_sort(ids, E, block_m)
-    rows = num_tiles * block_m
-    srt = sorted_ids[:rows].astype(np.int64)
-    real = srt < A
-    e_of = np.repeat(tile_expert[:num_tiles].astype(np.int64), block_m)
-    tok = np.where(real, srt // kk, 0)
-
-    # every product below runs over one expert's rows at a time: row r of the
-    # sorted layout belongs to expert e_of[r]
-    def per_expert(f, out_cols):
-        out = np.zeros((rows, out_cols))
-        for e in range(E):
-            sel = e_of == e
-            if sel.any():
-                out[sel] = f(e, sel)
-        return out
+    rows, srt, real, e_of = _row_layout(sorted_ids, tile_expert, num_tiles, block_m, A)
 
     # forward, saving what the backward reads
-    xs = np.where(real[:, None], x[tok], 0.0)                       # gathered tokens, sorted rows
-    g = per_expert(lambda e, sel: xs[sel] @ w1[e, :I].T, I)
-    u = per_expert(lambda e, sel: xs[sel] @ w1[e, I:].T, I)
+    xs, g, u = gate_up_rows(x, w1, sorted_ids, tile_expert, num_tiles, block_m, kk)
     h = rb(silu(g) * u)
-    y_sorted = rb(per_expert(lambda e, sel: h[sel] @ w2[e].T, H))
+    y_sorted = rb(_per_expert(e_of, E, rows, H, lambda e, sel: h[sel] @ w2[e].T))
     y = np.zeros((A, H))
     y[srt[real]] = y_sorted[real]
-    g_s, u_s = rb(g), rb(u)                                         # saved pre-activations
+    gu = np.concatenate([rb(g), rb(u)], axis=1)                     # saved pre-activations
 
-    # combine backward
-    wa = np.asarray(w, np.float64).reshape(A)
-    dy = np.where(real[:, None], rb(wa[np.where(real, srt, 0)][:, None] * dout[tok]), 0.0)
-    dw = (dout[np.arange(A) // kk] * y).sum(axis=1).reshape(T, kk)
+    # combine backward, router backward
+    dy, dw = combine_backward(dout, w, y, sorted_ids, num_tiles, block_m, exact)
     dw32 = F.round_fp32(dw).astype(np.float32)
     dlogits = route_backward(w[:, :k], ids[:, :k], dw[:, :k], E_routed, score)
-
-    # GEMM2 backward: dh and the SwiGLU backward; dW2
-    dh = per_expert(lambda e, sel: dy[sel] @ w2[e], I)
-    sg = 1.0 / (1.0 + np.exp(-g_s))
-    dg = dh * u_s * sg * (1.0 + g_s * (1.0 - sg))
-    du = dh * g_s * sg
-    dgu = rb(np.concatenate([dg, du], axis=1))
-    dw2 = np.zeros_like(w2)
-    dw1 = np.zeros_like(w1)
-    for e in range(E):
-        sel = (e_of == e) & real
-        if sel.any():
-            dw2[e] = dy[sel].T @ h[sel]
-            dw1[e] = dgu[sel].T @ xs[sel]
-    # GEMM1 backward: dx rows per assignment, then the sum over each token's slots
-    dx_sorted = rb(per_expert(lambda e, sel: dgu[sel] @ w1[e], H))
-    dx_rows = np.zeros((A, H))
-    dx_rows[srt[real]] = dx_sorted[real]
+    # GEMM2 backward through the SwiGLU; the weight gradients; GEMM1 backward
+    # to the dx rows, then the sum over each token's slots
+    dgu = swiglu_backward(dy, w2, gu, tile_expert, num_tiles, block_m, exact)
+    dw2 = weight_grad(h, dy, sorted_ids, tile_expert, num_tiles, block_m, A, E)
+    dw1 = weight_grad(xs, dgu, sorted_ids, tile_expert, num_tiles, block_m, A, E)
+    dx_rows = dx_rows_backward(dgu, w1, sorted_ids, tile_expert, num_tiles, block_m, A, exact)
     dx = rb(dx_rows.reshape(T, kk, H).sum(axis=1))
     f32 = (lambda v: v) if exact else (lambda v: F.round_fp32(v))
     return {"ids": ids, "w": w, "sorted_ids": sorted_ids, "tile_expert": tile_expert, "num_tiles": num_tiles,
-            "gu": np.concatenate([g_s, u_s], axis=1), "h": h, "y": y,
+            "gu": gu, "h": h, "y": y,
             "dy": dy, "dw": dw32, "dlogits": dlogits, "dgu": dgu, "dx_rows": dx_rows, "dx": dx,
             "dw1": f32(dw1), "dw2": f32(dw2)}
