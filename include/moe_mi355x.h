@@ -165,6 +165,26 @@ moe_status_t moe_align_sort(const int32_t* topk_ids, int64_t T, int32_t k, int32
                             void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_align_sort_noalloc -- moe_align_sort for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same kernels and the same outputs, bit for bit,
+ * with the workspace taken from a fixed scratch array the library holds in
+ * device memory, one per GPU (2 MiB, kept until the process ends). The call
+ * allocates nothing.
+ *
+ * Arguments, outputs and errors as moe_align_sort without ws / ws_bytes.
+ * Limit: T * k <= MOE_NOALLOC_MAX_ASSIGNMENTS (with any E <=
+ * MOE_MAX_EXPERTS); larger problems return MOE_ERR_WORKSPACE and enqueue
+ * nothing. Every call on one GPU shares that GPU's scratch: calls that
+ * overlap in time on one GPU (two streams, or two host threads) race and
+ * must be serialised by the caller; calls ordered on one stream are safe.
+ */
+#define MOE_NOALLOC_MAX_ASSIGNMENTS 262144
+moe_status_t moe_align_sort_noalloc(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, int32_t block_m,
+                                    int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
+                                    int32_t* tile_expert, int32_t* num_tiles, void* stream);
+
+/*
  * moe_quantize_fp8 -- bf16 -> FP8 E4M3 (OCP "E4M3FN", max 448) with one fp32
  * scale per block_rows x 128 block. TileScale PR #70, Design (FP8 E4M3 with
  * FP32 per-128 scales). Per block: amax = max|v|; s = fp32(amax / 448)

@@ -21,6 +21,7 @@ MOE_ERR_INVALID_ARG = 1
 MOE_ERR_UNSUPPORTED_SHAPE = 2
 MOE_ERR_WORKSPACE = 3
 MOE_ERR_DEVICE = 4
+MOE_NOALLOC_MAX_ASSIGNMENTS = 262144     # include/moe_mi355x.h: T * k limit of moe_align_sort_noalloc
 
 DTYPE_BF16 = 0
 DTYPE_FP8_BLOCK128 = 1
@@ -39,6 +40,7 @@ SIGNATURES = {
     "moe_sorted_capacity": (_I64, [_I64, _I32, _I32, _I32]),
     "moe_align_sort_workspace_bytes": (_SZ, [_I64, _I32, _I32]),
     "moe_align_sort": (_I32, [_P, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_align_sort_noalloc": (_I32, [_P, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P]),
     "moe_quantize_fp8": (_I32, [_P, _I64, _I64, _I32, _P, _P, _P]),
     "moe_quantize_mxfp8": (_I32, [_P, _I64, _I64, _P, _P, _P]),
     "moe_quantize_mxfp4": (_I32, [_P, _I64, _I64, _P, _P, _P]),
@@ -236,6 +238,19 @@ def moe_align_sort(topk_ids: torch.Tensor, E: int, block_m: int, out: Optional[S
     _check("moe_align_sort", lib().moe_align_sort(
         _p(topk_ids), T, k, E, block_m, _p(out.counts), _p(out.offsets), _p(out.sorted_ids),
         _p(out.tile_expert), _p(out.num_tiles), _p(out.ws), out.ws_bytes, _s(stream)))
+    return out
+
+
+def moe_align_sort_noalloc(topk_ids: torch.Tensor, E: int, block_m: int, out: SortResult, stream=None) -> SortResult:
+    """moe_align_sort with the library's fixed scratch instead of a workspace
+    (no device allocation in the call; `out` must be prepared beforehand)."""
+    _need(topk_ids, torch.int32, "topk_ids")
+    T, k = topk_ids.shape
+    if (out.T, out.k, out.E, out.block_m) != (T, k, E, block_m):
+        raise ValueError("moe_align_sort_noalloc: the SortResult was made for another problem")
+    _check("moe_align_sort_noalloc", lib().moe_align_sort_noalloc(
+        _p(topk_ids), T, k, E, block_m, _p(out.counts), _p(out.offsets), _p(out.sorted_ids),
+        _p(out.tile_expert), _p(out.num_tiles), _s(stream)))
     return out
 
 

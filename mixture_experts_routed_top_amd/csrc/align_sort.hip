@@ -19,6 +19,8 @@
 //      queue (tile -> expert, -1 past the last tile).
 // Nothing depends on the order of atomic operations, so the output is the
 // stable order by (expert, assignment) on every run.
+#include <mutex>
+
 #include "moe_common.cuh"
 #include "moe_launch.h"
 
@@ -208,7 +210,35 @@ int bits_for(int E) {
   return b;
 }
 
+constexpr int64_t kNoAllocWords = (kNoAllocMaxA + kAlignChunk - 1) / kAlignChunk * kMaxE + kNoAllocMaxA;
+
 }  // namespace
+
+// Fixed scratch for callers that cannot allocate (moe_align_sort_noalloc):
+// the workspace of up to kNoAllocMaxA assignments over kMaxE experts, in a
+// file-scope device array. Each GPU the library runs on holds its own copy
+// (2 MiB) until the process ends; every call on that GPU shares it. Its
+// contents need no clearing: the counting pass writes every word a call
+// reads before the later passes read it.
+static __device__ __align__(256) int32_t scratch[kNoAllocWords];
+
+size_t align_sort_scratch_bytes() { return static_cast<size_t>(kNoAllocWords) * sizeof(int32_t); }
+
+// Device address of this GPU's scratch array. In host code `scratch` is only a
+// host-side handle of the symbol, not a device address: the address is looked
+// up once per device, with that device current, and kept.
+hipError_t align_sort_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::once_flag once[kMaxDevices];
+  static void* addr[kMaxDevices];
+  static hipError_t err[kMaxDevices];
+  int d = -1;
+  if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(once[d], [d] { err[d] = hipGetSymbolAddress(&addr[d], HIP_SYMBOL(scratch)); });
+  if (err[d] != hipSuccess) return err[d];
+  *ptr = addr[d];
+  return hipSuccess;
+}
 
 size_t align_sort_ws_bytes(int64_t T, int k, int E) {
   const int64_t A = T * k;

@@ -201,6 +201,31 @@ moe_status_t moe_align_sort(const int32_t* topk_ids, int64_t T, int32_t k, int32
                                          static_cast<hipStream_t>(stream)));
 }
 
+moe_status_t moe_align_sort_noalloc(const int32_t* topk_ids, int64_t T, int32_t k, int32_t E, int32_t block_m,
+                                    int32_t* counts, int32_t* offsets, int32_t* sorted_ids, int32_t* tile_expert,
+                                    int32_t* num_tiles, void* stream) {
+  if (T < 0 || E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > E || k > MOE_MAX_TOPK)
+    return MOE_ERR_INVALID_ARG;
+  if (!valid_block_m(block_m)) return MOE_ERR_INVALID_ARG;
+  if (T > (int64_t{1} << 31) / k) return MOE_ERR_INVALID_ARG;
+  const int64_t cap = capacity(T, k, E, block_m);
+  if (cap >= (int64_t{1} << 31)) return MOE_ERR_INVALID_ARG;
+  // the fixed scratch covers MOE_NOALLOC_MAX_ASSIGNMENTS assignments
+  if (T * k > MOE_NOALLOC_MAX_ASSIGNMENTS) return MOE_ERR_WORKSPACE;
+  if (moe::align_sort_ws_bytes(T, k, E) > moe::align_sort_scratch_bytes()) return MOE_ERR_WORKSPACE;
+  if (T == 0) return MOE_OK;
+  if (!topk_ids || !counts || !offsets || !sorted_ids || !tile_expert || !num_tiles) return MOE_ERR_INVALID_ARG;
+  if (!aligned(topk_ids, 4) || !aligned(counts, 4) || !aligned(offsets, 4) || !aligned(sorted_ids, 4) ||
+      !aligned(tile_expert, 4) || !aligned(num_tiles, 4))
+    return MOE_ERR_INVALID_ARG;
+  moe::DeviceInfo dev;
+  if (moe_status_t st = current_device(&dev)) return st;
+  void* ws = nullptr;
+  if (moe::align_sort_scratch(&ws) != hipSuccess || ws == nullptr) return MOE_ERR_DEVICE;
+  return launched(moe::launch_align_sort(topk_ids, T, k, E, block_m, counts, offsets, sorted_ids,
+                                         tile_expert, num_tiles, cap, ws, static_cast<hipStream_t>(stream)));
+}
+
 moe_status_t moe_quantize_fp8(const uint16_t* in, int64_t rows, int64_t cols, int32_t block_rows,
                               uint8_t* q, float* scale, void* stream) {
   if (rows < 0 || cols < 0 || (block_rows != 1 && block_rows != 128)) return MOE_ERR_INVALID_ARG;

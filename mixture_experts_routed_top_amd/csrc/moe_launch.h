@@ -19,6 +19,11 @@ hipError_t launch_route(const float* logits, int64_t T, int E, int k, int score,
 // align_sort: chunked, deterministic counting sort (see align_sort.hip).
 constexpr int kAlignChunk = 1024;          // assignments per chunk of the counting pass
 size_t align_sort_ws_bytes(int64_t T, int k, int E);
+// The fixed align_sort scratch (no allocation): assignments it covers, its
+// size, and this device's address of it (looked up once per device).
+constexpr int64_t kNoAllocMaxA = int64_t{1} << 18;
+size_t align_sort_scratch_bytes();
+hipError_t align_sort_scratch(void** ptr);
 hipError_t launch_align_sort(const int32_t* ids, int64_t T, int k, int E, int block_m,
                              int32_t* counts, int32_t* offsets, int32_t* sorted_ids,
                              int32_t* tile_expert, int32_t* num_tiles, int64_t cap,
