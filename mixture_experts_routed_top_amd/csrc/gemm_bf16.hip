@@ -72,10 +72,12 @@ struct Cfg {
   static constexpr int T_BYTES = BM * 128, W_BYTES = B_ROWS * 128;
   static constexpr int T_GROUPS = BM / 8, W_GROUPS = B_ROWS / 8;
   static constexpr int GPW_T = T_GROUPS / WAVES;       // token loads per wave per k-step
-  static constexpr int GPW = GPW_T + W_GROUPS / WAVES;  // loads per wave per k-step
+  static constexpr int GPW_W = W_GROUPS / WAVES;       // weight loads per wave per k-step
+  static constexpr int GPW = GPW_T + GPW_W;            // loads per wave per k-step
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile is a multiple of 32");
   static_assert(BM % 8 == 0 && T_GROUPS % WAVES == 0 && W_GROUPS % WAVES == 0, "uniform loads per wave");
   static_assert(2 * T_BYTES + 3 * W_BYTES <= 160 * 1024, "the split stages fit in LDS");
+  static_assert(BN % (GPW_W * 8) == 0, "a wave's weight rows lie in one half (gate or up)");
 };
 
 // The XOR swizzle of the 16-byte chunks of LDS row `row`: row & 7, which
@@ -211,6 +213,18 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
   // that the LDS destinations and descriptors of the loads are scalar too
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WN, wn = wave % WN;
+  // LDS byte offsets of this lane's MFMA fragments in substep kk of a k-step:
+  // row wm * TM + lane % 32 (token) or wn * TN + lane % 32 (weight) at chunk
+  // 2 kk + lane / 32. Fragment rows start at multiples of 32, so every
+  // fragment row of a lane has the swizzle lane & 7 and the other fragments
+  // of the substep sit at compile-time offsets (32-row steps) from these.
+  uint32_t xo_t[Cfg<BM, BN, WM, WN, GEMM1, ACT>::BK / 16], xo_w[Cfg<BM, BN, WM, WN, GEMM1, ACT>::BK / 16];
+#pragma unroll
+  for (int kk = 0; kk < Cfg<BM, BN, WM, WN, GEMM1, ACT>::BK / 16; ++kk) {
+    const uint32_t cb = static_cast<uint32_t>(((kk * 2 + (lane >> 5)) ^ (lane & 7)) << 4);
+    xo_t[kk] = static_cast<uint32_t>((wm * Cfg<BM, BN, WM, WN, GEMM1, ACT>::TM + (lane & 31)) * 128) + cb;
+    xo_w[kk] = static_cast<uint32_t>((wn * Cfg<BM, BN, WM, WN, GEMM1, ACT>::TN + (lane & 31)) * 128) + cb;
+  }
   const int N = GEMM1 ? p.I : p.H;      // output columns
   const int K = GEMM1 ? p.H : p.I;      // reduction length
   const int ntn = (N + BN - 1) / BN;
@@ -251,74 +265,67 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
     const int wrows = GEMM1 ? C::HALVES * p.I : p.H;   // weight rows of one expert
     const __amdgpu_buffer_rsrc_t b_rsrc =
         make_rsrc(p.w + static_cast<int64_t>(e) * wrows * K, static_cast<uint32_t>(wrows) * K * 2);
-    // byte offset of the start of LDS row `row`'s source row: a token row
-    // (gathered by sorted id in GEMM1) or a weight row of expert e; kOob for
-    // pad rows, rows past N and rows past the tile
-    // (`sid`: the sorted id of a GEMM1 token row, loaded beforehand)
-    auto row_src = [&](int row, int sid) -> uint32_t {
-      if (row >= BM + C::B_ROWS) return kOob;
-      if (row < BM) {
-        int64_t src_row = -1;
+    // This lane's place in every direct-to-LDS load: a load fills 8 LDS rows
+    // (1 KB), lane l physical chunk l % 8 of row l / 8 of the group, and the
+    // swizzle is row & 7, so every row this lane fills holds the same logical
+    // chunk lc: one K column for all of the lane's loads. Keeping the per-load
+    // bookkeeping to one offset per gathered token row (and none per weight
+    // row) is what keeps the large tiles free of register spills.
+    const int lc = g_pc ^ g_row;
+    const int kcol = lc * 8;
+    // token rows: GEMM1 gathers them by sorted id (every id this lane needs is
+    // loaded before any is used, so the loads overlap), GEMM2 reads the sorted
+    // rows in place; toff = byte offset of this lane's chunk of each token row
+    // it fills (kOob for pad rows)
+    uint32_t toff[C::GPW_T];
+    {
+      int sid[C::GPW_T];
+#pragma unroll
+      for (int q = 0; q < C::GPW_T; ++q)
+        sid[q] = GEMM1 ? p.sorted_ids[row0 + (wave * C::GPW_T + q) * 8 + g_row] : 0;
+#pragma unroll
+      for (int q = 0; q < C::GPW_T; ++q) {
+        int64_t src = -1;
         if (GEMM1) {
-          if (sid < p.A) src_row = sid / p.k;
+          if (sid[q] < p.A) src = sid[q] / p.k;
         } else {
-          src_row = row0 + row;
+          src = row0 + (wave * C::GPW_T + q) * 8 + g_row;
         }
-        return src_row < 0 ? kOob : static_cast<uint32_t>(src_row * K * 2);
+        toff[q] = src < 0 ? kOob : static_cast<uint32_t>(src * K * 2 + lc * 16);
       }
-      const int br = row - BM;
-      int n, wrow;
-      if (GEMM1) {
-        const int half = br >= BN ? 1 : 0;
-        n = n0 + br - half * BN;
-        wrow = half * p.I + n;
-      } else {
-        n = n0 + br;
-        wrow = n;
-      }
-      return n < N ? static_cast<uint32_t>(wrow) * K * 2 : kOob;
-    };
-    uint32_t off[C::GPW];
-    int kcol[C::GPW];                                   // first K column of this lane's chunk
-    // load q of this wave fills the 8 LDS rows of group grp_of(q): in the
-    // split pipeline the first GPW_T are token groups, the rest weight groups
-    // (numbered from the first weight row)
-    auto grp_of = [&](int q) -> int {
-      return q < C::GPW_T ? wave * C::GPW_T + q : wave * (C::GPW - C::GPW_T) + (q - C::GPW_T);
-    };
-    auto row_of = [&](int q) -> int { return grp_of(q) * 8 + g_row + (q >= C::GPW_T ? BM : 0); };
-    // GEMM1 gathers its token rows by sorted id: every id this lane needs is
-    // loaded before any is used, so the loads overlap instead of each one
-    // waiting for the last (a weight row loads a harmless id too)
-    int sid[C::GPW];
-#pragma unroll
-    for (int q = 0; q < C::GPW; ++q) {
-      const int row = row_of(q);
-      sid[q] = GEMM1 ? p.sorted_ids[row0 + (row < BM ? row : 0)] : 0;
     }
+    // weight rows: a wave's groups are consecutive rows of one half (gate or
+    // up; BN is a multiple of the rows one wave loads), 8 rows apart; rows at
+    // or past column N read as zeros
+    const int br0 = wave * C::GPW_W * 8;                       // the wave's first weight row (uniform)
+    const int half = C::HALVES == 2 && br0 >= BN ? 1 : 0;
+    const int nfirst = n0 + br0 - half * BN + g_row;           // output column of the lane's first row
+    uint32_t woff[C::GPW_W];
 #pragma unroll
-    for (int q = 0; q < C::GPW; ++q) {
-      const int row = row_of(q);
-      const int lc = g_pc ^ swz(row);                   // logical chunk stored at this place
-      kcol[q] = lc * 8;
-      const uint32_t base = row_src(row, sid[q]);
-      off[q] = base == kOob ? kOob : base + lc * 16;
-    }
+    for (int q = 0; q < C::GPW_W; ++q)
+      woff[q] = nfirst + q * 8 < N ? static_cast<uint32_t>(half * p.I + nfirst + q * 8) * K * 2 + lc * 16 : kOob;
     // split pipeline: the token loads of k-step kt into `tb`, the weight loads into `wb`
     auto load_t = [&](char* tb, int kt) {
       const uint32_t soff = static_cast<uint32_t>(kt) * BK * 2;
+      // past K every chunk reads zeros: every offset here is below kOob (the
+      // operands stay under 2 GiB), so max() with kOob is the out-of-range
+      // offset (a plain max: the compiler branches around the loads on a select)
+      const uint32_t klim = kt * BK + kcol < K ? 0u : kOob;
 #pragma unroll
       for (int q = 0; q < C::GPW_T; ++q) {
-        const uint32_t o = kt * BK + kcol[q] < K ? off[q] : kOob;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr_t)(tb + grp_of(q) * 1024), 16, o, soff, 0, 0);
+        const uint32_t o = __builtin_elementwise_max(toff[q], klim);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr_t)(tb + (wave * C::GPW_T + q) * 1024), 16, o, soff,
+                                                 0, 0);
       }
     };
     auto load_w = [&](char* wb, int kt) {
       const uint32_t soff = static_cast<uint32_t>(kt) * BK * 2;
+      const uint32_t klim = kt * BK + kcol < K ? 0u : kOob;
 #pragma unroll
-      for (int q = C::GPW_T; q < C::GPW; ++q) {
-        const uint32_t o = kt * BK + kcol[q] < K ? off[q] : kOob;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lds_ptr_t)(wb + grp_of(q) * 1024), 16, o, soff, 0, 0);
+      for (int q = 0; q < C::GPW_W; ++q) {
+        const uint32_t o = __builtin_elementwise_max(woff[q], klim);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lds_ptr_t)(wb + (wave * C::GPW_W + q) * 1024), 16, o, soff,
+                                                 0, 0);
       }
     };
 
@@ -336,15 +343,18 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
     // `tbase`: the k-step's token rows; `wbase`: its weight rows
     auto compute = [&](const char* tbase, const char* wbase) {
       bf16x8 xf[2][C::FM], wf[2][C::HALVES][C::FN];
+      // fragment row (32 i + lane % 32 of the wave's rows) at its substep's
+      // chunk: the per-lane part xo_t / xo_w[kk] plus a compile-time offset
       auto read_frags = [&](int kk, int buf) {
-        const int ch = kk * 2 + (lane >> 5);
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i) xf[buf][i] = lds_frag(tbase, wm * C::TM + i * 32 + (lane & 31), ch);
+        for (int i = 0; i < C::FM; ++i)
+          xf[buf][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(tbase + xo_t[kk] + i * 32 * 128));
 #pragma unroll
         for (int h = 0; h < C::HALVES; ++h)
 #pragma unroll
           for (int j = 0; j < C::FN; ++j)
-            wf[buf][h][j] = lds_frag(wbase, h * BN + wn * C::TN + j * 32 + (lane & 31), ch);
+            wf[buf][h][j] = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const uint4*>(wbase + xo_w[kk] + (h * BN + j * 32) * 128));
       };
       read_frags(0, 0);
 #pragma unroll
@@ -470,6 +480,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
             }
           }
         }
+        // finish this block's accumulators before the next block's are read:
+        // with the accumulators in AGPRs (four-wave tiles), reading them all
+        // at once would need every VGPR and spill the task's load offsets
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     if constexpr (FUSE) fused_combine<BM, BN, C::THREADS>(p, row0, nt, ntn, N, reinterpret_cast<int32_t*>(stage1));
