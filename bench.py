@@ -533,14 +533,14 @@ def _stage_fns(layer, plan, x, logits):
         a, a_s = x, None
     gemm1 = M.moe_grouped_gemm_swiglu if layer.act == M.ACT_SWIGLU else M.moe_grouped_gemm_relu2
     fns.append((GEMM1_STAGE[layer.act], lambda: gemm1(d, a, a_s, layer.w1, layer.w1_scale, plan.sort,
-                                                      layer.H, layer.I, plan.h, plan.h_scale)))
+                                                      layer.H, layer.I, plan.h, plan.h_scale, ws=plan.ws)))
     if layer.fused_combine:
         fns.append(("gemm2_down_combine", lambda: M.moe_grouped_gemm_down_combine(
             d, plan.h, plan.h_scale, layer.w2, layer.w2_scale, plan.sort, layer.H, layer.I, plan.w, plan.counters,
             plan.y, plan.out)))
         return fns
     fns.append(("gemm2_down", lambda: M.moe_grouped_gemm_down(d, plan.h, plan.h_scale, layer.w2, layer.w2_scale,
-                                                                plan.sort, layer.H, layer.I, plan.y)))
+                                                                plan.sort, layer.H, layer.I, plan.y, ws=plan.ws)))
     fns.append(("combine", lambda: M.moe_combine(plan.y, plan.w, plan.out)))
     return fns
 

@@ -114,8 +114,8 @@ moe_status_t moe_route_shared(const float* logits, int64_t T, int32_t E, int32_t
  * moe_pick_block_m -- host only. The tile height (rows per tile of the
  * expert-sorted layout) this library's kernels use for a problem, from the
  * mean number of rows per expert (the adaptive token-tile geometry named in
- * the Abstract of "GC-MoE on SM120"). Returns a value in {16, 32, 64, 128,
- * 256}, or -1 for invalid arguments.
+ * the Abstract of "GC-MoE on SM120"). Returns a value in {32, 64, 128, 256}
+ * (every tile height the grouped GEMMs take), or -1 for invalid arguments.
  */
 int32_t moe_pick_block_m(int32_t dtype, int64_t T, int32_t k, int32_t E, int32_t H, int32_t I);
 
@@ -154,7 +154,9 @@ size_t moe_align_sort_workspace_bytes(int64_t T, int32_t k, int32_t E);
  *   ws          device workspace of at least
  *               moe_align_sort_workspace_bytes(T, k, E) bytes (contents
  *               undefined on entry and exit).
- * The result is deterministic (no dependence on atomic ordering).
+ * The result is deterministic (no dependence on atomic ordering). block_m 16
+ * gives a valid layout, but the grouped GEMMs take 32, 64, 128 or 256 only
+ * (they return MOE_ERR_UNSUPPORTED_SHAPE for 16).
  * Errors: MOE_ERR_INVALID_ARG (block_m not in {16, 32, 64, 128, 256}),
  * MOE_ERR_WORKSPACE, MOE_ERR_DEVICE. Expert ids outside [0, E) are not
  * detected on the device: the caller guarantees them (moe_route does).
@@ -256,6 +258,18 @@ moe_status_t moe_quantize_mxfp4(const uint16_t* in, int64_t rows, int64_t cols,
  * I % 128 == 0; MX needs H % 128 == 0 and I % 128 == 0
  * (else MOE_ERR_UNSUPPORTED_SHAPE). block_m must be one this dtype's kernels
  * support (moe_pick_block_m returns one), else MOE_ERR_UNSUPPORTED_SHAPE.
+ *
+ * ws, ws_bytes: optional device workspace (NULL: none) of at least
+ * moe_grouped_gemm_workspace_bytes() bytes, 256-byte aligned. Its first 4096
+ * bytes are counters: zero them before the first use; every call that
+ * completes leaves them zero again (the rest holds partial sums and needs no
+ * clearing). With
+ * it, the BF16 kernels balance their last round of tiles by splitting those
+ * tiles' K sum in two halves computed by two workgroups and added in fp32
+ * (a different summation order for those tiles; deterministic for a given
+ * problem and device); the FP8 / MX kernels ignore it. Calls that may run at
+ * the same time need workspaces of their own. ws_bytes too small ->
+ * MOE_ERR_WORKSPACE; misaligned -> MOE_ERR_INVALID_ARG.
  */
 moe_status_t moe_grouped_gemm_swiglu(int32_t dtype, const void* x, const void* x_scale,
                                      const void* w1, const void* w1_scale,
@@ -263,7 +277,17 @@ moe_status_t moe_grouped_gemm_swiglu(int32_t dtype, const void* x, const void* x
                                      const int32_t* num_tiles,
                                      int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
                                      int32_t block_m, int64_t cap,
-                                     void* h, void* h_scale, void* stream);
+                                     void* h, void* h_scale, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_grouped_gemm_workspace_bytes -- host only. Bytes of the optional
+ * workspace of the grouped GEMM calls on the current device: a counter per
+ * split slot and two 256 x 256 fp32 partial tiles per slot, one slot per two
+ * workgroups of the persistent grid (64 MiB on a 256-CU MI355X). Returns 0
+ * when no supported device is current. Not a passage of the pages: the
+ * work-balance split is this implementation's.
+ */
+size_t moe_grouped_gemm_workspace_bytes(void);
 
 /*
  * moe_grouped_gemm_swiglu_h32 -- moe_grouped_gemm_swiglu that also writes
@@ -275,9 +299,9 @@ moe_status_t moe_grouped_gemm_swiglu(int32_t dtype, const void* x, const void* x
  *       into h[r, n] / h_scale (pad rows: 0). Rows past num_tiles * block_m
  *       are not touched.
  * h and h_scale are written exactly as moe_grouped_gemm_swiglu writes them
- * (the same kernels run; only the extra stores are added). Other arguments
- * and errors as moe_grouped_gemm_swiglu; h32 NULL or misaligned ->
- * MOE_ERR_INVALID_ARG.
+ * (the same kernels run; only the extra stores are added; with the same ws
+ * or none alike). Other arguments and errors as moe_grouped_gemm_swiglu; h32
+ * NULL or misaligned -> MOE_ERR_INVALID_ARG.
  */
 moe_status_t moe_grouped_gemm_swiglu_h32(int32_t dtype, const void* x, const void* x_scale,
                                          const void* w1, const void* w1_scale,
@@ -285,7 +309,8 @@ moe_status_t moe_grouped_gemm_swiglu_h32(int32_t dtype, const void* x, const voi
                                          const int32_t* num_tiles,
                                          int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
                                          int32_t block_m, int64_t cap,
-                                         void* h, void* h_scale, float* h32, void* stream);
+                                         void* h, void* h_scale, float* h32, void* ws, size_t ws_bytes,
+                                         void* stream);
 
 /*
  * moe_grouped_gemm_relu2 -- GEMM1 of an ungated expert with the squared-ReLU
@@ -298,8 +323,8 @@ moe_status_t moe_grouped_gemm_swiglu_h32(int32_t dtype, const void* x, const voi
  *   h[r, n] = bf16( max(g, 0)^2 )
  *   BF16 only: x [T, H] bf16; W1 [E, I, H] bf16; h [cap, I] bf16; x_scale,
  *   w1_scale and h_scale are ignored (pass NULL).
- * Errors as for moe_grouped_gemm_swiglu; dtype other than BF16 ->
- * MOE_ERR_UNSUPPORTED_SHAPE.
+ * ws, ws_bytes and errors as for moe_grouped_gemm_swiglu; dtype other than
+ * BF16 -> MOE_ERR_UNSUPPORTED_SHAPE.
  */
 moe_status_t moe_grouped_gemm_relu2(int32_t dtype, const void* x, const void* x_scale,
                                     const void* w1, const void* w1_scale,
@@ -307,7 +332,7 @@ moe_status_t moe_grouped_gemm_relu2(int32_t dtype, const void* x, const void* x_
                                     const int32_t* num_tiles,
                                     int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
                                     int32_t block_m, int64_t cap,
-                                    void* h, void* h_scale, void* stream);
+                                    void* h, void* h_scale, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_grouped_gemm_down -- GEMM2 (down projection) over the sorted rows; the
@@ -325,7 +350,8 @@ moe_status_t moe_grouped_gemm_relu2(int32_t dtype, const void* x, const void* x_
  *   MXFP4W_MXFP8A: h [cap, I] E4M3 + h_scale [cap, I/32] E8M0;
  *                  W2 [E*H, I/2] packed E2M1 + w2_scale [E*H, I/32] E8M0.
  *   y [A, H] bf16, out: every row a < A is written exactly once.
- * Shape rules as for moe_grouped_gemm_swiglu.
+ * Shape rules, ws and ws_bytes as for moe_grouped_gemm_swiglu (GEMM1 and
+ * GEMM2 on one stream may share one workspace).
  */
 moe_status_t moe_grouped_gemm_down(int32_t dtype, const void* h, const void* h_scale,
                                    const void* w2, const void* w2_scale,
@@ -333,7 +359,7 @@ moe_status_t moe_grouped_gemm_down(int32_t dtype, const void* h, const void* h_s
                                    const int32_t* num_tiles,
                                    int64_t T, int32_t H, int32_t I, int32_t E, int32_t k,
                                    int32_t block_m, int64_t cap,
-                                   uint16_t* y, void* stream);
+                                   uint16_t* y, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_down_combine_workspace_bytes -- host only. Bytes of the counter

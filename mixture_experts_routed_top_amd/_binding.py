@@ -45,13 +45,14 @@ SIGNATURES = {
     "moe_quantize_mxfp8": (_I32, [_P, _I64, _I64, _P, _P, _P]),
     "moe_quantize_mxfp4": (_I32, [_P, _I64, _I64, _P, _P, _P]),
     "moe_grouped_gemm_swiglu": (_I32, [_I32, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32,
-                                       _I32, _I64, _P, _P, _P]),
+                                       _I32, _I64, _P, _P, _P, _SZ, _P]),
+    "moe_grouped_gemm_workspace_bytes": (_SZ, []),
     "moe_grouped_gemm_swiglu_h32": (_I32, [_I32, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32,
-                                           _I32, _I64, _P, _P, _P, _P]),
+                                           _I32, _I64, _P, _P, _P, _P, _SZ, _P]),
     "moe_grouped_gemm_relu2": (_I32, [_I32, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32,
-                                      _I32, _I64, _P, _P, _P]),
+                                      _I32, _I64, _P, _P, _P, _SZ, _P]),
     "moe_grouped_gemm_down": (_I32, [_I32, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32,
-                                     _I32, _I64, _P, _P]),
+                                     _I32, _I64, _P, _P, _SZ, _P]),
     "moe_combine": (_I32, [_P, _P, _I64, _I32, _I32, _P, _P]),
     "moe_down_combine_workspace_bytes": (_SZ, [_I64, _I32]),
     "moe_grouped_gemm_down_combine": (_I32, [_I32, _P, _P, _P, _P, _P, _P, _P, _I64, _I32, _I32, _I32, _I32,
@@ -303,20 +304,37 @@ def _h_alloc(dtype, cap, I, device):
     return h, torch.empty((cap, I // 32), dtype=torch.uint8, device=device)
 
 
+def moe_grouped_gemm_workspace(device) -> torch.Tensor:
+    """Workspace of the grouped GEMM calls on `device`, zero-filled (calls leave its counters zero)."""
+    with torch.cuda.device(device):
+        n = lib().moe_grouped_gemm_workspace_bytes()
+    if n == 0:
+        raise RuntimeError("moe_grouped_gemm_workspace_bytes: no supported device")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def _ws(ws):
+    """(pointer, bytes) of an optional grouped-GEMM workspace."""
+    if ws is None:
+        return None, 0
+    _need(ws, torch.uint8, "ws")
+    return _p(ws), ws.numel()
+
+
 def moe_grouped_gemm_swiglu(dtype: int, x, x_scale, w1, w1_scale, sort: SortResult, H: int, I: int,
-                            h=None, h_scale=None, stream=None):
+                            h=None, h_scale=None, stream=None, ws=None):
     if h is None:
         h, h_scale = _h_alloc(dtype, max(sort.cap, 1), I, x.device)
     _check_gemm(dtype, True, True, x, x_scale, w1, w1_scale, sort, H, I, h, h_scale)
     _check("moe_grouped_gemm_swiglu", lib().moe_grouped_gemm_swiglu(
         dtype, _p(x), _p(x_scale), _p(w1), _p(w1_scale), _p(sort.sorted_ids), _p(sort.tile_expert),
         _p(sort.num_tiles), sort.T, H, I, sort.E, sort.k, sort.block_m, sort.cap, _p(h), _p(h_scale),
-        _s(stream)))
+        *_ws(ws), _s(stream)))
     return h, h_scale
 
 
 def moe_grouped_gemm_swiglu_h32(dtype: int, x, x_scale, w1, w1_scale, sort: SortResult, H: int, I: int,
-                                h=None, h_scale=None, h32=None, stream=None):
+                                h=None, h_scale=None, h32=None, stream=None, ws=None):
     """moe_grouped_gemm_swiglu that also returns the fp32 h before its storage
     rounding: (h, h_scale, h32 [cap, I] fp32)."""
     if h is None:
@@ -328,30 +346,32 @@ def moe_grouped_gemm_swiglu_h32(dtype: int, x, x_scale, w1, w1_scale, sort: Sort
     _check("moe_grouped_gemm_swiglu_h32", lib().moe_grouped_gemm_swiglu_h32(
         dtype, _p(x), _p(x_scale), _p(w1), _p(w1_scale), _p(sort.sorted_ids), _p(sort.tile_expert),
         _p(sort.num_tiles), sort.T, H, I, sort.E, sort.k, sort.block_m, sort.cap, _p(h), _p(h_scale), _p(h32),
+        *_ws(ws),
         _s(stream)))
     return h, h_scale, h32
 
 
 def moe_grouped_gemm_relu2(dtype: int, x, x_scale, w1, w1_scale, sort: SortResult, H: int, I: int,
-                           h=None, h_scale=None, stream=None):
+                           h=None, h_scale=None, stream=None, ws=None):
     if h is None:
         h, h_scale = _h_alloc(dtype, max(sort.cap, 1), I, x.device)
     _check_gemm(dtype, True, False, x, x_scale, w1, w1_scale, sort, H, I, h, h_scale)
     _check("moe_grouped_gemm_relu2", lib().moe_grouped_gemm_relu2(
         dtype, _p(x), _p(x_scale), _p(w1), _p(w1_scale), _p(sort.sorted_ids), _p(sort.tile_expert),
         _p(sort.num_tiles), sort.T, H, I, sort.E, sort.k, sort.block_m, sort.cap, _p(h), _p(h_scale),
-        _s(stream)))
+        *_ws(ws), _s(stream)))
     return h, h_scale
 
 
 def moe_grouped_gemm_down(dtype: int, h, h_scale, w2, w2_scale, sort: SortResult, H: int, I: int, y=None,
-                          stream=None):
+                          stream=None, ws=None):
     if y is None:
         y = torch.empty((max(sort.T * sort.k, 1), H), dtype=torch.bfloat16, device=h.device)
     _check_gemm(dtype, False, True, h, h_scale, w2, w2_scale, sort, H, I, y, None)
     _check("moe_grouped_gemm_down", lib().moe_grouped_gemm_down(
         dtype, _p(h), _p(h_scale), _p(w2), _p(w2_scale), _p(sort.sorted_ids), _p(sort.tile_expert),
-        _p(sort.num_tiles), sort.T, H, I, sort.E, sort.k, sort.block_m, sort.cap, _p(y), _s(stream)))
+        _p(sort.num_tiles), sort.T, H, I, sort.E, sort.k, sort.block_m, sort.cap, _p(y), *_ws(ws),
+        _s(stream)))
     return y
 
 

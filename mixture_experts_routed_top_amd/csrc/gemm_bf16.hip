@@ -48,8 +48,9 @@ namespace moe {
 
 namespace {
 
-constexpr int kXcds = 8;
+constexpr int kXcds = kSplitXcds;
 constexpr int kGroup = 4;       // m-tiles of one expert that walk the n-tiles side by side
+constexpr int kMinSplitSteps = 8;   // the last round is split along K only from 8 k-steps (K >= 512)
 constexpr int kActSwiglu = 0;   // h = silu(gate) * up
 constexpr int kActRelu2 = 1;    // h = max(g, 0)^2, one projection
 
@@ -111,6 +112,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+
+// Cache policy of a buffer access with device-scope coherence (sc1), the
+// policy the compiler gives device-scope atomic loads and stores.
+constexpr int kDeviceScope = 16;
 
 struct Params {
   const uint16_t* a;       // GEMM1: x [T, H]; GEMM2: h [cap, I]
@@ -124,6 +130,8 @@ struct Params {
   const float* topk_w;     // GEMM2 with the fused combine: gate weights [A]
   uint16_t* comb;          //   combined output [T, H]
   int32_t* counters;       //   [T, ceil(H / BN)] finished slots per (token, column tile); zero between calls
+  int32_t* split_cnt;      // optional K-split of the last round: halves finished per slot; zero between calls
+  float* split_part;       //   fp32 partial tiles, two per slot
   int64_t A;
   uint32_t a_bytes;        // bytes of the token operand (below 2^31)
   int H, I, k;
@@ -251,11 +259,30 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
   // m-tile finds the slices still in L2, loses even when the walk is smaller
   // than an XCD's 4 MB L2: on the Qwen3-30B-A3B shape GEMM2's 3.1 MB walk ran
   // 322 us that way against 309 us grouped.
-  int probe = t0 + local < t1 ? grouped_probe(t0 + local, ntn, num_tiles, p.tile_expert, lane) : 0;
-  for (int64_t task = t0 + local; task < t1; task += per_xcd) {
+  //
+  // Work balance: the slice's tasks go round robin over the XCD's
+  // workgroups, so when the last round holds at most half as many tasks as
+  // there are workgroups, most of them would idle through it. Given the split
+  // workspace, each task of that round is then cut in two along K (items
+  // 2j and 2j + 1 of the split range, k-steps [0, nk/2) and [nk/2, nk)), and
+  // the workgroup that finishes second adds the two fp32 partial tiles and
+  // runs the epilogue. Items are wave-uniform.
+  const int64_t nslice = t1 - t0;
+  const int64_t rounds = nslice / per_xcd, left = nslice - rounds * per_xcd;
+  const bool split = p.split_cnt != nullptr && left > 0 && 2 * left <= per_xcd && nk >= kMinSplitSteps;
+  const int64_t nfull = split ? rounds * per_xcd : nslice;       // items below nfull are whole tasks
+  const int64_t nitems = split ? nfull + 2 * left : nslice;
+  auto task_of = [&](int64_t it) { return t0 + (it < nfull ? it : nfull + (it - nfull) / 2); };
+  int probe = local < nitems ? grouped_probe(task_of(local), ntn, num_tiles, p.tile_expert, lane) : 0;
+  for (int64_t it = local; it < nitems; it += per_xcd) {
+    const int64_t task = task_of(it);
+    const bool part = it >= nfull;                  // half of a split task
+    const int khalf = part ? static_cast<int>((it - nfull) & 1) : 0;
+    const int kb = khalf ? nk / 2 : 0;              // k-steps [kb, ke) of this item
+    const int ke = part && khalf == 0 ? nk / 2 : nk;
     int nt, mt, e;
     grouped_task<kGroup>(task, ntn, num_tiles, p.tile_expert, lane, probe, nt, mt, e);
-    if (task + per_xcd < t1) probe = grouped_probe(task + per_xcd, ntn, num_tiles, p.tile_expert, lane);
+    if (it + per_xcd < nitems) probe = grouped_probe(task_of(it + per_xcd), ntn, num_tiles, p.tile_expert, lane);
     const int64_t row0 = static_cast<int64_t>(mt) * BM;
     const int n0 = nt * BN;
 
@@ -397,7 +424,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
     // barrier after that wait also means every wave has finished step
     // s - 1, whose buffers step s refills; the loads are issued ahead of the
     // MFMAs (the scheduling barrier keeps them there). Six steps repeat the
-    // buffer pattern; the k-steps past the end load zeros and are not computed.
+    // buffer pattern; the k-steps past the item's end are loaded (zeros past
+    // K) but not computed.
     auto step = [&](char* tb, char* wb, char* tb_next, char* wb_next2, int s) {
       wait_vmcnt<C::GPW - C::GPW_T>();
       barrier_no_fence();
@@ -406,27 +434,86 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
       __builtin_amdgcn_sched_barrier(0);
       compute(tb, wb);
     };
-    load_t(stage0, 0);
-    load_w(wst0, 0);
-    load_w(wst1, 1);
-    for (int kt = 0;; kt += 6) {
+    load_t(stage0, kb);
+    load_w(wst0, kb);
+    load_w(wst1, kb + 1);
+    for (int kt = kb;; kt += 6) {
       step(stage0, wst0, stage1, wst2, kt);
-      if (kt + 1 >= nk) break;
+      if (kt + 1 >= ke) break;
       step(stage1, wst1, stage0, wst0, kt + 1);
-      if (kt + 2 >= nk) break;
+      if (kt + 2 >= ke) break;
       step(stage0, wst2, stage1, wst1, kt + 2);
-      if (kt + 3 >= nk) break;
+      if (kt + 3 >= ke) break;
       step(stage1, wst0, stage0, wst2, kt + 3);
-      if (kt + 4 >= nk) break;
+      if (kt + 4 >= ke) break;
       step(stage0, wst1, stage1, wst0, kt + 4);
-      if (kt + 5 >= nk) break;
+      if (kt + 5 >= ke) break;
       step(stage1, wst2, stage0, wst1, kt + 5);
-      if (kt + 6 >= nk) break;
+      if (kt + 6 >= ke) break;
     }
     // the loads issued past the end have landed and every wave is done
     // with LDS before the next task refills it
     wait_vmcnt<0>();
     barrier_no_fence();
+
+    if (part) {
+      // Both halves store their partial tile (lane-major f32x4 rows: whole
+      // 1 KB wave rows) and count; the second to count adds the other half's
+      // tile to its own (fp32 addition commutes, so the sum does not depend
+      // on which half finishes first) and resets the counter for the next
+      // call. The task's slot: items 2j, 2j + 1 of this XCD's split range.
+      // The tiles move with the cache policy of device-scope atomics (sc1:
+      // stores write through, loads bypass the non-coherent cache levels),
+      // so the store waits (vmcnt 0) before the count are all the ordering
+      // the exchange needs. Release / acquire fences at device scope would
+      // instead write back and invalidate the whole L2 of the XCD, whose
+      // other workgroups are still streaming their operands through it
+      // (measured: a split GEMM1 slower than none).
+      constexpr int NV = C::HALVES * C::FM * C::FN * 4;        // f32x4 per lane
+      const int64_t slot = static_cast<int64_t>(xcd) * split_slots_per_xcd(G) + (it - nfull) / 2;
+      const __amdgpu_buffer_rsrc_t prs =
+          make_rsrc(p.split_part + slot * 2 * NV * C::THREADS * 4, static_cast<uint32_t>(2 * NV * C::THREADS * 16));
+      const uint32_t mine = static_cast<uint32_t>((khalf * NV * C::THREADS + tid) * 16);
+      const uint32_t other = static_cast<uint32_t>(((khalf ^ 1) * NV * C::THREADS + tid) * 16);
+#pragma unroll
+      for (int h = 0; h < C::HALVES; ++h)
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const f32x4 v = {acc[h][i][j][4 * q], acc[h][i][j][4 * q + 1], acc[h][i][j][4 * q + 2],
+                               acc[h][i][j][4 * q + 3]};
+              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), prs,
+                                                     mine + (((h * C::FM + i) * C::FN + j) * 4 + q) * C::THREADS * 16,
+                                                     0, kDeviceScope);
+            }
+      wait_vmcnt<0>();
+      __syncthreads();
+      int32_t* flag = reinterpret_cast<int32_t*>(stage0);        // LDS is free until the next task
+      if (tid == 0) {
+        const int32_t was = __hip_atomic_fetch_add(p.split_cnt + slot, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (was == 1) __hip_atomic_store(p.split_cnt + slot, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *flag = was;
+      }
+      __syncthreads();
+      if (*flag == 0) continue;   // the other half finishes the task (this was the workgroup's last item)
+#pragma unroll
+      for (int h = 0; h < C::HALVES; ++h)
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const f32x4 o = __builtin_bit_cast(
+                  f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                             prs, other + (((h * C::FM + i) * C::FN + j) * 4 + q) * C::THREADS * 16, 0, kDeviceScope));
+#pragma unroll
+              for (int r = 0; r < 4; ++r) acc[h][i][j][4 * q + r] += o[r];
+            }
+    }
 
 
     // epilogue: lane holds output columns 8*(v/4) + 4*(lane/32) + v%4 of token lane%32
@@ -505,6 +592,11 @@ hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s, const
   p.out = static_cast<uint16_t*>(g.out);
   p.gu = static_cast<uint16_t*>(g.out_scale);   // BF16 SwiGLU GEMM1: the optional saved pre-activations
   p.h32 = GEMM1 ? static_cast<float*>(g.h32) : nullptr;
+  // the fused combine keeps whole tasks (its counters follow every tile's stores)
+  static_assert(BM * C::HALVES * BN <= kSplitTileFloats, "a partial tile fits its workspace slot");
+  p.split_cnt = !FUSE && g.split_ws ? static_cast<int32_t*>(g.split_ws) : nullptr;
+  p.split_part = !FUSE && g.split_ws ? reinterpret_cast<float*>(static_cast<char*>(g.split_ws) + kSplitCntBytes)
+                                     : nullptr;
   p.A = g.T * g.k;
   p.a_bytes = static_cast<uint32_t>((GEMM1 ? g.T * g.H : g.cap * g.I) * 2);
   p.H = g.H;

@@ -54,6 +54,14 @@ int64_t capacity(int64_t T, int32_t k, int32_t E, int32_t bm) {
 
 moe_status_t launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_DEVICE; }
 
+// The optional K-split workspace of the grouped GEMMs: NULL, or 256-byte
+// aligned and at least moe_grouped_gemm_workspace_bytes() bytes.
+moe_status_t check_split_ws(const void* ws, size_t ws_bytes, const moe::DeviceInfo& dev) {
+  if (!ws) return MOE_OK;
+  if (dev.num_cus > moe::kSplitMaxGrid || ws_bytes < moe::split_ws_bytes(dev.num_cus)) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
 // Shape and pointer checks shared by both grouped GEMMs.
 moe_status_t check_gemm(int32_t dtype, const void* act, const void* act_scale, const void* w,
                         const void* w_scale, const int32_t* sorted_ids, const int32_t* tile_expert,
@@ -267,15 +275,18 @@ moe_status_t moe_grouped_gemm_swiglu(int32_t dtype, const void* x, const void* x
                                      const void* w1_scale, const int32_t* sorted_ids,
                                      const int32_t* tile_expert, const int32_t* num_tiles, int64_t T,
                                      int32_t H, int32_t I, int32_t E, int32_t k, int32_t block_m, int64_t cap,
-                                     void* h, void* h_scale, void* stream) {
+                                     void* h, void* h_scale, void* ws, size_t ws_bytes, void* stream) {
   if (moe_status_t st = check_gemm(dtype, x, x_scale, w1, w1_scale, sorted_ids, tile_expert, num_tiles, T, H,
                                    I, E, k, block_m, cap, h, h_scale, true))
     return st;
   if (T == 0) return MOE_OK;
+  if (ws && !aligned(ws, 256)) return MOE_ERR_INVALID_ARG;
   moe::DeviceInfo dev;
   if (moe_status_t st = current_device(&dev)) return st;
+  if (moe_status_t st = check_split_ws(ws, ws_bytes, dev)) return st;
   moe::GemmArgs g{x, x_scale, w1, w1_scale, sorted_ids, tile_expert, num_tiles, h, h_scale,
                   T, H, I, E, k, block_m, cap};
+  g.split_ws = ws;
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (dtype) {
     case MOE_DTYPE_BF16:
@@ -290,17 +301,21 @@ moe_status_t moe_grouped_gemm_swiglu_h32(int32_t dtype, const void* x, const voi
                                          const void* w1_scale, const int32_t* sorted_ids,
                                          const int32_t* tile_expert, const int32_t* num_tiles, int64_t T,
                                          int32_t H, int32_t I, int32_t E, int32_t k, int32_t block_m, int64_t cap,
-                                         void* h, void* h_scale, float* h32, void* stream) {
+                                         void* h, void* h_scale, float* h32, void* ws, size_t ws_bytes,
+                                         void* stream) {
   if (moe_status_t st = check_gemm(dtype, x, x_scale, w1, w1_scale, sorted_ids, tile_expert, num_tiles, T, H,
                                    I, E, k, block_m, cap, h, h_scale, true))
     return st;
   if (T == 0) return MOE_OK;
   if (!h32 || !aligned(h32, 16)) return MOE_ERR_INVALID_ARG;
+  if (ws && !aligned(ws, 256)) return MOE_ERR_INVALID_ARG;
   moe::DeviceInfo dev;
   if (moe_status_t st = current_device(&dev)) return st;
+  if (moe_status_t st = check_split_ws(ws, ws_bytes, dev)) return st;
   moe::GemmArgs g{x, x_scale, w1, w1_scale, sorted_ids, tile_expert, num_tiles, h, h_scale,
                   T, H, I, E, k, block_m, cap};
   g.h32 = h32;
+  g.split_ws = ws;
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (dtype) {
     case MOE_DTYPE_BF16:
@@ -329,38 +344,51 @@ moe_status_t moe_grouped_gemm_swiglu_save(const void* x, const void* w1, const i
 moe_status_t moe_grouped_gemm_relu2(int32_t dtype, const void* x, const void* x_scale, const void* w1,
                                     const void* w1_scale, const int32_t* sorted_ids, const int32_t* tile_expert,
                                     const int32_t* num_tiles, int64_t T, int32_t H, int32_t I, int32_t E,
-                                    int32_t k, int32_t block_m, int64_t cap, void* h, void* h_scale,
-                                    void* stream) {
+                                    int32_t k, int32_t block_m, int64_t cap, void* h, void* h_scale, void* ws,
+                                    size_t ws_bytes, void* stream) {
   if (moe_status_t st = check_gemm(dtype, x, x_scale, w1, w1_scale, sorted_ids, tile_expert, num_tiles, T, H,
                                    I, E, k, block_m, cap, h, h_scale, true, false))
     return st;
   if (dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (T == 0) return MOE_OK;
+  if (ws && !aligned(ws, 256)) return MOE_ERR_INVALID_ARG;
   moe::DeviceInfo dev;
   if (moe_status_t st = current_device(&dev)) return st;
+  if (moe_status_t st = check_split_ws(ws, ws_bytes, dev)) return st;
   moe::GemmArgs g{x, x_scale, w1, w1_scale, sorted_ids, tile_expert, num_tiles, h, h_scale,
                   T, H, I, E, k, block_m, cap};
+  g.split_ws = ws;
   return launched(moe::launch_gemm1_relu2_bf16(g, dev, static_cast<hipStream_t>(stream)));
 }
 
 moe_status_t moe_grouped_gemm_down(int32_t dtype, const void* h, const void* h_scale, const void* w2,
                                    const void* w2_scale, const int32_t* sorted_ids, const int32_t* tile_expert,
                                    const int32_t* num_tiles, int64_t T, int32_t H, int32_t I, int32_t E,
-                                   int32_t k, int32_t block_m, int64_t cap, uint16_t* y, void* stream) {
+                                   int32_t k, int32_t block_m, int64_t cap, uint16_t* y, void* ws, size_t ws_bytes,
+                                   void* stream) {
   if (moe_status_t st = check_gemm(dtype, h, h_scale, w2, w2_scale, sorted_ids, tile_expert, num_tiles, T, H, I,
                                    E, k, block_m, cap, y, nullptr, false))
     return st;
   if (T == 0) return MOE_OK;
+  if (ws && !aligned(ws, 256)) return MOE_ERR_INVALID_ARG;
   moe::DeviceInfo dev;
   if (moe_status_t st = current_device(&dev)) return st;
+  if (moe_status_t st = check_split_ws(ws, ws_bytes, dev)) return st;
   moe::GemmArgs g{h, h_scale, w2, w2_scale, sorted_ids, tile_expert, num_tiles, y, nullptr,
                   T, H, I, E, k, block_m, cap};
+  g.split_ws = ws;
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (dtype) {
     case MOE_DTYPE_BF16: return launched(moe::launch_gemm2_bf16(g, dev, s));
     case MOE_DTYPE_FP8_BLOCK128: return launched(moe::launch_gemm2_fp8(g, dev, s));
     default: return launched(moe::launch_gemm2_mx(g, dev, s));
   }
+}
+
+size_t moe_grouped_gemm_workspace_bytes(void) {
+  moe::DeviceInfo dev;
+  if (current_device(&dev) != MOE_OK || dev.num_cus > moe::kSplitMaxGrid) return 0;
+  return moe::split_ws_bytes(dev.num_cus);
 }
 
 size_t moe_down_combine_workspace_bytes(int64_t T, int32_t H) {

@@ -1,8 +1,7 @@
 // Top-k routing: one wavefront per token.
 //
 // Selection is a radix select on order-preserving integer keys of the fp32
-// logits: 32 ballot rounds find the k-th largest key (no cross-lane data
-// movement), the k winners are the keys above it plus the lowest-index keys
+// logits: 32 counting rounds find the k-th largest key, the k winners are the keys above it plus the lowest-index keys
 // equal to it, and one compaction through LDS puts them in slot order (logit
 // descending, equal logits -> lower expert index). The gate weights are the
 // softmax over the selected logits, summed in slot order, or the sigmoid of
@@ -32,6 +31,46 @@ __device__ __forceinline__ bool before(uint32_t ka, int ea, uint32_t kb, int eb)
 
 __device__ __forceinline__ int popc(uint64_t m) { return __popcll(m); }
 
+// DPP lane patterns (within each row of 16 lanes): swap neighbours, swap
+// pairs, mirror each half row, mirror the row.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+__device__ __forceinline__ int dpp_add(int v, int ctrl) {
+  switch (ctrl) {   // the control must be a constant of the instruction
+    case kDppXor1: return v + __builtin_amdgcn_update_dpp(0, v, kDppXor1, 0xF, 0xF, false);
+    case kDppXor2: return v + __builtin_amdgcn_update_dpp(0, v, kDppXor2, 0xF, 0xF, false);
+    case kDppHalfMirror: return v + __builtin_amdgcn_update_dpp(0, v, kDppHalfMirror, 0xF, 0xF, false);
+    default: return v + __builtin_amdgcn_update_dpp(0, v, kDppMirror, 0xF, 0xF, false);
+  }
+}
+
+// Number of the wave's keys >= c (wave-uniform). Padding keys are 0, below
+// every c >= 1. With one or two keys a lane, one ballot and one scalar
+// popcount per key. With more, a lane counts its own keys and the counts
+// are added across lanes by DPP moves (quad swaps, then the half-row and row
+// mirrors leave the row's sum in every lane of a row of 16) and four lane
+// reads: one ballot per key would make the CU's single scalar unit the
+// bottleneck (8 keys a lane, 64 waves a CU, 32 rounds).
+template <int PER_LANE>
+__device__ __forceinline__ int count_ge(const uint32_t (&key)[PER_LANE], uint32_t c) {
+  if constexpr (PER_LANE <= 2) {
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i) n += popc(__ballot(key[i] >= c));
+    return n;
+  } else {
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i) n += key[i] >= c ? 1 : 0;
+    n = dpp_add(n, kDppXor1);
+    n = dpp_add(n, kDppXor2);
+    n = dpp_add(n, kDppHalfMirror);
+    n = dpp_add(n, kDppMirror);
+    return __builtin_amdgcn_readlane(n, 0) + __builtin_amdgcn_readlane(n, 16) + __builtin_amdgcn_readlane(n, 32) +
+           __builtin_amdgcn_readlane(n, 48);
+  }
+}
+
 template <int PER_LANE>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void route_kernel(const float* __restrict__ logits, int64_t T,
                                                                     int E, int k, int score, int n_shared,
@@ -54,17 +93,20 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void route_kernel(const float*
     const int e = lane + 64 * i;
     ok[i] = e < E;
     val[i] = ok[i] ? row[e] : 0.0f;
-    key[i] = order_key(val[i]);
+    key[i] = ok[i] ? order_key(val[i]) : 0u;   // padding: below every candidate tau | bit
   }
 
-  // the k-th largest key: the largest tau with #{key >= tau} >= k
+  // the k-th largest key: the largest tau with #{key >= tau} >= k. Once a
+  // candidate has exactly k keys at or above it, those keys are the winners
+  // and the lower bits cannot change the selection below (every key equal to
+  // tau is then taken), so the search stops there: after about 15 of the 32
+  // rounds for distinct random logits.
   uint32_t tau = 0;
   for (int b = 31; b >= 0; --b) {
     const uint32_t cand = tau | (1u << b);
-    int cnt = 0;
-#pragma unroll
-    for (int i = 0; i < PER_LANE; ++i) cnt += popc(__ballot(ok[i] && key[i] >= cand));
-    if (cnt >= k) tau = cand;
+    const int n = count_ge<PER_LANE>(key, cand);
+    if (n >= k) tau = cand;
+    if (n == k) break;
   }
   // winners: every key above tau, then the lowest-index keys equal to tau
   int n_gt = 0;

@@ -32,6 +32,7 @@ class Plan:
     out: torch.Tensor
     train: Optional["TrainBuffers"] = None
     counters: Optional[torch.Tensor] = None      # fused combine: zeroed counter workspace
+    ws: Optional[torch.Tensor] = None            # BF16 GEMMs: zeroed K-split workspace (last-round balance)
 
 
 @dataclass
@@ -71,7 +72,8 @@ class MoeLayer:
     """
 
     def __init__(self, dtype: int, w1: torch.Tensor, w2: torch.Tensor, k: int, score: int = B.SCORE_SOFTMAX,
-                 act: int = B.ACT_SWIGLU, n_shared: int = 0, fused_combine: bool = False):
+                 act: int = B.ACT_SWIGLU, n_shared: int = 0, fused_combine: bool = False,
+                 split_tail: bool = True):
         E, twoI, H = w1.shape
         if act not in (B.ACT_SWIGLU, B.ACT_RELU2):
             raise ValueError("unknown activation")
@@ -81,6 +83,8 @@ class MoeLayer:
             raise ValueError("the fused combine is implemented for the BF16 path")
         self.dtype, self.score, self.act, self.n_shared = dtype, score, act, n_shared
         self.fused_combine = fused_combine
+        # the BF16 GEMMs split their last round of tiles along K when given a workspace
+        self.split_tail = split_tail and dtype == B.DTYPE_BF16
         self.k_routed, self.k = k, k + n_shared          # slots per token: routed, then shared
         self.E, self.H, self.I = E, H, (twoI // 2 if act == B.ACT_SWIGLU else twoI)
         if w2.shape != (E, H, self.I):
@@ -135,7 +139,8 @@ class MoeLayer:
                     sort, xq, xs, h, h_scale,
                     torch.empty((max(T * self.k, 1), self.H), dtype=torch.bfloat16, device=device),
                     torch.empty((T, self.H), dtype=torch.bfloat16, device=device), tb,
-                    B.moe_down_combine_workspace(T, self.H, device) if self.fused_combine else None)
+                    B.moe_down_combine_workspace(T, self.H, device) if self.fused_combine else None,
+                    B.moe_grouped_gemm_workspace(device) if self.split_tail and T > 0 else None)
 
     def forward(self, x: torch.Tensor, logits: torch.Tensor, plan: Optional[Plan] = None,
                 stream=None) -> torch.Tensor:
@@ -153,13 +158,13 @@ class MoeLayer:
             a, a_scale = B.moe_quantize_mxfp8(x, p.xq, p.xs, stream=stream)
         gemm1 = B.moe_grouped_gemm_swiglu if self.act == B.ACT_SWIGLU else B.moe_grouped_gemm_relu2
         gemm1(self.dtype, a, a_scale, self.w1, self.w1_scale, p.sort, self.H, self.I, p.h, p.h_scale,
-              stream=stream)
+              stream=stream, ws=p.ws)
         if self.fused_combine:
             B.moe_grouped_gemm_down_combine(self.dtype, p.h, p.h_scale, self.w2, self.w2_scale, p.sort, self.H,
                                             self.I, p.w, p.counters, p.y, p.out, stream=stream)
             return p.out
         B.moe_grouped_gemm_down(self.dtype, p.h, p.h_scale, self.w2, self.w2_scale, p.sort, self.H, self.I,
-                                p.y, stream=stream)
+                                p.y, stream=stream, ws=p.ws)
         return B.moe_combine(p.y, p.w, p.out, stream=stream)
 
     __call__ = forward
@@ -178,7 +183,8 @@ class MoeLayer:
         self._route(logits, p, stream)
         B.moe_align_sort(p.ids, self.E, p.block_m, out=p.sort, stream=stream)
         B.moe_grouped_gemm_swiglu_save(x, self.w1, p.sort, self.H, self.I, p.h, p.train.gu, stream=stream)
-        B.moe_grouped_gemm_down(self.dtype, p.h, None, self.w2, None, p.sort, self.H, self.I, p.y, stream=stream)
+        B.moe_grouped_gemm_down(self.dtype, p.h, None, self.w2, None, p.sort, self.H, self.I, p.y, stream=stream,
+                                ws=p.ws)
         return B.moe_combine(p.y, p.w, p.out, stream=stream)
 
     def backward(self, x: torch.Tensor, dout: torch.Tensor, plan: Plan, stream=None) -> TrainBuffers:

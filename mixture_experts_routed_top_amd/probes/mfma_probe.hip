@@ -7,6 +7,14 @@
 //          FP4 x FP4 operands. This is what the roofline of the MXFP4-weight
 //          GEMMs is priced against: FP4 on one operand only issues at the
 //          FP8 rate, so those GEMMs are reported against the FP8 peak.
+//   lds    the BF16 GEMMs' inner loop without its operand loads: a
+//          workgroup of 8 waves, each wave a 64 x 128 tile (the forward
+//          GEMMs' per-wave tile), reads its MFMA fragments (16 bytes a lane)
+//          from 128-byte LDS rows, the next 16-K substep's fragments while
+//          the current substep's MFMAs run, one barrier per 64-K step; with
+//          the 16-byte chunk XOR-swizzled by row & 7 and by (row >> 1) & 7.
+//          Also the plain LDS read bandwidth of 16-byte reads. This is the
+//          compute side's own ceiling, with operand loads taken out.
 //   accum  the accumulation precision of one MFMA: one output is a sum of
 //          two large products (equal, or cancelling) and many small ones of
 //          magnitude 2^e, C = 0; the result is printed beside the exact sum.
@@ -95,6 +103,153 @@ double rate(int cus, float* out, double flop_per_mfma, double peak, const char* 
   printf("{\"probe\": \"rate\", \"mfma\": \"%s\", \"tflops\": %.1f, \"published_dense_peak_tflops\": %.1f, "
          "\"frac_of_peak\": %.3f}\n", name, tf, peak, tf / peak);
   return tf;
+}
+
+// ------------------------------------------------------------------ MFMA + LDS
+// Offset of 16-byte chunk c of LDS row `row` (128-byte rows).
+template <int SWZ>
+__device__ __forceinline__ uint32_t lds_off(int row, int c) {
+  const int s = SWZ == 0 ? (row & 7) : ((row >> 1) & 7);
+  return static_cast<uint32_t>(row * 128 + ((c ^ s) << 4));
+}
+
+// WM x WN waves, each FM x FN 32 x 32 output blocks; LDS holds BM token rows
+// and BN weight rows of 64 bf16 (one 64-K step), filled once.
+template <int WM, int WN, int FM, int FN, int SWZ>
+__global__ __launch_bounds__(64 * WM * WN, 1) void mfma_lds_kernel(float* out, int iters) {
+  constexpr int TM = FM * 32, TN = FN * 32, BM = WM * TM, BN = WN * TN;
+  constexpr int BYTES = (BM + BN) * 128;
+  static_assert(BYTES <= 160 * 1024, "one k-step of both operands fits in LDS");
+  __shared__ __attribute__((aligned(1024))) char lds[BYTES];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  for (int i = tid; i < BYTES / 4; i += 64 * WM * WN) reinterpret_cast<float*>(lds)[i] = 0.001f * (i & 255);
+  __syncthreads();
+  const char* tok = lds;
+  const char* wgt = lds + BM * 128;
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+  for (int it = 0; it < iters; ++it) {
+    __builtin_amdgcn_s_barrier();
+    bf16x8 xf[2][FM], wf[2][FN];
+    auto frags = [&](int kk, int buf) {
+      const int ch = kk * 2 + (lane >> 5);   // rows < BM / BN, chunk < 8: inside the array
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        xf[buf][i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
+                                                    tok + lds_off<SWZ>(wm * TM + i * 32 + (lane & 31), ch)));
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        wf[buf][j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(
+                                                    wgt + lds_off<SWZ>(wn * TN + j * 32 + (lane & 31), ch)));
+    };
+    frags(0, 0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int cur = kk & 1;
+      if (kk + 1 < 4) frags(kk + 1, cur ^ 1);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[cur][j], xf[cur][i], acc[i][j], 0, 0, 0);
+    }
+    // the next substep's reads interleaved with the current substep's MFMAs
+    constexpr int READS = FM + FN, MFMAS = FM * FN, PAIRS = READS < MFMAS ? READS : MFMAS;
+    __builtin_amdgcn_sched_group_barrier(0x100, READS, 0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      if (kk + 1 < 4) {
+#pragma unroll
+        for (int q = 0; q < PAIRS; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        if (MFMAS > PAIRS) __builtin_amdgcn_sched_group_barrier(0x008, MFMAS - PAIRS, 0);
+        if (READS > PAIRS) __builtin_amdgcn_sched_group_barrier(0x100, READS - PAIRS, 0);
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, MFMAS, 0);
+      }
+    }
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s += acc[i][j][v];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+// 4 waves, each reading 16 bytes a lane from 32 consecutive 128-byte rows, 8 reads an iteration.
+template <int SWZ>
+__global__ __launch_bounds__(256, 1) void lds_read_kernel(float* out, int iters) {
+  __shared__ __attribute__((aligned(1024))) char lds[512 * 128];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < 512 * 128 / 4; i += 256) reinterpret_cast<float*>(lds)[i] = 0.001f * (i & 255);
+  __syncthreads();
+  uint4 s = {0, 0, 0, 0};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int row = (wave * 8 + r) * 32 % 512 + (lane & 31);   // < 512
+      const uint4 v = *reinterpret_cast<const uint4*>(lds + lds_off<SWZ>(row, (it & 3) * 2 + (lane >> 5)));
+      s.x ^= v.x;
+      s.y += v.y;
+      s.z ^= v.z;
+      s.w += v.w;
+    }
+  }
+  out[blockIdx.x * blockDim.x + threadIdx.x] = static_cast<float>(s.x + s.y + s.z + s.w);
+}
+
+template <class K>
+float best_ms(K kernel, int grid, int block, int iters, float* out) {
+  hipEvent_t a, b;
+  CK(hipEventCreate(&a));
+  CK(hipEventCreate(&b));
+  kernel<<<grid, block>>>(out, iters);
+  CK(hipDeviceSynchronize());
+  float best = 1e30f;
+  for (int r = 0; r < 5; ++r) {
+    CK(hipEventRecord(a));
+    kernel<<<grid, block>>>(out, iters);
+    CK(hipEventRecord(b));
+    CK(hipEventSynchronize(b));
+    float ms;
+    CK(hipEventElapsedTime(&ms, a, b));
+    if (ms < best) best = ms;
+  }
+  return best;
+}
+
+void mfma_lds(int cus, float* out) {
+  const int iters = 2000;
+  const double flop = 8.0 * 4 * 8 * 32768.0 * iters;   // 8 waves x 4 substeps x 8 MFMAs x 32x32x16x2
+  const float m7 = best_ms(mfma_lds_kernel<4, 2, 2, 4, 0>, cus, 512, iters, out);
+  const float m1 = best_ms(mfma_lds_kernel<4, 2, 2, 4, 1>, cus, 512, iters, out);
+  const char* sw[2] = {"row & 7", "(row >> 1) & 7"};
+  const float ms[2] = {m7, m1};
+  for (int i = 0; i < 2; ++i) {
+    const double tf = cus * flop / (ms[i] * 1e-3) / 1e12;
+    printf("{\"probe\": \"mfma_lds\", \"tile\": \"8 waves x 64x128\", \"swizzle\": \"%s\", \"tflops\": %.1f, "
+           "\"frac_of_bf16_peak\": %.3f}\n", sw[i], tf, tf / 2516.6);
+  }
+  const int riters = 20000;
+  const float r7 = best_ms(lds_read_kernel<0>, cus, 256, riters, out);
+  const float r1 = best_ms(lds_read_kernel<1>, cus, 256, riters, out);
+  const float rs[2] = {r7, r1};
+  for (int i = 0; i < 2; ++i) {
+    const double bytes = cus * 4.0 * 8 * 64 * 16 * riters;
+    printf("{\"probe\": \"lds_read_b128\", \"swizzle\": \"%s\", \"tb_s\": %.2f, "
+           "\"bytes_per_clock_per_cu_at_2.4GHz\": %.1f}\n", sw[i], bytes / (rs[i] * 1e-3) / 1e12,
+           bytes / (rs[i] * 1e-3) / cus / 2.4e9);
+  }
 }
 
 // ------------------------------------------------------------------ accumulation
@@ -201,6 +356,7 @@ int main(int argc, char** argv) {
   rate<kFp8Fp8>(prop.multiProcessorCount, out, 32.0 * 32 * 64 * 2, 5033.2, "scale_32x32x64_fp8xfp8");
   rate<kFp4Fp8>(prop.multiProcessorCount, out, 32.0 * 32 * 64 * 2, 5033.2, "scale_32x32x64_fp4xfp8");
   rate<kFp4Fp4>(prop.multiProcessorCount, out, 32.0 * 32 * 64 * 2, 10066.3, "scale_32x32x64_fp4xfp4");
+  mfma_lds(prop.multiProcessorCount, out);
   // FP8: large products 448 (+448 or -448), small 2^e
   for (int e = -9; e <= -2; ++e) {
     accum(0, 0x7E, 0x00, e4m3_pow2(e), out);

@@ -122,9 +122,9 @@ def _gemm_args(dtype=0, T=64, H=256, I=128, E=8, k=2, bm=32, cap=None, x=FAKE, w
 
 def test_gemm_host_validation():
     L = _lib()
-    sw = lambda *a, **kw: L.moe_grouped_gemm_swiglu(*_gemm_args(*a, **kw), FAKE, FAKE, NULL)
-    r2 = lambda *a, **kw: L.moe_grouped_gemm_relu2(*_gemm_args(*a, **kw), FAKE, FAKE, NULL)
-    dn = lambda *a, **kw: L.moe_grouped_gemm_down(*_gemm_args(*a, **kw), FAKE, NULL)
+    sw = lambda *a, **kw: L.moe_grouped_gemm_swiglu(*_gemm_args(*a, **kw), FAKE, FAKE, NULL, 0, NULL)
+    r2 = lambda *a, **kw: L.moe_grouped_gemm_relu2(*_gemm_args(*a, **kw), FAKE, FAKE, NULL, 0, NULL)
+    dn = lambda *a, **kw: L.moe_grouped_gemm_down(*_gemm_args(*a, **kw), FAKE, NULL, 0, NULL)
     # the squared-ReLU GEMM1 is BF16 only, rejected before anything is enqueued
     assert r2(dtype=1, H=256, I=128) == 2
     assert r2(dtype=2, H=256, I=128, T=0, x=NULL, w=NULL) == 2
@@ -139,6 +139,10 @@ def test_gemm_host_validation():
         assert f(x=NULL) == 1
         assert f(w=MIS) == 1
         assert f(T=0, x=NULL, w=NULL) == 0
+    # the optional K-split workspace must be 256-byte aligned (checked before the device)
+    assert L.moe_grouped_gemm_swiglu(*_gemm_args(), FAKE, FAKE, MIS, 1 << 30, NULL) == 1
+    assert L.moe_grouped_gemm_relu2(*_gemm_args(), FAKE, FAKE, MIS, 1 << 30, NULL) == 1
+    assert L.moe_grouped_gemm_down(*_gemm_args(), FAKE, MIS, 1 << 30, NULL) == 1
 
 
 def test_combine_host_validation():

@@ -514,3 +514,65 @@ def test_fp8_promotion_tiny_and_huge_blocks(bm):
     absref = O.grouped_gemm_down(np.abs(hhat[:rows]), np.abs(w2h), sorted_ids, tile_expert, num_tiles, bm, T * k)
     assert_within_rounding(got, ref, (1.05 * (I + 3 * I // 128) * U32 + 1.01 * F8F6F4_GROUP_LOSS) * absref,
                            min_exact=0.98)
+
+
+# ------------------------------------------------------------ K-split of a short last round (BF16)
+WS_COUNTER_BYTES = 4096   # the grouped-GEMM workspace starts with its split counters
+SPLIT_SHAPES = [  # T, H, E, k, I; round-robin routing: 640 rows per expert, 3 tiles of 256 each (48 tiles)
+    (2560, 512, 16, 4, 1024),    # GEMM1 (K = 512): 384 tasks, a last round of 16 per XCD of 32 workgroups
+    (2560, 2048, 16, 4, 512),    # GEMM2 (K = 512): 384 tasks, likewise
+]
+
+
+@pytest.mark.parametrize("T,H,E,k,I", SPLIT_SHAPES)
+def test_bf16_gemms_k_split_last_round(T, H, E, k, I):
+    """Given the workspace, the BF16 GEMMs cut the tiles of a short last round
+    in two along K and add the two fp32 halves. h and Y stay within the fp32
+    accumulation bound of the float64 oracle; h is still RN_bf16 of the
+    kernel's own fp32 h, bit for bit; a second call is bitwise identical; the
+    workspace's counters are zero again after every call; and on a 256-CU GPU, where these
+    shapes leave a last round of 16 tiles per XCD, the split tiles' fp32 sums
+    differ from the unsplit call's somewhere (the split ran)."""
+    from oracle import formats as F
+    bm = 256
+    rng = np.random.default_rng(T + H + I)
+    x = f64(_bf16(rng.standard_normal((T, H))))
+    w1 = f64(_bf16(rng.standard_normal((E, 2 * I, H)) * 0.05))
+    w2 = f64(_bf16(rng.standard_normal((E, H, I)) * 0.05))
+    ids = (np.arange(T * k) % E).reshape(T, k).astype(np.int32)
+    sort, (sorted_ids, tile_expert, num_tiles) = _sort_from_oracle(ids, E, bm)
+    rows = num_tiles * bm
+    assert num_tiles == 48
+    say("bf16 k-split", T, H, E, k, I)
+    ws = M.moe_grouped_gemm_workspace("cuda:0")
+    xa, w1a, w2a = cuda(_bf16(x)), cuda(_bf16(w1)), cuda(_bf16(w2))
+    h0, _, h32_0 = M.moe_grouped_gemm_swiglu_h32(M.DTYPE_BF16, xa, None, w1a, None, sort, H, I)
+    h1, _, h32_1 = M.moe_grouped_gemm_swiglu_h32(M.DTYPE_BF16, xa, None, w1a, None, sort, H, I, ws=ws)
+    torch.cuda.synchronize()
+    assert not ws[:WS_COUNTER_BYTES].any()     # the counters; the rest holds partial tiles
+    h2, _ = M.moe_grouped_gemm_swiglu(M.DTYPE_BF16, xa, None, w1a, None, sort, H, I, ws=ws)
+    y0 = M.moe_grouped_gemm_down(M.DTYPE_BF16, h1, None, w2a, None, sort, H, I)
+    y1 = M.moe_grouped_gemm_down(M.DTYPE_BF16, h1, None, w2a, None, sort, H, I, ws=ws)
+    y2 = M.moe_grouped_gemm_down(M.DTYPE_BF16, h1, None, w2a, None, sort, H, I, ws=ws)
+    torch.cuda.synchronize()
+    assert not ws[:WS_COUNTER_BYTES].any()     # the counters; the rest holds partial tiles
+    assert torch.equal(h1[:rows], h2[:rows]) and torch.equal(y1, y2)
+    v32 = h32_1[:rows].cpu().numpy().astype(np.float64)
+    np.testing.assert_array_equal(f64(h1[:rows]), F.round_bf16(v32))
+    # h: the fp32 h within the accumulation bound of the float64 h (a split sum has fewer rounding steps
+    # on any path than the H-term sequential one)
+    g, u = _values(x, w1, sorted_ids, tile_expert, num_tiles, bm, k, rows)
+    sig = 1.0 / (1.0 + np.exp(-np.clip(g, -700, 700)))
+    href = g * sig * u
+    ga, ua = _abs_sums(x, w1, sorted_ids, tile_expert, num_tiles, bm, k, rows)
+    dg, du = H * U32 * ga, H * U32 * ua
+    delta = 1.1 * dg * (np.abs(u) + du) + np.abs(g * sig) * du + 8 * U32 * np.abs(href)
+    assert not (np.abs(v32 - href) > delta + 1e-37).any()
+    # Y from the kernel's own h
+    hval = f64(h1[:rows])
+    yref = O.grouped_gemm_down(hval, w2, sorted_ids, tile_expert, num_tiles, bm, T * k)
+    yabs = O.grouped_gemm_down(np.abs(hval), np.abs(w2), sorted_ids, tile_expert, num_tiles, bm, T * k)
+    assert_within_rounding(f64(y1), yref, 1.01 * I * U32 * yabs, min_exact=0.99)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        split_ran = not torch.equal(h32_0[:rows], h32_1[:rows]) if H == 512 else not torch.equal(y0, y1)
+        assert split_ran, "the last round was not split"
