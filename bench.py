@@ -122,6 +122,64 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str, copy_mib: int, 
     print(json.dumps(out))
 
 
+# rocprofv3 --pmc of SQ_* / GRBM_GUI_ACTIVE: GRBM_GUI_ACTIVE comes summed over
+# the 8 XCDs (per-XCD busy cycles = value / 8, which over the dispatch's
+# duration gives the clock the kernel ran at); the SQ counters are summed over
+# every CU (LDS) or SIMD (MFMA busy).
+N_XCD, N_CU, N_SIMD = 8, 256, 1024
+SQ_SET = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F8",
+          "SQ_INSTS_VALU_MFMA_MOPS_F6F4", "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_BUSY_CU_CYCLES",
+          "GRBM_GUI_ACTIVE")
+
+
+def _counters(workload: str, kernel: str, dtype: int):
+    """MFMA / LDS utilisation of a kernel from the committed counter record,
+    or None when there is none or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_sq_counters.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("src_hash") != _src_hash(KERNEL_SRC[kernel][dtype]):
+        return None
+    return {k: rec[k] for k in ("mfma_busy", "clock_ghz", "lds_active", "lds_bank_conflict_share")}
+
+
+def write_counters(workload: str, csv_path: str, command: str):
+    """Turn one rocprofv3 --pmc pass of SQ_SET into per-launch MFMA / LDS
+    records of the two grouped GEMMs (profiles/<kernel>_<workload>_sq_counters.json)."""
+    import csv
+    from workloads import get_config
+    cfg = get_config(workload)
+    per = {}
+    for r in csv.DictReader(open(csv_path)):
+        role = _kernel_role(r["Kernel_Name"])
+        if role is None:
+            continue
+        d = per.setdefault(role, {}).setdefault(r["Dispatch_Id"], {})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+        d["_ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    out = []
+    for role, disp in per.items():
+        name = GEMM1_STAGE[cfg.act] if role == "gemm1" else role
+        avg = {c: sum(d[c] for d in disp.values()) / len(disp) for c in SQ_SET + ("_ns",)}
+        cyc = avg["GRBM_GUI_ACTIVE"] / N_XCD
+        mops = avg["SQ_INSTS_VALU_MFMA_MOPS_BF16"] + avg["SQ_INSTS_VALU_MFMA_MOPS_F8"] + \
+            avg["SQ_INSTS_VALU_MFMA_MOPS_F6F4"]
+        rec = {"kernel": name, "workload": workload, "src_hash": _src_hash(KERNEL_SRC[name][cfg.dtype]),
+               "launches": len(disp), "duration_us": round(avg["_ns"] / 1e3, 1),
+               "clock_ghz": round(cyc / avg["_ns"], 3),
+               "mfma_busy": round(avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * N_SIMD), 4),
+               "mfma_flop_counted": int(mops * 512),
+               "lds_active": round(avg["SQ_LDS_IDX_ACTIVE"] / (cyc * N_CU), 4),
+               "lds_bank_conflict_share": round(avg["SQ_LDS_BANK_CONFLICT"] / max(avg["SQ_LDS_IDX_ACTIVE"], 1), 4),
+               "counters_per_launch": {c: avg[c] for c in SQ_SET}, "command": command}
+        path = os.path.join(ROOT, "profiles", f"{name}_{workload}_sq_counters.json")
+        with open(path, "w") as fh:
+            json.dump(rec, fh, indent=1)
+        out.append(rec)
+    print(json.dumps(out))
+
+
 def stats_markdown(csv_path: str, title: str, command: str, out_path: str, bench_log: str = ""):
     """A short markdown table of a rocprofv3 --stats kernel summary, with the
     bench line the same profiled run printed (its HIP-event stage times)."""
@@ -224,6 +282,8 @@ def main(argv=None):
                     help="first run a plain streaming copy of this many MiB (HBM counter calibration)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM traffic records from two rocprofv3 counter passes and exit")
+    ap.add_argument("--write-counters", metavar="SQ_CSV",
+                    help="write the MFMA / LDS counter records from a rocprofv3 pass of the SQ counters and exit")
     ap.add_argument("--traffic-command", default="", help="the command that made the profile")
     ap.add_argument("--sweep", choices=("grid", "tokens"), default=None,
                     help="throughput sweep, one JSON line per shape: the BF16 parameter grid or the token sweep")
@@ -238,6 +298,9 @@ def main(argv=None):
 
     if a.stats_md:
         stats_markdown(a.stats_md[0], a.stats_md[1], a.traffic_command, a.stats_md[2], a.bench_log)
+        return 0
+    if a.write_counters:
+        write_counters(a.workload, a.write_counters, a.traffic_command)
         return 0
     if a.write_traffic:
         write_traffic(a.workload, a.write_traffic[0], a.write_traffic[1], a.copy_probe_mib or 1024,
@@ -357,7 +420,8 @@ def measure(cfg, inp, steps: int, warmup: int, block_m=None, data=None, fused_co
         achieved = dom_flops / (stage_us[dom] * 1e-6) / 1e12
         roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
-    roofline.update({"traffic": _traffic(cfg.name, dom, cfg.dtype), "avg_launch_us": stage_us[dom],
+    roofline.update({"traffic": _traffic(cfg.name, dom, cfg.dtype), "counters": _counters(cfg.name, dom, cfg.dtype),
+                     "avg_launch_us": stage_us[dom],
                      "algorithmic": f"{fl_mult}*T*(k+shared)*H*I = {dom_flops} FLOP per launch; "
                                     f"{bytes_note} = {dom_bytes} B per launch"})
 

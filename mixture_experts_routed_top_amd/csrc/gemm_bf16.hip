@@ -499,20 +499,24 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
       }
       __syncthreads();
       if (*flag == 0) continue;   // the other half finishes the task (this was the workgroup's last item)
+      // the other half's tile, 16 loads in flight at a time (one at a time,
+      // each waited for, the 32 round trips took 15 us)
+      constexpr int G16 = NV < 16 ? NV : 16;
+      static_assert(NV % G16 == 0, "whole groups of loads");
 #pragma unroll
-      for (int h = 0; h < C::HALVES; ++h)
+      for (int c = 0; c < NV; c += G16) {
+        f32x4 o[G16];
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i)
+        for (int u = 0; u < G16; ++u)
+          o[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               prs, other + (c + u) * C::THREADS * 16, 0, kDeviceScope));
 #pragma unroll
-          for (int j = 0; j < C::FN; ++j)
+        for (int u = 0; u < G16; ++u) {
+          const int v = c + u, q = v % 4, j = v / 4 % C::FN, i = v / (4 * C::FN) % C::FM, h = v / (4 * C::FN * C::FM);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const f32x4 o = __builtin_bit_cast(
-                  f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                             prs, other + (((h * C::FM + i) * C::FN + j) * 4 + q) * C::THREADS * 16, 0, kDeviceScope));
-#pragma unroll
-              for (int r = 0; r < 4; ++r) acc[h][i][j][4 * q + r] += o[r];
-            }
+          for (int r = 0; r < 4; ++r) acc[h][i][j][4 * q + r] += o[u][r];
+        }
+      }
     }
 
 
