@@ -521,6 +521,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
 
 
     // epilogue: lane holds output columns 8*(v/4) + 4*(lane/32) + v%4 of token lane%32
+    // (GEMM1: h = the activation, stored as bf16; GEMM2: Y rows scattered to
+    // assignment order)
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) {
       const int m = wm * C::TM + i * 32 + (lane & 31);
@@ -536,38 +538,86 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
       }
 #pragma unroll
       for (int j = 0; j < C::FN; ++j) {
+        if constexpr (!GEMM1) {
+          // Y: lanes r and r + 32 hold columns 8g .. 8g + 3 and 8g + 4 .. 8g + 7
+          // of the same row. One lane swap per word (v_permlane32_swap trades
+          // the upper lanes' first operand for the lower lanes' second) gives
+          // lane r groups 0 and 1 whole and lane r + 32 groups 2 and 3, stored
+          // 16 bytes at a time: half the store instructions of 8-byte pieces.
+          uint32_t u[4][2], from_lo[2][2], from_hi[2][2];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int n = n0 + wn * C::TN + j * 32 + g * 8 + (lane >> 5) * 4;
-          float o[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float gv = acc[0][i][j][g * 4 + r];
-            if (GEMM1 && ACT == kActSwiglu) {
-              const float uv = acc[C::HALVES - 1][i][j][g * 4 + r];
-              o[r] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
-            } else if (GEMM1) {
-              o[r] = gv > 0.0f ? gv * gv : 0.0f;
-            } else {
-              o[r] = gv;
-            }
+          for (int g = 0; g < 4; ++g) {
+            u[g][0] = pack_bf16x2(acc[0][i][j][4 * g], acc[0][i][j][4 * g + 1]);
+            u[g][1] = pack_bf16x2(acc[0][i][j][4 * g + 2], acc[0][i][j][4 * g + 3]);
           }
-          if (row_ok && n < N) {
-            uint2 st;
-            st.x = pack_bf16x2(o[0], o[1]);
-            st.y = pack_bf16x2(o[2], o[3]);
-            *reinterpret_cast<uint2*>(p.out + dst_row * N + n) = st;
-            if (GEMM1 && p.h32 != nullptr)   // the values rounded to bf16 above, for checking that rounding
-              *reinterpret_cast<f32x4*>(p.h32 + dst_row * N + n) = f32x4{o[0], o[1], o[2], o[3]};
-            if (GEMM1 && ACT == kActSwiglu && p.gu != nullptr) {
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int w = 0; w < 2; ++w) {
+              const auto r = __builtin_amdgcn_permlane32_swap(u[q][w], u[q + 2][w], false, false);
+              from_lo[q][w] = r[0];   // upper lanes: the lower lane's u[q + 2][w]
+              from_hi[q][w] = r[1];   // lower lanes: the upper lane's u[q][w]
+            }
+          const bool upper = lane >= 32;
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int n = n0 + wn * C::TN + j * 32 + (upper ? q + 2 : q) * 8;
+            const uint4 st = upper ? make_uint4(from_lo[q][0], from_lo[q][1], u[q + 2][0], u[q + 2][1])
+                                   : make_uint4(u[q][0], u[q][1], from_hi[q][0], from_hi[q][1]);
+            if (row_ok && n < N) *reinterpret_cast<uint4*>(p.out + dst_row * N + n) = st;   // N % 8 == 0
+          }
+        } else {
+          // h: the activation of the four column groups, then the same lane
+          // swap as Y above, so h is stored 16 bytes at a time
+          float hv[4][4];
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float gv = acc[0][i][j][g * 4 + r];
+              if (ACT == kActSwiglu) {
+                const float uv = acc[C::HALVES - 1][i][j][g * 4 + r];
+                hv[g][r] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+              } else {
+                hv[g][r] = gv > 0.0f ? gv * gv : 0.0f;
+              }
+            }
+          uint32_t u[4][2], from_lo[2][2], from_hi[2][2];
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            u[g][0] = pack_bf16x2(hv[g][0], hv[g][1]);
+            u[g][1] = pack_bf16x2(hv[g][2], hv[g][3]);
+          }
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int w = 0; w < 2; ++w) {
+              const auto r = __builtin_amdgcn_permlane32_swap(u[q][w], u[q + 2][w], false, false);
+              from_lo[q][w] = r[0];
+              from_hi[q][w] = r[1];
+            }
+          const bool upper = lane >= 32;
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int n = n0 + wn * C::TN + j * 32 + (upper ? q + 2 : q) * 8;
+            const uint4 st = upper ? make_uint4(from_lo[q][0], from_lo[q][1], u[q + 2][0], u[q + 2][1])
+                                   : make_uint4(u[q][0], u[q][1], from_hi[q][0], from_hi[q][1]);
+            if (n < N) *reinterpret_cast<uint4*>(p.out + dst_row * N + n) = st;   // N % 8 == 0
+          }
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int n = n0 + wn * C::TN + j * 32 + g * 8 + (lane >> 5) * 4;
+            if (n >= N) continue;
+            if (p.h32 != nullptr)   // the values rounded to bf16 above, for checking that rounding
+              *reinterpret_cast<f32x4*>(p.h32 + dst_row * N + n) = f32x4{hv[g][0], hv[g][1], hv[g][2], hv[g][3]};
+            if (ACT == kActSwiglu && p.gu != nullptr) {
               // training forward: the gate and up pre-activations for the backward
-              const float gv[4] = {acc[0][i][j][g * 4], acc[0][i][j][g * 4 + 1], acc[0][i][j][g * 4 + 2],
-                                   acc[0][i][j][g * 4 + 3]};
-              const float uv[4] = {acc[C::HALVES - 1][i][j][g * 4], acc[C::HALVES - 1][i][j][g * 4 + 1],
-                                   acc[C::HALVES - 1][i][j][g * 4 + 2], acc[C::HALVES - 1][i][j][g * 4 + 3]};
               uint16_t* gr = p.gu + dst_row * 2 * N + n;
-              *reinterpret_cast<uint2*>(gr) = make_uint2(pack_bf16x2(gv[0], gv[1]), pack_bf16x2(gv[2], gv[3]));
-              *reinterpret_cast<uint2*>(gr + N) = make_uint2(pack_bf16x2(uv[0], uv[1]), pack_bf16x2(uv[2], uv[3]));
+              *reinterpret_cast<uint2*>(gr) = make_uint2(pack_bf16x2(acc[0][i][j][g * 4], acc[0][i][j][g * 4 + 1]),
+                                                         pack_bf16x2(acc[0][i][j][g * 4 + 2], acc[0][i][j][g * 4 + 3]));
+              *reinterpret_cast<uint2*>(gr + N) =
+                  make_uint2(pack_bf16x2(acc[C::HALVES - 1][i][j][g * 4], acc[C::HALVES - 1][i][j][g * 4 + 1]),
+                             pack_bf16x2(acc[C::HALVES - 1][i][j][g * 4 + 2], acc[C::HALVES - 1][i][j][g * 4 + 3]));
             }
           }
         }

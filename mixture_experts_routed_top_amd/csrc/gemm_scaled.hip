@@ -606,20 +606,38 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_scaled_kernel(Params p
       for (int i = 0; i < C::FM; ++i) {
         const int m = wm * C::TM + i * 32 + (lane & 31);
         const int sid = p.sorted_ids[row0 + m];
-        if (sid >= p.A) continue;
+        const bool row_ok = sid < p.A;
         const float fs = MODE == kFp8Block ? fprev[0][i] : 1.0f;
 #pragma unroll
-        for (int j = 0; j < C::FN; ++j)
+        for (int j = 0; j < C::FN; ++j) {
+          // lanes r and r + 32 hold columns 8g .. 8g + 3 and 8g + 4 .. 8g + 7 of
+          // the same row: one lane swap per word (v_permlane32_swap: the upper
+          // lanes' first operand for the lower lanes' second) leaves lane r
+          // groups 0, 1 and lane r + 32 groups 2, 3 whole, stored 16 bytes at
+          // a time (every lane takes part in the swap; pad rows store nothing)
+          uint32_t u[4][2], from_lo[2][2], from_hi[2][2];
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
-            const int n = n0 + wn * C::TN + j * 32 + g * 8 + (lane >> 5) * 4;
-            if (n < N) {
-              uint2 st;
-              st.x = pack_bf16x2(acc[0][i][j][4 * g] * fs, acc[0][i][j][4 * g + 1] * fs);
-              st.y = pack_bf16x2(acc[0][i][j][4 * g + 2] * fs, acc[0][i][j][4 * g + 3] * fs);
-              *reinterpret_cast<uint2*>(y + static_cast<int64_t>(sid) * N + n) = st;
-            }
+            u[g][0] = pack_bf16x2(acc[0][i][j][4 * g] * fs, acc[0][i][j][4 * g + 1] * fs);
+            u[g][1] = pack_bf16x2(acc[0][i][j][4 * g + 2] * fs, acc[0][i][j][4 * g + 3] * fs);
           }
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int w = 0; w < 2; ++w) {
+              const auto r = __builtin_amdgcn_permlane32_swap(u[q][w], u[q + 2][w], false, false);
+              from_lo[q][w] = r[0];
+              from_hi[q][w] = r[1];
+            }
+          const bool upper = lane >= 32;
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int n = n0 + wn * C::TN + j * 32 + (upper ? q + 2 : q) * 8;
+            const uint4 st = upper ? make_uint4(from_lo[q][0], from_lo[q][1], u[q + 2][0], u[q + 2][1])
+                                   : make_uint4(u[q][0], u[q][1], from_hi[q][0], from_hi[q][1]);
+            if (row_ok && n < N) *reinterpret_cast<uint4*>(y + static_cast<int64_t>(sid) * N + n) = st;   // N % 128 == 0
+          }
+        }
       }
     }
   }
