@@ -334,6 +334,39 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_bwd_kernel(Params p) {
       const int nl = wn * TN + j * 32 + (lane & 31);
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
+        if constexpr (MODE == kDx) {
+          // dx rows: lanes r and r + 32 hold the two 4-index halves of each
+          // 8-index group (the guard m < M is uniform per group, as M % 8 ==
+          // 0); one lane swap per word (v_permlane32_swap: the upper lanes'
+          // first operand for the lower lanes' second) leaves lane r groups 0,
+          // 1 and lane r + 32 groups 2, 3 whole, stored 16 bytes at a time
+          const int mb = m0 + wm * TM + i * 32;
+          const int sid = p.sorted_ids[row0 + nl];
+          uint32_t o[4][2], from_lo[2][2], from_hi[2][2];
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            o[g][0] = pack_bf16x2(acc[i][j][g * 4], acc[i][j][g * 4 + 1]);
+            o[g][1] = pack_bf16x2(acc[i][j][g * 4 + 2], acc[i][j][g * 4 + 3]);
+          }
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int w = 0; w < 2; ++w) {
+              const auto x = __builtin_amdgcn_permlane32_swap(o[q][w], o[q + 2][w], false, false);
+              from_lo[q][w] = x[0];
+              from_hi[q][w] = x[1];
+            }
+          const bool upper = lane >= 32;
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int m = mb + (upper ? q + 2 : q) * 8;
+            const uint4 st = upper ? make_uint4(from_lo[q][0], from_lo[q][1], o[q + 2][0], o[q + 2][1])
+                                   : make_uint4(o[q][0], o[q][1], from_hi[q][0], from_hi[q][1]);
+            if (m < p.M && sid < p.A)
+              *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + static_cast<int64_t>(sid) * p.M + m) = st;
+          }
+          continue;
+        }
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int m = m0 + wm * TM + i * 32 + g * 8 + (lane >> 5) * 4;

@@ -52,6 +52,22 @@ constexpr int kGroup = 4;       // m-tiles of one expert that walk the n-tiles s
 constexpr int kFp8Block = 1;
 constexpr int kMx = 2;
 
+// One row's 32 E4M3 codes of a 32-column fragment, held as in the MFMA
+// output: lane r (< 32) has columns 8g .. 8g + 3 in q[g], lane r + 32 has
+// columns 8g + 4 .. 8g + 7. One lane swap per pair of words
+// (v_permlane32_swap: the upper lanes' first operand for the lower lanes'
+// second) gives lane r columns 0 .. 15 and lane r + 32 columns 16 .. 31,
+// each stored with one 16-byte store at dst (16-byte aligned). Called by
+// every lane of the wave.
+__device__ __forceinline__ void store_codes_x32(uint8_t* dst, const uint32_t (&q)[4], int lane) {
+  const auto a = __builtin_amdgcn_permlane32_swap(q[0], q[2], false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(q[1], q[3], false, false);
+  if (lane < 32)
+    *reinterpret_cast<uint4*>(dst) = make_uint4(q[0], a[1], q[1], b[1]);
+  else
+    *reinterpret_cast<uint4*>(dst + 16) = make_uint4(a[0], q[2], b[0], q[3]);
+}
+
 template <int BM, int BN, int WM, int WN, bool GEMM1, int MODE, int NST_ = 2, int KSUB_ = 1>
 struct Cfg {
   static constexpr int NST = NST_;                          // LDS stages (2 or 4)
@@ -561,14 +577,14 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_scaled_kernel(Params p
           const float s = am > 0.0f ? __fdiv_rn(am, 448.0f) : 1.0f;
           const int64_t row = row0 + m;
 #pragma unroll
-          for (int j = 0; j < C::FN; ++j)
+          for (int j = 0; j < C::FN; ++j) {
+            uint32_t q[4];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const int n = n0 + wn * C::TN + j * 32 + g * 8 + (lane >> 5) * 4;
-              const uint32_t q = pack_e4m3x4(__fdiv_rn(hv[i][j][4 * g], s), __fdiv_rn(hv[i][j][4 * g + 1], s),
-                                             __fdiv_rn(hv[i][j][4 * g + 2], s), __fdiv_rn(hv[i][j][4 * g + 3], s));
-              *reinterpret_cast<uint32_t*>(hq + row * N + n) = q;
-            }
+            for (int g = 0; g < 4; ++g)
+              q[g] = pack_e4m3x4(__fdiv_rn(hv[i][j][4 * g], s), __fdiv_rn(hv[i][j][4 * g + 1], s),
+                                 __fdiv_rn(hv[i][j][4 * g + 2], s), __fdiv_rn(hv[i][j][4 * g + 3], s));
+            store_codes_x32(hq + row * N + n0 + wn * C::TN + j * 32, q, lane);
+          }
           if (wn == 0 && lane < 32) static_cast<float*>(p.out_scale)[row * (N / 128) + n0 / 128] = s;
         }
         __syncthreads();   // red is reused by the next task
@@ -589,13 +605,12 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_scaled_kernel(Params p
             const float inv = mx_inv_scale(x);
             const int nb = n0 + wn * C::TN + j * 32;
             if (nb >= N) continue;   // a ragged last column tile: whole 32-column fragments past I
+            uint32_t q[4];
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const int n = nb + g * 8 + (lane >> 5) * 4;
-              const uint32_t q = pack_e4m3x4(hv[i][j][4 * g] * inv, hv[i][j][4 * g + 1] * inv,
-                                             hv[i][j][4 * g + 2] * inv, hv[i][j][4 * g + 3] * inv);
-              *reinterpret_cast<uint32_t*>(hq + row * N + n) = q;
-            }
+            for (int g = 0; g < 4; ++g)
+              q[g] = pack_e4m3x4(hv[i][j][4 * g] * inv, hv[i][j][4 * g + 1] * inv, hv[i][j][4 * g + 2] * inv,
+                                 hv[i][j][4 * g + 3] * inv);
+            store_codes_x32(hq + row * N + nb, q, lane);
             if (lane < 32) static_cast<uint8_t*>(p.out_scale)[row * (N / 32) + nb / 32] = static_cast<uint8_t>(x + 127);
           }
         }
