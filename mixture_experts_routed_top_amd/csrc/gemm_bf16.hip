@@ -118,6 +118,11 @@ typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 // policy the compiler gives device-scope atomic loads and stores.
 constexpr int kDeviceScope = 16;
 
+// The fused combine's y rows: written through with device-scope stores (the
+// counts then only wait for the stores), or stored normally and made visible
+// by a device-scope release fence (which writes back the XCD's whole L2).
+constexpr bool kFuseWriteThrough = true;
+
 struct Params {
   const uint16_t* a;       // GEMM1: x [T, H]; GEMM2: h [cap, I]
   const uint16_t* w;       // GEMM1: W1 [E, 2I, H] (SwiGLU) or [E, I, H] (ReLU2); GEMM2: W2 [E, H, I]
@@ -155,7 +160,12 @@ __device__ __forceinline__ void fused_combine(const Params& p, int64_t row0, int
   constexpr int WAVES = THREADS / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = nt * BN;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  const __amdgpu_buffer_rsrc_t yrs = make_rsrc(p.out, static_cast<uint32_t>(p.A * N * 2));
+  if (kFuseWriteThrough) {
+    wait_vmcnt<0>();   // this wave's y rows went out with device-scope stores: they are now visible
+  } else {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  }
   __syncthreads();
   for (int r = tid; r < BM; r += THREADS) {
     const int sid = p.sorted_ids[row0 + r];
@@ -171,7 +181,8 @@ __device__ __forceinline__ void fused_combine(const Params& p, int64_t row0, int
     last_tok[r] = t;
   }
   __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  // the other workgroups' rows are read with device-scope loads (past any
+  // stale line in this XCD's L2), so no acquire fence invalidates the L2
   for (int r = wave; r < BM; r += WAVES) {
     const int t = last_tok[r];                 // the same for every lane of the wave
     if (t < 0) continue;
@@ -184,12 +195,12 @@ __device__ __forceinline__ void fused_combine(const Params& p, int64_t row0, int
       for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
       for (int j = 0; j < p.k; ++j) {
         const float wj = p.topk_w[a0 + j];
-        const uint4 q = *reinterpret_cast<const uint4*>(p.out + (a0 + j) * N + n);
-        const uint32_t w4[4] = {q.x, q.y, q.z, q.w};
+        const u32x4 q = __builtin_amdgcn_raw_buffer_load_b128(yrs, static_cast<uint32_t>(((a0 + j) * N + n) * 2), 0,
+                                                              kDeviceScope);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          acc[2 * i] = __builtin_fmaf(wj, __uint_as_float(w4[i] << 16), acc[2 * i]);
-          acc[2 * i + 1] = __builtin_fmaf(wj, __uint_as_float(w4[i] & 0xFFFF0000u), acc[2 * i + 1]);
+          acc[2 * i] = __builtin_fmaf(wj, __uint_as_float(q[i] << 16), acc[2 * i]);
+          acc[2 * i + 1] = __builtin_fmaf(wj, __uint_as_float(q[i] & 0xFFFF0000u), acc[2 * i + 1]);
         }
       }
       uint4 o;
@@ -564,7 +575,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
             const int n = n0 + wn * C::TN + j * 32 + (upper ? q + 2 : q) * 8;
             const uint4 st = upper ? make_uint4(from_lo[q][0], from_lo[q][1], u[q + 2][0], u[q + 2][1])
                                    : make_uint4(u[q][0], u[q][1], from_hi[q][0], from_hi[q][1]);
-            if (row_ok && n < N) *reinterpret_cast<uint4*>(p.out + dst_row * N + n) = st;   // N % 8 == 0
+            if (row_ok && n < N) {   // N % 8 == 0
+              if (FUSE && kFuseWriteThrough)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, st),
+                                                       make_rsrc(p.out, static_cast<uint32_t>(p.A * N * 2)),
+                                                       static_cast<uint32_t>((dst_row * N + n) * 2), 0, kDeviceScope);
+              else
+                *reinterpret_cast<uint4*>(p.out + dst_row * N + n) = st;
+            }
           }
         } else {
           // h: the activation of the four column groups, then the same lane

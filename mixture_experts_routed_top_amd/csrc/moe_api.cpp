@@ -406,6 +406,8 @@ moe_status_t moe_grouped_gemm_down_combine(int32_t dtype, const void* h, const v
                                    E, k, block_m, cap, y, nullptr, false))
     return st;
   if (dtype != MOE_DTYPE_BF16) return MOE_ERR_UNSUPPORTED_SHAPE;
+  // the kernel addresses y with 32-bit byte offsets
+  if (T * k * static_cast<int64_t>(H) * 2 >= (int64_t{1} << 31)) return MOE_ERR_UNSUPPORTED_SHAPE;
   if (T == 0) return MOE_OK;
   if (!topk_w || !out || !counters || !aligned(out, 16) || !aligned(topk_w, 4) || !aligned(counters, 4))
     return MOE_ERR_INVALID_ARG;
