@@ -373,7 +373,8 @@ size_t moe_down_combine_workspace_bytes(int64_t T, int32_t H);
  * top-k combine fused into its epilogue (TileScale PR #70, Design: "Kernel
  * 2" runs the L2 GEMM, the scatter to (token, slot) rows and the reduce).
  *
- * Writes y exactly as moe_grouped_gemm_down and, in the same launch,
+ * Writes y exactly as moe_grouped_gemm_down without a workspace (the last
+ * round of tiles is never split along K here) and, in the same launch,
  *   out[t, c] = bf16( sum_{j = 0..k-1} topk_w[t, j] * y[t*k + j, c] ),
  * the result moe_combine gives, bit for bit: the workgroup that stores the
  * last of a token's k rows for a block of columns sums that block in fp32 in
@@ -384,8 +385,9 @@ size_t moe_down_combine_workspace_bytes(int64_t T, int32_t H);
  *     must hold zeros before the call; every call leaves it zero again, so
  *     clear it once when it is allocated. Two calls that overlap in time must
  *     not share a workspace.
- * BF16 only (other dtypes -> MOE_ERR_UNSUPPORTED_SHAPE); other arguments and
- * errors as moe_grouped_gemm_down; a workspace below the size ->
+ * BF16 only, and y below 2 GiB (T * k * H * 2 bytes: the kernel addresses it
+ * with 32-bit offsets); otherwise MOE_ERR_UNSUPPORTED_SHAPE. Other arguments
+ * and errors as moe_grouped_gemm_down; a workspace below the size ->
  * MOE_ERR_WORKSPACE.
  */
 moe_status_t moe_grouped_gemm_down_combine(int32_t dtype, const void* h, const void* h_scale,
