@@ -83,3 +83,32 @@ def test_src_hash_ignores_comments(tmp_path, monkeypatch):
     assert bench._src_hash("k.hip") == h0
     (csrc / "k.hip").write_text("int a = 1;\nint b = 3;\n")
     assert bench._src_hash("k.hip") != h0
+
+
+def test_write_counters(tmp_path, monkeypatch):
+    """The SQ counter record: GRBM_GUI_ACTIVE summed over 8 XCDs gives the
+    clock over the dispatch time; MFMA busy over 1024 SIMDs, LDS activity
+    over 256 CUs; averaged over dispatches; ignored once the source changes."""
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "_src_hash", lambda fname: "h1")
+    name = "void moe::(anonymous namespace)::gemm_bf16_kernel<256, 128, 4, 2, true, 0, false>(Params)"
+    cyc = 900_000                      # per XCD: 2.0 GHz over a 450 us dispatch
+    vals = {"GRBM_GUI_ACTIVE": 8 * cyc, "SQ_VALU_MFMA_BUSY_CYCLES": 0.5 * cyc * 1024,
+            "SQ_INSTS_VALU_MFMA_MOPS_BF16": 1000.0, "SQ_INSTS_VALU_MFMA_MOPS_F8": 0.0,
+            "SQ_INSTS_VALU_MFMA_MOPS_F6F4": 0.0, "SQ_LDS_IDX_ACTIVE": 0.4 * cyc * 256,
+            "SQ_LDS_BANK_CONFLICT": 0.1 * cyc * 256, "SQ_BUSY_CU_CYCLES": 1.0}
+    lines = ['"Dispatch_Id","Kernel_Name","Counter_Name","Counter_Value","Start_Timestamp","End_Timestamp"']
+    for d in (1, 2):
+        lines += [f'{d},"{name}","{c}",{v},1000,{1000 + 450_000}' for c, v in vals.items()]
+    csv_path = tmp_path / "pmc_counter_collection.csv"
+    csv_path.write_text("\n".join(lines) + "\n")
+    bench.write_counters("qwen3_30b_a3b_bf16", str(csv_path), "the command")
+    rec = json.load(open(tmp_path / "profiles" / "gemm1_swiglu_qwen3_30b_a3b_bf16_sq_counters.json"))
+    assert rec["launches"] == 2 and rec["duration_us"] == 450.0
+    assert rec["clock_ghz"] == 2.0 and rec["mfma_busy"] == 0.5
+    assert rec["lds_active"] == 0.4 and rec["lds_bank_conflict_share"] == 0.25
+    assert rec["mfma_flop_counted"] == 512_000 and rec["command"] == "the command"
+    assert bench._counters("qwen3_30b_a3b_bf16", "gemm1_swiglu", 0)["mfma_busy"] == 0.5
+    monkeypatch.setattr(bench, "_src_hash", lambda fname: "h2")
+    assert bench._counters("qwen3_30b_a3b_bf16", "gemm1_swiglu", 0) is None
