@@ -31,26 +31,27 @@ __device__ __forceinline__ bool before(uint32_t ka, int ea, uint32_t kb, int eb)
 
 __device__ __forceinline__ int popc(uint64_t m) { return __popcll(m); }
 
-// DPP lane patterns (within each row of 16 lanes): swap neighbours, swap
-// pairs, mirror each half row, mirror the row.
+// DPP lane patterns: within each row of 16 lanes, swap neighbours, swap
+// pairs, mirror each half row, mirror the row; across rows, lane 15 of each
+// row to the next row, lane 31 to rows 2 and 3 (the row masks below pick
+// which rows take them).
 constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+constexpr int kDppBcast15 = 0x142, kDppBcast31 = 0x143;
 
-__device__ __forceinline__ int dpp_add(int v, int ctrl) {
-  switch (ctrl) {   // the control must be a constant of the instruction
-    case kDppXor1: return v + __builtin_amdgcn_update_dpp(0, v, kDppXor1, 0xF, 0xF, false);
-    case kDppXor2: return v + __builtin_amdgcn_update_dpp(0, v, kDppXor2, 0xF, 0xF, false);
-    case kDppHalfMirror: return v + __builtin_amdgcn_update_dpp(0, v, kDppHalfMirror, 0xF, 0xF, false);
-    default: return v + __builtin_amdgcn_update_dpp(0, v, kDppMirror, 0xF, 0xF, false);
-  }
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_add(int v) {
+  // rows outside ROW_MASK keep v (the moved value is not added there)
+  return v + __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
 }
 
 // Number of the wave's keys >= c (wave-uniform). Padding keys are 0, below
 // every c >= 1. With one or two keys a lane, one ballot and one scalar
 // popcount per key. With more, a lane counts its own keys and the counts
 // are added across lanes by DPP moves (quad swaps, then the half-row and row
-// mirrors leave the row's sum in every lane of a row of 16) and four lane
-// reads: one ballot per key would make the CU's single scalar unit the
-// bottleneck (8 keys a lane, 64 waves a CU, 32 rounds).
+// mirrors leave each row's sum in all its lanes; two row broadcasts then
+// leave the wave's sum in lane 63), read once: one ballot per key would make
+// the CU's single scalar unit the bottleneck (8 keys a lane, 64 waves a CU,
+// up to 32 rounds).
 template <int PER_LANE>
 __device__ __forceinline__ int count_ge(const uint32_t (&key)[PER_LANE], uint32_t c) {
   if constexpr (PER_LANE <= 2) {
@@ -62,12 +63,13 @@ __device__ __forceinline__ int count_ge(const uint32_t (&key)[PER_LANE], uint32_
     int n = 0;
 #pragma unroll
     for (int i = 0; i < PER_LANE; ++i) n += key[i] >= c ? 1 : 0;
-    n = dpp_add(n, kDppXor1);
-    n = dpp_add(n, kDppXor2);
-    n = dpp_add(n, kDppHalfMirror);
-    n = dpp_add(n, kDppMirror);
-    return __builtin_amdgcn_readlane(n, 0) + __builtin_amdgcn_readlane(n, 16) + __builtin_amdgcn_readlane(n, 32) +
-           __builtin_amdgcn_readlane(n, 48);
+    n = dpp_add<kDppXor1>(n);
+    n = dpp_add<kDppXor2>(n);
+    n = dpp_add<kDppHalfMirror>(n);
+    n = dpp_add<kDppMirror>(n);             // every lane: its row's sum
+    n = dpp_add<kDppBcast15, 0xA>(n);       // rows 1, 3: rows 0 + 1, rows 2 + 3
+    n = dpp_add<kDppBcast31, 0xC>(n);       // rows 2, 3: + rows 0 + 1 (row 3: all four)
+    return __builtin_amdgcn_readlane(n, 63);
   }
 }
 
