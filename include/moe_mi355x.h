@@ -260,14 +260,15 @@ moe_status_t moe_quantize_mxfp4(const uint16_t* in, int64_t rows, int64_t cols,
  * support (moe_pick_block_m returns one), else MOE_ERR_UNSUPPORTED_SHAPE.
  *
  * ws, ws_bytes: optional device workspace (NULL: none) of at least
- * moe_grouped_gemm_workspace_bytes() bytes, 256-byte aligned. Its first 4096
+ * moe_grouped_gemm_workspace_bytes() bytes, 256-byte aligned. Its first 8192
  * bytes are counters: zero them before the first use; every call that
  * completes leaves them zero again (the rest holds partial sums and needs no
- * clearing). With
- * it, the BF16 kernels balance their last round of tiles by splitting those
- * tiles' K sum in two halves computed by two workgroups and added in fp32
- * (a different summation order for those tiles; deterministic for a given
- * problem and device); the FP8 / MX kernels ignore it. Calls that may run at
+ * clearing). With it, the BF16 kernels hand out their tiles from per-XCD
+ * queues (workgroups that run faster take more tiles), and balance a short
+ * last round of tiles by splitting those tiles' K sum in two halves computed
+ * by two workgroups and added in fp32 (a different summation order for those
+ * tiles; deterministic for a given problem and device); the FP8 / MX kernels
+ * ignore it. Calls that may run at
  * the same time need workspaces of their own. ws_bytes too small ->
  * MOE_ERR_WORKSPACE; misaligned -> MOE_ERR_INVALID_ARG.
  */
@@ -281,9 +282,10 @@ moe_status_t moe_grouped_gemm_swiglu(int32_t dtype, const void* x, const void* x
 
 /*
  * moe_grouped_gemm_workspace_bytes -- host only. Bytes of the optional
- * workspace of the grouped GEMM calls on the current device: a counter per
- * split slot and two 256 x 256 fp32 partial tiles per slot, one slot per two
- * workgroups of the persistent grid (64 MiB on a 256-CU MI355X). Returns 0
+ * workspace of the grouped GEMM calls on the current device: 8192 bytes of
+ * counters (a counter per split slot, the per-XCD queues) and two 256 x 256
+ * fp32 partial tiles per slot, one slot per two workgroups of the persistent
+ * grid (64 MiB on a 256-CU MI355X). Returns 0
  * when no supported device is current. Not a passage of the pages: the
  * work-balance split is this implementation's.
  */

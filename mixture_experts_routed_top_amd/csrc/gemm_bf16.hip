@@ -137,6 +137,7 @@ struct Params {
   int32_t* counters;       //   [T, ceil(H / BN)] finished slots per (token, column tile); zero between calls
   int32_t* split_cnt;      // optional K-split of the last round: halves finished per slot; zero between calls
   float* split_part;       //   fp32 partial tiles, two per slot
+  int32_t* queue;          // optional per-XCD item queues (claimed, finished); zero between calls
   int64_t A;
   uint32_t a_bytes;        // bytes of the token operand (below 2^31)
   int H, I, k;
@@ -278,6 +279,17 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
   // 2j and 2j + 1 of the split range, k-steps [0, nk/2) and [nk/2, nk)), and
   // the workgroup that finishes second adds the two fp32 partial tiles and
   // runs the epilogue. Items are wave-uniform.
+  //
+  // With the workspace the items are also handed out dynamically: a
+  // workgroup's first item is `local`, every further one is claimed from its
+  // XCD's queue (an atomic counter) when the current item starts, so the
+  // claim's latency hides behind the k-loop and workgroups that run faster
+  // take more items, in the same order. Wave 0 makes the claim; the other
+  // waves read it from LDS after the k-loop. The last workgroup of an XCD to
+  // finish resets the XCD's counters for the next call; nothing waits.
+  const bool dyn = p.queue != nullptr;
+  int32_t* const qclaim = dyn ? p.queue + xcd * kQueueStride : nullptr;
+  int32_t* const qdone = dyn ? qclaim + kQueueStride / 2 : nullptr;
   const int64_t nslice = t1 - t0;
   const int64_t rounds = nslice / per_xcd, left = nslice - rounds * per_xcd;
   const bool split = p.split_cnt != nullptr && left > 0 && 2 * left <= per_xcd && nk >= kMinSplitSteps;
@@ -285,15 +297,19 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
   const int64_t nitems = split ? nfull + 2 * left : nslice;
   auto task_of = [&](int64_t it) { return t0 + (it < nfull ? it : nfull + (it - nfull) / 2); };
   int probe = local < nitems ? grouped_probe(task_of(local), ntn, num_tiles, p.tile_expert, lane) : 0;
-  for (int64_t it = local; it < nitems; it += per_xcd) {
+  int64_t it_next = 0;
+  for (int64_t it = local; it < nitems; it = it_next) {
     const int64_t task = task_of(it);
+    int32_t claimed = 0;   // wave 0, lane 0: the next item, per_xcd + the queue's count
+    if (dyn && tid == 0) claimed = __hip_atomic_fetch_add(qclaim, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const bool part = it >= nfull;                  // half of a split task
     const int khalf = part ? static_cast<int>((it - nfull) & 1) : 0;
     const int kb = khalf ? nk / 2 : 0;              // k-steps [kb, ke) of this item
     const int ke = part && khalf == 0 ? nk / 2 : nk;
     int nt, mt, e;
     grouped_task<kGroup>(task, ntn, num_tiles, p.tile_expert, lane, probe, nt, mt, e);
-    if (it + per_xcd < nitems) probe = grouped_probe(task_of(it + per_xcd), ntn, num_tiles, p.tile_expert, lane);
+    if (!dyn && it + per_xcd < nitems)
+      probe = grouped_probe(task_of(it + per_xcd), ntn, num_tiles, p.tile_expert, lane);
     const int64_t row0 = static_cast<int64_t>(mt) * BM;
     const int n0 = nt * BN;
 
@@ -466,6 +482,19 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
     // with LDS before the next task refills it
     wait_vmcnt<0>();
     barrier_no_fence();
+    if (dyn) {
+      // the claimed item, through wst2: the next item's first loads go to
+      // stage0, wst0 and wst1, and wst2 is refilled only after its first
+      // barrier, which every wave reaches after reading this
+      int32_t* const slot_next = reinterpret_cast<int32_t*>(wst2);
+      if (tid == 0) *slot_next = claimed;
+      __syncthreads();
+      const int32_t c = *slot_next;
+      it_next = c >= 0 ? per_xcd + static_cast<int64_t>(c) : nitems;   // (a counter never zeroed: stop)
+      if (it_next < nitems) probe = grouped_probe(task_of(it_next), ntn, num_tiles, p.tile_expert, lane);
+    } else {
+      it_next = it + per_xcd;
+    }
 
     if (part) {
       // Both halves store their partial tile (lane-major f32x4 rows: whole
@@ -647,6 +676,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
     }
     if constexpr (FUSE) fused_combine<BM, BN, C::THREADS>(p, row0, nt, ntn, N, reinterpret_cast<int32_t*>(stage1));
   }
+  // the last workgroup of the XCD to get here (every one has made its final,
+  // failing claim by then) resets the XCD's queue for the next call
+  if (dyn && tid == 0 &&
+      __hip_atomic_fetch_add(qdone, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == per_xcd - 1) {
+    __hip_atomic_store(qclaim, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(qdone, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 template <int BM, int BN, int WM, int WN, bool GEMM1, int ACT = kActSwiglu, bool FUSE = false>
@@ -667,7 +703,8 @@ hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s, const
   // the fused combine keeps whole tasks (its counters follow every tile's stores)
   static_assert(BM * C::HALVES * BN <= kSplitTileFloats, "a partial tile fits its workspace slot");
   p.split_cnt = !FUSE && g.split_ws ? static_cast<int32_t*>(g.split_ws) : nullptr;
-  p.split_part = !FUSE && g.split_ws ? reinterpret_cast<float*>(static_cast<char*>(g.split_ws) + kSplitCntBytes)
+  p.queue = !FUSE && g.split_ws ? reinterpret_cast<int32_t*>(static_cast<char*>(g.split_ws) + kQueueOffset) : nullptr;
+  p.split_part = !FUSE && g.split_ws ? reinterpret_cast<float*>(static_cast<char*>(g.split_ws) + kWsCounterBytes)
                                      : nullptr;
   p.A = g.T * g.k;
   p.a_bytes = static_cast<uint32_t>((GEMM1 ? g.T * g.H : g.cap * g.I) * 2);

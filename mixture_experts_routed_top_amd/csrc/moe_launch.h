@@ -56,21 +56,24 @@ struct GemmArgs {
   void* split_ws = nullptr;   // BF16, optional: K-split workspace (split_ws_bytes), counters zero between calls
 };
 
-// K-split of the last round of the BF16 grouped GEMMs (gemm_bf16.hip): the
-// workspace holds one int32 counter per slot (kSplitCntBytes), then two fp32
-// partial tiles per slot, each as large as the largest tile (256 x 256). A
-// split round holds at most half as many tasks as an XCD has workgroups, so
-// a grid of `grid` workgroups uses at most kSplitXcds * split_slots_per_xcd
-// slots.
+// Workspace of the BF16 grouped GEMMs (gemm_bf16.hip): one int32 counter per
+// K-split slot (the first 4096 bytes), the per-XCD item queues (a claim and
+// a finish counter per XCD, 128 bytes apart, from kQueueOffset), then two
+// fp32 partial tiles per slot, each as large as the largest tile (256 x 256),
+// from kWsCounterBytes. A split round holds at most half as many tasks as an
+// XCD has workgroups, so a grid of `grid` workgroups uses at most
+// kSplitXcds * split_slots_per_xcd slots.
 constexpr int kSplitXcds = 8;
 __host__ __device__ constexpr int split_slots_per_xcd(int grid) {
   return ((grid + kSplitXcds - 1) / kSplitXcds + 1) / 2;
 }
-constexpr size_t kSplitCntBytes = 4096;        // counters of grids up to 2048 workgroups
+constexpr size_t kQueueOffset = 4096;          // split counters of grids up to 2048 workgroups before it
+constexpr int kQueueStride = 32;               // int32 per XCD: claim at 0, finish at kQueueStride / 2
+constexpr size_t kWsCounterBytes = 8192;       // every counter; zero between calls
 constexpr size_t kSplitTileFloats = 256 * 256;
 constexpr int kSplitMaxGrid = 2048;
 inline size_t split_ws_bytes(int grid) {
-  return kSplitCntBytes +
+  return kWsCounterBytes +
          static_cast<size_t>(kSplitXcds) * split_slots_per_xcd(grid) * 2 * kSplitTileFloats * sizeof(float);
 }
 

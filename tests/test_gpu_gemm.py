@@ -517,7 +517,7 @@ def test_fp8_promotion_tiny_and_huge_blocks(bm):
 
 
 # ------------------------------------------------------------ K-split of a short last round (BF16)
-WS_COUNTER_BYTES = 4096   # the grouped-GEMM workspace starts with its split counters
+WS_COUNTER_BYTES = 8192   # the grouped-GEMM workspace starts with its counters (split slots, queues)
 SPLIT_SHAPES = [  # T, H, E, k, I; round-robin routing: 640 rows per expert, 3 tiles of 256 each (48 tiles)
     (2560, 512, 16, 4, 1024),    # GEMM1 (K = 512): 384 tasks, a last round of 16 per XCD of 32 workgroups
     (2560, 2048, 16, 4, 512),    # GEMM2 (K = 512): 384 tasks, likewise
