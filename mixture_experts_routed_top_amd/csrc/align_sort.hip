@@ -4,8 +4,8 @@
 // per-tile rescan of experts; Liger-Kernel PR #1463, Summary: empty experts
 // own no work).
 //
-// A deterministic counting sort in four launches (three for small problems,
-// where 2 and 3 run as one block):
+// A deterministic counting sort in four launches (two for small problems,
+// where 2-4 run as one: scan_scatter_kernel below):
 //   1. count_rank: each 1024-assignment chunk is split over 4 wavefronts; a
 //      wave ranks its 64 assignments at a time by matching equal expert ids
 //      with one ballot per id bit (a wave-wide "match any"), so each
@@ -156,67 +156,6 @@ __global__ __launch_bounds__(1024) void offsets_kernel(const int32_t* __restrict
   }
 }
 
-// scan_chunks and offsets in one block of 1024 threads, for small problems
-// (E * nchunks <= kOneBlockScan; a launch costs more than the work there):
-// P = 1024 / E threads per expert, each summing a contiguous run of chunks
-// (for one chunk the experts are contiguous, so the loads coalesce), then
-// the exclusive prefixes per chunk, the totals and the padded offsets.
-constexpr int kOneBlockScan = 4096;
-
-__global__ __launch_bounds__(1024) void scan_offsets_kernel(int32_t* __restrict__ chunk_counts, int nchunks, int E,
-                                                            int block_m, int32_t* __restrict__ counts,
-                                                            int32_t* __restrict__ offsets,
-                                                            int32_t* __restrict__ num_tiles) {
-  __shared__ int32_t part[1024];   // [p][e]: the run sum of thread (p, e)
-  __shared__ int sh[16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int P = 1;
-  while (P * 2 * E <= 1024) P *= 2;
-  const int e = tid % E, pp = tid / E;
-  const bool active = pp < P;
-  const int run = (nchunks + P - 1) / P;
-  const int c0 = pp * run, c1 = c0 + run < nchunks ? c0 + run : nchunks;
-  int sum = 0;
-  if (active)
-    for (int c = c0; c < c1; ++c) sum += chunk_counts[static_cast<int64_t>(c) * E + e];
-  if (active) part[pp * E + e] = sum;
-  __syncthreads();
-  if (active) {
-    int base = 0;
-    for (int q = 0; q < pp; ++q) base += part[q * E + e];
-    for (int c = c0; c < c1; ++c) {
-      const int64_t idx = static_cast<int64_t>(c) * E + e;
-      const int v = chunk_counts[idx];
-      chunk_counts[idx] = base;
-      base += v;
-    }
-  }
-  // totals, then the padded offsets over the experts (as offsets_kernel)
-  int tot = 0;
-  if (tid < E)
-    for (int q = 0; q < P; ++q) tot += part[q * E + tid];
-  if (tid < E) counts[tid] = tot;
-  const int pad = tid < E ? (tot + block_m - 1) / block_m * block_m : 0;
-  int inc = pad;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(inc, o);
-    if (lane >= o) inc += u;
-  }
-  if (lane == 63) sh[wave] = inc;
-  __syncthreads();
-  int wbase = 0, all = 0;
-  for (int w = 0; w < 16; ++w) {
-    if (w < wave) wbase += sh[w];
-    all += sh[w];
-  }
-  if (tid < E) offsets[tid] = wbase + inc - pad;
-  if (tid == 0) {
-    offsets[E] = all;
-    *num_tiles = all / block_m;
-  }
-}
-
 // Largest e in [0, E) with off[e] <= r (off non-decreasing, off[0] = 0 <= r).
 __device__ __forceinline__ int find_expert(const int32_t* off, int E, int r) {
   int lo = 0, hi = E - 1;
@@ -263,6 +202,102 @@ __global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict_
   if (i < cap / block_m) {
     const int r = static_cast<int>(i) * block_m;
     tile_expert[i] = r < total ? find_expert(off, E, r) : -1;
+  }
+}
+
+// Steps 2-4 in one launch, for small problems (E * nchunks <= kFusedScan,
+// where a launch costs more than the work): every block of 256 assignments
+// reads all the chunk counts (coalesced) and adds them into per-expert
+// totals and per-expert prefixes before its own chunk with LDS atomics
+// (integer sums: the order does not matter), scans the padded offsets, then
+// scatters like scatter_kernel. Block 0 writes counts, offsets, num_tiles.
+constexpr int kFusedScan = 2048;
+
+__global__ __launch_bounds__(256) void scan_scatter_kernel(const int32_t* __restrict__ ids,
+                                                           const int32_t* __restrict__ local_rank,
+                                                           const int32_t* __restrict__ chunk_counts, int nchunks,
+                                                           int64_t A, int E, int block_m, int64_t cap,
+                                                           int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ num_tiles,
+                                                           int32_t* __restrict__ sorted_ids,
+                                                           int32_t* __restrict__ tile_expert) {
+  __shared__ int32_t tot[kMaxE];
+  __shared__ int32_t pre[kMaxE];
+  __shared__ int32_t off[kMaxE + 1];
+  __shared__ int sh[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t i0 = static_cast<int64_t>(blockIdx.x) * 256;
+  const int cb = i0 < A ? static_cast<int>(i0 / kAlignChunk) : nchunks;   // this block's chunk (256 | 1024)
+  for (int e = tid; e < E; e += 256) {
+    tot[e] = 0;
+    pre[e] = 0;
+  }
+  __syncthreads();
+  const int n = E * nchunks;
+  for (int idx = tid; idx < n; idx += 256) {
+    const int c = idx / E, e = idx - c * E;
+    const int v = chunk_counts[idx];
+    if (v) {
+      atomicAdd(&tot[e], v);
+      if (c < cb) atomicAdd(&pre[e], v);
+    }
+  }
+  __syncthreads();
+  // exclusive scan of the padded counts over the experts, 4 a thread
+  int loc[4], sum = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid * 4 + q;
+    loc[q] = e < E ? (tot[e] + block_m - 1) / block_m * block_m : 0;
+    sum += loc[q];
+  }
+  int inc = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(inc, o);
+    if (lane >= o) inc += u;
+  }
+  if (lane == 63) sh[wave] = inc;
+  __syncthreads();
+  int wbase = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    if (w < wave) wbase += sh[w];
+    all += sh[w];
+  }
+  int run = wbase + inc - sum;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid * 4 + q;
+    if (e < E) off[e] = run;
+    run += loc[q];
+  }
+  if (tid == 0) off[E] = all;
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    for (int e = tid; e <= E; e += 256) {
+      offsets[e] = off[e];
+      if (e < E) counts[e] = tot[e];
+    }
+    if (tid == 0) *num_tiles = all / block_m;
+  }
+  const int64_t i = i0 + tid;
+  if (i < A) {
+    const int e = ids[i];
+    sorted_ids[off[e] + pre[e] + local_rank[i]] = static_cast<int32_t>(i);
+  }
+  if (i < cap) {
+    const int r = static_cast<int>(i);
+    bool pad = r >= all;
+    if (!pad) {
+      const int e = find_expert(off, E, r);
+      pad = r - off[e] >= tot[e];
+    }
+    if (pad) sorted_ids[r] = static_cast<int32_t>(A);
+  }
+  if (i < cap / block_m) {
+    const int r = static_cast<int>(i) * block_m;
+    tile_expert[i] = r < all ? find_expert(off, E, r) : -1;
   }
 }
 
@@ -317,15 +352,17 @@ hipError_t launch_align_sort(const int32_t* ids, int64_t T, int k, int E, int bl
   int32_t* chunk_counts = static_cast<int32_t*>(ws);
   int32_t* local_rank = chunk_counts + static_cast<int64_t>(nchunks) * E;
   count_rank_kernel<<<nchunks, 256, 0, s>>>(ids, A, E, bits_for(E), chunk_counts, local_rank);
-  if (static_cast<int64_t>(E) * nchunks <= kOneBlockScan) {
-    scan_offsets_kernel<<<1, 1024, 0, s>>>(chunk_counts, nchunks, E, block_m, counts, offsets, num_tiles);
+  const int64_t n = cap > A ? cap : A;
+  const unsigned blocks = static_cast<unsigned>((n + 255) / 256);
+  if (static_cast<int64_t>(E) * nchunks <= kFusedScan) {
+    scan_scatter_kernel<<<blocks, 256, 0, s>>>(ids, local_rank, chunk_counts, nchunks, A, E, block_m, cap, counts,
+                                               offsets, num_tiles, sorted_ids, tile_expert);
   } else {
     scan_chunks_kernel<<<E, 256, 0, s>>>(chunk_counts, nchunks, E, counts);
     offsets_kernel<<<1, 1024, 0, s>>>(counts, E, block_m, offsets, num_tiles);
+    scatter_kernel<<<blocks, 256, 0, s>>>(ids, local_rank, chunk_counts, counts, offsets, A, E, block_m, cap,
+                                          sorted_ids, tile_expert);
   }
-  const int64_t n = cap > A ? cap : A;
-  scatter_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(
-      ids, local_rank, chunk_counts, counts, offsets, A, E, block_m, cap, sorted_ids, tile_expert);
   return hipGetLastError();
 }
 
