@@ -211,6 +211,7 @@ struct Params {
   int64_t A;
   uint32_t a_rows;           // rows of the token operand (T for GEMM1, cap for GEMM2)
   int E, H, I, k;
+  int n_begin, n_end;        // the launch covers output columns [n_begin, n_end) (multiples of 128)
 };
 
 template <int BM, int BN, int WM, int WN, bool GEMM1, int MODE, int NST, int OCC, int KSUB>
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_scaled_kernel(Params p
   const int wm = wave / WN, wn = wave % WN;
   const int N = GEMM1 ? p.I : p.H;
   const int K = GEMM1 ? p.H : p.I;
-  const int ntn = (N + BN - 1) / BN;
+  const int ntn = (p.n_end - p.n_begin + BN - 1) / BN;
   const int num_tiles = *p.num_tiles;
   const int total = num_tiles * ntn;
   const int nk128 = K / 128;                         // 128-K substeps
@@ -271,7 +272,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_scaled_kernel(Params p
       e = p.tile_expert[mt];
     }
     const int64_t row0 = static_cast<int64_t>(mt) * BM;
-    const int n0 = nt * BN;
+    const int n0 = p.n_begin + nt * BN;
     const __amdgpu_buffer_rsrc_t w_rsrc =
         make_rsrc(p.w + static_cast<int64_t>(e) * wrows * wrow_bytes, static_cast<uint32_t>(wrows) * wrow_bytes);
     const __amdgpu_buffer_rsrc_t ws_rsrc =
@@ -662,7 +663,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_scaled_kernel(Params p
 // the weight stream, and a second workgroup per CU fills the gaps one
 // workgroup's pipeline leaves between tasks (LDS and registers must fit OCC)
 template <int BM, int BN, int WM, int WN, bool GEMM1, int MODE, int NST = 2, int OCC = 1, int KSUB = 1>
-hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
+hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s, int n_begin = 0, int n_end = -1) {
   using C = Cfg<BM, BN, WM, WN, GEMM1, MODE, NST, KSUB>;
   static_assert(OCC * (NST * C::STAGE + WN * BM * 4 + (NST > 2 ? 1024 : 0)) <= 160 * 1024, "OCC workgroups fit in LDS");
   Params p;
@@ -683,7 +684,9 @@ hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   p.I = g.I;
   p.k = g.k;
   const int N = GEMM1 ? g.I : g.H;
-  const int64_t max_tasks = (g.cap / BM) * ((N + BN - 1) / BN);
+  p.n_begin = n_begin;
+  p.n_end = n_end < 0 ? N : n_end;
+  const int64_t max_tasks = (g.cap / BM) * ((p.n_end - n_begin + BN - 1) / BN);
   int64_t grid = static_cast<int64_t>(dev.num_cus) * OCC;
   if (grid > max_tasks) grid = max_tasks;
   if (grid < 1) grid = 1;
@@ -694,7 +697,16 @@ hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
 hipError_t launch_gemm1_mx_tiles(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   switch (g.block_m) {
     case 256: return launch<256, 128, 4, 2, true, kMx>(g, dev, s);
-    case 128: return launch<128, 256, 4, 2, true, kMx>(g, dev, s);
+    case 128: {
+      // I % 256 == 128 (the MXFP4 shape's 640): the last 256-column tile
+      // would be half empty, a fifth of the MFMA work on zero weight rows;
+      // 128-column tiles take the last 128 columns in a second launch
+      // (same-process medians: T = 16384 827 -> 777 us, T = 8192 554 -> 524)
+      if (g.I % 256 == 0 || g.I < 256) return launch<128, 256, 4, 2, true, kMx>(g, dev, s);
+      const hipError_t e = launch<128, 256, 4, 2, true, kMx>(g, dev, s, 0, g.I - 128);
+      if (e != hipSuccess) return e;
+      return launch<128, 128, 4, 2, true, kMx>(g, dev, s, g.I - 128);
+    }
     case 64: return launch<64, 256, 1, 8, true, kMx>(g, dev, s);
     case 32: return launch<32, 256, 1, 8, true, kMx, 2, 1, 2>(g, dev, s);
     default: return hipErrorInvalidValue;

@@ -236,6 +236,9 @@ SCALED_SHAPES = [  # T, H, E, k, I, block_m
     (1, 256, 4, 2, 128, 32),
     (700, 1024, 8, 4, 384, 256),   # 256-row tiles: full and ragged tiles, partial column tiles
     (200, 640, 8, 2, 384, 32),     # 32-row tiles with an odd number of 128-K steps in both GEMMs
+    # 128-row tiles with I % 256 == 128: the MX GEMM1 takes the last 128 columns in a second launch
+    (300, 512, 8, 4, 384, 128),
+    (257, 1024, 16, 4, 640, 128),
 ]
 
 
