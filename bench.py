@@ -103,13 +103,19 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str, copy_mib: int, 
     w_fac = nbytes / (1024.0 * sum(copy_w) / len(copy_w))
     out = []
     for role in ("gemm1", "gemm2_down"):
-        fk = [v for k, vs in fetch.items() if _kernel_role(k) == role for v in vs]
-        wk = [v for k, vs in write.items() if _kernel_role(k) == role for v in vs]
+        # a GEMM call may launch more than one kernel (the MX GEMM1 covers its
+        # last 128 columns in a second launch): average each kernel over its
+        # dispatches, then add the kernels of one call
+        fks = {k: vs for k, vs in fetch.items() if _kernel_role(k) == role}
+        wks = {k: vs for k, vs in write.items() if _kernel_role(k) == role}
+        fk = [v for vs in fks.values() for v in vs]
+        wk = [v for vs in wks.values() for v in vs]
         if role == "gemm1":
             role = GEMM1_STAGE[cfg.act]
         if not fk or not wk:
             continue
-        f_kib, w_kib = sum(fk) / len(fk), sum(wk) / len(wk)
+        f_kib = sum(sum(vs) / len(vs) for vs in fks.values())
+        w_kib = sum(sum(vs) / len(vs) for vs in wks.values())
         rec = {"kernel": role, "workload": workload, "src_hash": _src_hash(KERNEL_SRC[role][cfg.dtype]),
                "fetch_kib_per_launch": round(f_kib, 1), "write_kib_per_launch": round(w_kib, 1),
                "copy_probe_bytes": nbytes, "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4),
@@ -155,18 +161,23 @@ def write_counters(workload: str, csv_path: str, command: str):
         role = _kernel_role(r["Kernel_Name"])
         if role is None:
             continue
-        d = per.setdefault(role, {}).setdefault(r["Dispatch_Id"], {})
+        d = per.setdefault(role, {}).setdefault(r["Kernel_Name"], {}).setdefault(r["Dispatch_Id"], {})
         d[r["Counter_Name"]] = float(r["Counter_Value"])
         d["_ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
     out = []
-    for role, disp in per.items():
+    for role, kernels in per.items():
         name = GEMM1_STAGE[cfg.act] if role == "gemm1" else role
-        avg = {c: sum(d[c] for d in disp.values()) / len(disp) for c in SQ_SET + ("_ns",)}
+        # one call may launch several kernels (see write_traffic): average each
+        # over its dispatches and add them, so every share below is of the
+        # call's total cycles
+        avg = {c: sum(sum(d[c] for d in disp.values()) / len(disp) for disp in kernels.values())
+               for c in SQ_SET + ("_ns",)}
+        disp = {k: d for kd in kernels.values() for k, d in kd.items()}
         cyc = avg["GRBM_GUI_ACTIVE"] / N_XCD
         mops = avg["SQ_INSTS_VALU_MFMA_MOPS_BF16"] + avg["SQ_INSTS_VALU_MFMA_MOPS_F8"] + \
             avg["SQ_INSTS_VALU_MFMA_MOPS_F6F4"]
         rec = {"kernel": name, "workload": workload, "src_hash": _src_hash(KERNEL_SRC[name][cfg.dtype]),
-               "launches": len(disp), "duration_us": round(avg["_ns"] / 1e3, 1),
+               "launches": len(disp), "kernels_per_call": len(kernels), "duration_us": round(avg["_ns"] / 1e3, 1),
                "clock_ghz": round(cyc / avg["_ns"], 3),
                "mfma_busy": round(avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * N_SIMD), 4),
                "mfma_flop_counted": int(mops * 512),

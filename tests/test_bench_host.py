@@ -112,3 +112,27 @@ def test_write_counters(tmp_path, monkeypatch):
     assert bench._counters("qwen3_30b_a3b_bf16", "gemm1_swiglu", 0)["mfma_busy"] == 0.5
     monkeypatch.setattr(bench, "_src_hash", lambda fname: "h2")
     assert bench._counters("qwen3_30b_a3b_bf16", "gemm1_swiglu", 0) is None
+
+
+def test_write_counters_adds_the_kernels_of_one_call(tmp_path, monkeypatch):
+    """A call that launches two kernels (the MX GEMM1's two column ranges):
+    each kernel is averaged over its dispatches and the two are added."""
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "_src_hash", lambda fname: "h1")
+    names = ["void moe::(anonymous namespace)::gemm_scaled_kernel<128, 256, 4, 2, true, 2, 2, 1, 1>(Params)",
+             "void moe::(anonymous namespace)::gemm_scaled_kernel<128, 128, 4, 2, true, 2, 2, 1, 1>(Params)"]
+    lines = ['"Dispatch_Id","Kernel_Name","Counter_Name","Counter_Value","Start_Timestamp","End_Timestamp"']
+    d = 0
+    for step in range(3):
+        for name, cyc, ns in ((names[0], 800_000, 400_000), (names[1], 200_000, 100_000)):
+            d += 1
+            for c in bench.SQ_SET:
+                v = {"GRBM_GUI_ACTIVE": 8 * cyc, "SQ_VALU_MFMA_BUSY_CYCLES": 0.5 * cyc * 1024}.get(c, 0.0)
+                lines.append(f'{d},"{name}","{c}",{v},0,{ns}')
+    csv_path = tmp_path / "p.csv"
+    csv_path.write_text("\n".join(lines) + "\n")
+    bench.write_counters("mxfp4_moe_t16384", str(csv_path), "cmd")
+    rec = json.load(open(tmp_path / "profiles" / "gemm1_swiglu_mxfp4_moe_t16384_sq_counters.json"))
+    assert rec["kernels_per_call"] == 2 and rec["launches"] == 6
+    assert rec["duration_us"] == 500.0 and rec["clock_ghz"] == 2.0 and rec["mfma_busy"] == 0.5
