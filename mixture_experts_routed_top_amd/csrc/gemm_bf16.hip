@@ -141,6 +141,7 @@ struct Params {
   int64_t A;
   uint32_t a_bytes;        // bytes of the token operand (below 2^31)
   int H, I, k;
+  int n_begin, n_end;      // the launch covers output columns [n_begin, n_end) (multiples of 8)
 };
 
 // The weighted top-k combine fused into GEMM2 (TileScale PR #70, Design:
@@ -160,7 +161,7 @@ __device__ __forceinline__ void fused_combine(const Params& p, int64_t row0, int
                                               int32_t* last_tok) {
   constexpr int WAVES = THREADS / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n0 = nt * BN;
+  const int n0 = p.n_begin + nt * BN;
   const __amdgpu_buffer_rsrc_t yrs = make_rsrc(p.out, static_cast<uint32_t>(p.A * N * 2));
   if (kFuseWriteThrough) {
     wait_vmcnt<0>();   // this wave's y rows went out with device-scope stores: they are now visible
@@ -247,7 +248,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
   }
   const int N = GEMM1 ? p.I : p.H;      // output columns
   const int K = GEMM1 ? p.H : p.I;      // reduction length
-  const int ntn = (N + BN - 1) / BN;
+  const int ntn = (p.n_end - p.n_begin + BN - 1) / BN;
   const int num_tiles = *p.num_tiles;
   const int total = num_tiles * ntn;
   const int nk = (K + BK - 1) / BK;
@@ -311,7 +312,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
     if (!dyn && it + per_xcd < nitems)
       probe = grouped_probe(task_of(it + per_xcd), ntn, num_tiles, p.tile_expert, lane);
     const int64_t row0 = static_cast<int64_t>(mt) * BM;
-    const int n0 = nt * BN;
+    const int n0 = p.n_begin + nt * BN;
 
     // source of every LDS row this lane fills: a byte offset into the token
     // operand (rows < BM) or into expert e's weights (kOob: zeros)
@@ -686,7 +687,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
 }
 
 template <int BM, int BN, int WM, int WN, bool GEMM1, int ACT = kActSwiglu, bool FUSE = false>
-hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s, const CombineArgs* cmb = nullptr) {
+hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s, const CombineArgs* cmb = nullptr,
+                  int n_begin = 0, int n_end = -1) {
   using C = Cfg<BM, BN, WM, WN, GEMM1, ACT>;
   Params p;
   p.topk_w = cmb ? cmb->topk_w : nullptr;
@@ -712,7 +714,9 @@ hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s, const
   p.I = g.I;
   p.k = g.k;
   const int N = GEMM1 ? g.I : g.H;
-  const int64_t max_tasks = (g.cap / BM) * ((N + BN - 1) / BN);
+  p.n_begin = n_begin;
+  p.n_end = n_end < 0 ? N : n_end;
+  const int64_t max_tasks = (g.cap / BM) * ((p.n_end - n_begin + BN - 1) / BN);
   int64_t grid = dev.num_cus;
   if (grid > max_tasks) grid = max_tasks;
   if (grid < 1) grid = 1;
@@ -723,6 +727,21 @@ hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s, const
 }  // namespace
 
 bool gemm_bf16_supports(int block_m) { return block_m == 32 || block_m == 64 || block_m == 128 || block_m == 256; }
+
+// A 256-row launch whose last column tile would be at most half full runs
+// the whole tiles first and the rest with tiles half as wide. Used for the
+// squared-ReLU GEMM1: at the Nemotron shape (I = 1856 = 7 x 256 + 64, T =
+// 8192) it took 591 us against 614 for one launch (same-process medians).
+// GEMM2 at H = 2688 = 10 x 256 + 128 was slower split (608 us against 597):
+// its last tile is half full, not a quarter, and the second launch's own
+// ramp-up and tail cost more than that saves.
+template <int BN, class Wide, class Narrow>
+hipError_t two_widths(int N, Wide wide, Narrow narrow) {
+  const int rem = N % BN;
+  if (N < BN || rem == 0 || rem > BN / 2) return wide(0, -1);
+  const hipError_t e = wide(0, N - rem);
+  return e != hipSuccess ? e : narrow(N - rem, N);
+}
 
 // Tiles: 256 rows x 128 output columns (128 gate + 128 up weight rows) for
 // the largest row tile; 128- and 64-row tiles keep 256 weight rows a
@@ -745,7 +764,10 @@ hipError_t launch_gemm1_bf16(const GemmArgs& g, const DeviceInfo& dev, hipStream
 // ReLU2: one projection per output column, so the tiles of GEMM2's shape
 hipError_t launch_gemm1_relu2_bf16(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   switch (g.block_m) {
-    case 256: return launch<256, 256, 4, 2, true, kActRelu2>(g, dev, s);
+    case 256:
+      return two_widths<256>(
+          g.I, [&](int a, int b) { return launch<256, 256, 4, 2, true, kActRelu2>(g, dev, s, nullptr, a, b); },
+          [&](int a, int b) { return launch<256, 128, 4, 2, true, kActRelu2>(g, dev, s, nullptr, a, b); });
     case 128: return launch<128, 256, 2, 4, true, kActRelu2>(g, dev, s);
     case 64: return launch<64, 256, 2, 4, true, kActRelu2>(g, dev, s);
     case 32: return launch<32, 256, 1, 4, true, kActRelu2>(g, dev, s);

@@ -86,6 +86,9 @@ SHAPES = [  # T, H, E, k, I, block_m
     (260, 64, 4, 2, 200, 256),
     (300, 120, 4, 2, 312, 256),
     (280, 448, 4, 2, 64, 256),
+    # 256-row tiles, I % 256 == 64: the squared-ReLU GEMM1 covers the last
+    # 64 columns with a second launch of 128-column tiles
+    (300, 640, 8, 4, 320, 256),
 ]
 
 
