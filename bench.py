@@ -103,9 +103,9 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str, copy_mib: int, 
     w_fac = nbytes / (1024.0 * sum(copy_w) / len(copy_w))
     out = []
     for role in ("gemm1", "gemm2_down"):
-        # a GEMM call may launch more than one kernel (the MX GEMM1 covers its
-        # last 128 columns in a second launch): average each kernel over its
-        # dispatches, then add the kernels of one call
+        # a GEMM call may launch more than one kernel (the MX GEMM1 and the
+        # BF16 squared-ReLU GEMM1 cover their last columns in a second launch):
+        # average each kernel over its dispatches, then add the kernels of one call
         fks = {k: vs for k, vs in fetch.items() if _kernel_role(k) == role}
         wks = {k: vs for k, vs in write.items() if _kernel_role(k) == role}
         fk = [v for vs in fks.values() for v in vs]
