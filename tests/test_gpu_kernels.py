@@ -201,7 +201,10 @@ def test_mx_quant_random_matches_oracle(rows, cols, std):
 
 
 # ------------------------------------------------------------------ combine
-@pytest.mark.parametrize("T,k,H", [(129, 8, 2048), (1, 1, 8), (64, 2, 256), (37, 10, 2560), (3, 32, 7168)])
+@pytest.mark.parametrize("T,k,H", [(129, 8, 2048), (1, 1, 8), (64, 2, 256), (37, 10, 2560), (3, 32, 7168),
+                                   # every slot count from 3 to 9 (the kernel is specialised for k <= 10)
+                                   (17, 3, 1024), (17, 4, 1024), (19, 5, 512), (50, 6, 2688), (11, 7, 256),
+                                   (21, 9, 2048)])
 def test_combine_matches_oracle(T, k, H):
     rng = np.random.default_rng(T * k)
     y = f64(_bf16_tensor(rng.standard_normal((T * k, H))))
