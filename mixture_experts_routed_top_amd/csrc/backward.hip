@@ -18,6 +18,15 @@ namespace moe {
 
 namespace {
 
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+
+// 16 bytes of a row that is read once: a non-temporal load keeps it from
+// displacing lines that are read again (dout, read by all k rows of a token)
+__device__ __forceinline__ uint4 load_stream(const uint16_t* p) {
+  const u32x4v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // one wave per sorted row; each lane handles 8 consecutive columns per pass
 __global__ __launch_bounds__(256) void backward_combine_kernel(const uint16_t* __restrict__ dout,
                                                                const float* __restrict__ w,
@@ -44,7 +53,7 @@ __global__ __launch_bounds__(256) void backward_combine_kernel(const uint16_t* _
 #pragma unroll 4
   for (int c = lane * 8; c < H; c += 512) {
     const uint4 dq = *reinterpret_cast<const uint4*>(dr + c);
-    const uint4 yq = *reinterpret_cast<const uint4*>(yr + c);
+    const uint4 yq = load_stream(yr + c);
     const uint32_t dv[4] = {dq.x, dq.y, dq.z, dq.w}, yv[4] = {yq.x, yq.y, yq.z, yq.w};
     uint32_t o[4];
 #pragma unroll

@@ -8,13 +8,24 @@
 // The sum runs in fp32 in slot order with one fused multiply-add per slot.
 // For k up to 10 the slot count is a template argument and every slot row's
 // load is issued before the first is used (k loads in flight per thread,
-// instead of one load and its full latency per slot).
+// instead of one load and its full latency per slot). The y rows are read
+// once: non-temporal loads keep them from displacing other lines in the
+// caches (Qwen3-30B-A3B shape 54.2 -> 49.3 us, FP8 H 7168 shape 208 -> 177
+// us; non-temporal stores of the output measured slower and are not used).
 #include "moe_common.cuh"
 #include "moe_launch.h"
 
 namespace moe {
 
 namespace {
+
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+
+// 16 bytes of a y row, read once
+__device__ __forceinline__ uint4 load_stream(const uint16_t* p) {
+  const u32x4v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
 
 // KS > 0: k == KS, known at compile time; KS == 0: any k
 template <int KS>
@@ -45,13 +56,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
       float wj[KS];
 #pragma unroll
       for (int j = 0; j < KS; ++j) {
-        q[j] = *reinterpret_cast<const uint4*>(yrow + static_cast<int64_t>(j) * H);
+        q[j] = load_stream(yrow + static_cast<int64_t>(j) * H);
         wj[j] = w[t * KS + j];
       }
 #pragma unroll
       for (int j = 0; j < KS; ++j) add(wj[j], q[j]);
     } else {
-      for (int j = 0; j < k; ++j) add(w[t * k + j], *reinterpret_cast<const uint4*>(yrow + static_cast<int64_t>(j) * H));
+      for (int j = 0; j < k; ++j) add(w[t * k + j], load_stream(yrow + static_cast<int64_t>(j) * H));
     }
     uint4 o;
     o.x = pack_bf16x2(acc[0], acc[1]);
