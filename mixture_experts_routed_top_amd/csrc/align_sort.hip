@@ -5,7 +5,8 @@
 // own no work).
 //
 // A deterministic counting sort in four launches (two for small problems,
-// where 2-4 run as one: scan_scatter_kernel below):
+// where 2-4 run as one: scan_scatter_kernel below; one workgroup for at most
+// 2048 assignments: one_block_kernel, the same steps in LDS):
 //   1. count_rank: each 1024-assignment chunk is split over 4 wavefronts; a
 //      wave ranks its 64 assignments at a time by matching equal expert ids
 //      with one ballot per id bit (a wave-wide "match any"), so each
@@ -301,6 +302,125 @@ __global__ __launch_bounds__(256) void scan_scatter_kernel(const int32_t* __rest
   }
 }
 
+// The whole sort in one workgroup, for at most kOneBlockMaxA assignments
+// (2048: one launch instead of two pays only while one CU finishes the work
+// quickly; the MXFP4 512-expert shape at T = 128, 1280 assignments, took
+// 11.5 against 14.5 us, but at 8192 and 10240 assignments it was 1.7-3 us
+// slower than the two launches):
+// each of the 16 waves ranks a contiguous share (up to 16 groups of 64, the
+// same ballot match as count_rank_kernel) and keeps ranks and experts in
+// registers; the per-wave counts are scanned over the waves (each wave's
+// base inside its expert) and the padded totals over the experts, all in
+// LDS; then every wave scatters its share, each expert's thread writes its
+// tiles of the tile queue, the pad rows are spread over all threads, and the
+// rows and tiles past the last tile are filled. The result is the same
+// stable order.
+constexpr int kOneBlockWaves = 16, kOneBlockGroups = 2;
+constexpr int64_t kOneBlockMaxA = int64_t{kOneBlockWaves} * kOneBlockGroups * 64;
+
+__global__ __launch_bounds__(1024) void one_block_kernel(const int32_t* __restrict__ ids, int A, int E, int nbits,
+                                                         int block_m, int cap, int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ num_tiles,
+                                                         int32_t* __restrict__ sorted_ids,
+                                                         int32_t* __restrict__ tile_expert) {
+  __shared__ int32_t wcnt[kOneBlockWaves][kMaxE];   // per-wave counts, then per-wave bases
+  __shared__ int32_t off[kMaxE + 1];
+  __shared__ int32_t tot[kMaxE];
+  __shared__ int sh[kOneBlockWaves];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int e = tid; e < E; e += 1024)
+#pragma unroll
+    for (int w = 0; w < kOneBlockWaves; ++w) wcnt[w][e] = 0;
+  __syncthreads();
+
+  // this wave's share: [lo, hi), a multiple of 64 long
+  const int per = ((A + kOneBlockWaves - 1) / kOneBlockWaves + 63) / 64 * 64;
+  const int lo = wave * per, hi = lo + per < A ? lo + per : A;
+  int r[kOneBlockGroups], ex[kOneBlockGroups];
+  // every id of the share is loaded before the first is used: one load
+  // latency for the wave, not one per group
+#pragma unroll
+  for (int g = 0; g < kOneBlockGroups; ++g) {
+    const int a = lo + g * 64 + lane;
+    ex[g] = g * 64 < per && a < hi ? ids[a] : 0;
+  }
+#pragma unroll
+  for (int g = 0; g < kOneBlockGroups; ++g) {
+    r[g] = 0;
+    if (g * 64 < per) {
+      const int a = lo + g * 64 + lane;
+      const bool valid = a < hi;
+      const int e = ex[g];
+      uint64_t m = __ballot(valid);
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t bb = __ballot(bit);
+        m &= bit ? bb : ~bb;
+      }
+      const int rk = rank_below(m);
+      const int b0 = valid ? wcnt[wave][e] : 0;
+      r[g] = b0 + rk;
+      if (valid && rk == 0) wcnt[wave][e] = b0 + __popcll(m);  // one writer per distinct expert
+    }
+  }
+  __syncthreads();
+  // each expert: exclusive prefix over the waves, and its total
+  for (int e = tid; e < E; e += 1024) {
+    int run = 0;
+#pragma unroll
+    for (int w = 0; w < kOneBlockWaves; ++w) {
+      const int c = wcnt[w][e];
+      wcnt[w][e] = run;
+      run += c;
+    }
+    tot[e] = run;
+  }
+  __syncthreads();
+  // padded offsets: exclusive scan over the experts (E <= 1024, one a thread)
+  const int p = tid < E ? (tot[tid] + block_m - 1) / block_m * block_m : 0;
+  int inc = p;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(inc, o);
+    if (lane >= o) inc += u;
+  }
+  if (lane == 63) sh[wave] = inc;
+  __syncthreads();
+  int wbase = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kOneBlockWaves; ++w) {
+    if (w < wave) wbase += sh[w];
+    all += sh[w];
+  }
+  if (tid < E) off[tid] = wbase + inc - p;
+  if (tid == 0) off[E] = all;
+  __syncthreads();
+
+#pragma unroll
+  for (int g = 0; g < kOneBlockGroups; ++g) {
+    const int a = lo + g * 64 + lane;
+    if (g * 64 < per && a < hi) sorted_ids[off[ex[g]] + wcnt[wave][ex[g]] + r[g]] = a;
+  }
+  for (int e = tid; e < E; e += 1024) {
+    counts[e] = tot[e];
+    offsets[e] = off[e];
+    for (int t = off[e] / block_m; t < off[e + 1] / block_m; ++t) tile_expert[t] = e;
+  }
+  // pad rows: slot j of expert e (j < block_m - 1) is row off[e] + tot[e] + j
+  // if that is below off[e + 1]; spread over all threads
+  for (int i = tid; i < E * (block_m - 1); i += 1024) {
+    const int e = i / (block_m - 1), row = off[e] + tot[e] + (i - e * (block_m - 1));
+    if (row < off[e + 1]) sorted_ids[row] = A;
+  }
+  for (int row = all + tid; row < cap; row += 1024) sorted_ids[row] = A;
+  for (int t = all / block_m + tid; t < cap / block_m; t += 1024) tile_expert[t] = -1;
+  if (tid == 0) {
+    offsets[E] = all;
+    *num_tiles = all / block_m;
+  }
+}
+
 int bits_for(int E) {
   int b = 0;
   while ((1 << b) < E) ++b;
@@ -348,6 +468,11 @@ hipError_t launch_align_sort(const int32_t* ids, int64_t T, int k, int E, int bl
                              int32_t* offsets, int32_t* sorted_ids, int32_t* tile_expert,
                              int32_t* num_tiles, int64_t cap, void* ws, hipStream_t s) {
   const int64_t A = T * k;
+  if (A <= kOneBlockMaxA) {
+    one_block_kernel<<<1, 1024, 0, s>>>(ids, static_cast<int>(A), E, bits_for(E), block_m, static_cast<int>(cap),
+                                        counts, offsets, num_tiles, sorted_ids, tile_expert);
+    return hipGetLastError();
+  }
   const int nchunks = static_cast<int>((A + kAlignChunk - 1) / kAlignChunk);
   int32_t* chunk_counts = static_cast<int32_t*>(ws);
   int32_t* local_rank = chunk_counts + static_cast<int64_t>(nchunks) * E;

@@ -99,7 +99,9 @@ def test_align_sort_matches_oracle(name, bm):
 @pytest.mark.parametrize("T,E,k", [(1, 8, 2), (511, 4, 2), (512, 4, 2), (513, 4, 2), (1023, 1, 1),
                                    (1025, 3, 1), (40, 1024, 7), (3000, 512, 10),
                                    # at 16384 assignments and just past it
-                                   (2048, 128, 8), (2049, 128, 8), (16384, 1024, 1), (16385, 7, 1)])
+                                   (2048, 128, 8), (2049, 128, 8), (16384, 1024, 1), (16385, 7, 1),
+                                   # at 2048 assignments (the one-workgroup sort) and just past it
+                                   (256, 64, 8), (257, 64, 8), (2048, 1024, 1), (683, 3, 3)])
 def test_align_sort_edges(T, E, k):
     rng = np.random.default_rng(T + E)
     ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
