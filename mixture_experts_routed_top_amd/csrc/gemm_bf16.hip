@@ -312,6 +312,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
     if (!dyn && it + per_xcd < nitems)
       probe = grouped_probe(task_of(it + per_xcd), ntn, num_tiles, p.tile_expert, lane);
     const int64_t row0 = static_cast<int64_t>(mt) * BM;
+    // GEMM2: the destination rows of this lane's stores, loaded with the
+    // task's first operand loads, so that the epilogue does not start with a
+    // round trip (GEMM2 1-2% faster on the Qwen3, Scout and Nemotron shapes)
+    int out_sid[C::FM];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) out_sid[i] = GEMM1 ? 0 : p.sorted_ids[row0 + wm * C::TM + i * 32 + (lane & 31)];
     const int n0 = p.n_begin + nt * BN;
 
     // source of every LDS row this lane fills: a byte offset into the token
@@ -573,7 +579,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_bf16_kernel(Params p) {
         dst_row = row0 + m;
         row_ok = true;
       } else {
-        const int sid = p.sorted_ids[row0 + m];
+        const int sid = out_sid[i];
         row_ok = sid < p.A;
         dst_row = sid;
       }
