@@ -273,6 +273,11 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_scaled_kernel(Params p
     }
     const int64_t row0 = static_cast<int64_t>(mt) * BM;
     const int n0 = p.n_begin + nt * BN;
+    // GEMM2: the destination rows of this lane's stores, loaded ahead of the
+    // task's operand loads so that the epilogue does not start with a round trip
+    int out_sid[C::FM];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i) out_sid[i] = GEMM1 ? 0 : p.sorted_ids[row0 + wm * C::TM + i * 32 + (lane & 31)];
     const __amdgpu_buffer_rsrc_t w_rsrc =
         make_rsrc(p.w + static_cast<int64_t>(e) * wrows * wrow_bytes, static_cast<uint32_t>(wrows) * wrow_bytes);
     const __amdgpu_buffer_rsrc_t ws_rsrc =
@@ -621,7 +626,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_scaled_kernel(Params p
 #pragma unroll
       for (int i = 0; i < C::FM; ++i) {
         const int m = wm * C::TM + i * 32 + (lane & 31);
-        const int sid = p.sorted_ids[row0 + m];
+        const int sid = out_sid[i];
         const bool row_ok = sid < p.A;
         const float fs = MODE == kFp8Block ? fprev[0][i] : 1.0f;
 #pragma unroll
