@@ -1,7 +1,7 @@
 """moe_align_sort_noalloc (the allocation-free align_sort, fixed scratch)
 through the C ABI: its outputs equal moe_align_sort's (workspace from the
-caller) and the oracle's, bit for bit, on two calls in a row, the second with
-a smaller problem that reuses the scratch the first left behind."""
+caller) and the oracle's, bit for bit, on calls in a row, each with a smaller
+problem that reuses the scratch the one before left behind."""
 import numpy as np
 import pytest
 import torch
@@ -27,8 +27,9 @@ def _filled(sort: M.SortResult, value: int) -> M.SortResult:
 
 
 def test_align_sort_noalloc_matches_workspace_call():
-    # the second problem is smaller in T, k and E and uses another row tile
-    for T, E, k, bm, seed in [(16384, 512, 10, 64, 1), (700, 64, 4, 32, 2)]:
+    # each problem is smaller in T, k and E than the one before and uses another row tile;
+    # the last (1600 assignments) takes the one-workgroup sort
+    for T, E, k, bm, seed in [(16384, 512, 10, 64, 1), (700, 64, 4, 32, 2), (200, 32, 8, 16, 3)]:
         ids = _ids(T, E, k, seed)
         dids = torch.from_numpy(ids).to(DEV)
         say("align_sort_noalloc", T, E, k, bm)
