@@ -3,7 +3,12 @@
 // Selection is a radix select on order-preserving integer keys of the fp32
 // logits: 32 counting rounds find the k-th largest key, the k winners are the keys above it plus the lowest-index keys
 // equal to it, and one compaction through LDS puts them in slot order (logit
-// descending, equal logits -> lower expert index). The gate weights are the
+// descending, equal logits -> lower expert index). With more than 128
+// experts the select runs on a few candidates instead of every key: the k-th
+// largest of the 64 lanes' maxima is a lower bound of the k-th largest key
+// (k lanes hold a key at least that large), so every winner is among the
+// keys at or above it; when those are at most 64 (about k + 1 for random
+// logits) they are gathered in expert order, one a lane, and selected there. The gate weights are the
 // softmax over the selected logits, summed in slot order, or the sigmoid of
 // each selected logit, both in double precision and rounded once to fp32 (TileScale PR #70, Design: routing precedes the expert
 // GEMMs; the renormalised top-k softmax equals a softmax over the k selected
@@ -81,6 +86,9 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void route_kernel(const float*
   __shared__ uint32_t s_key[kWavesPerBlock][32];
   __shared__ int s_e[kWavesPerBlock][32];
   __shared__ float s_v[kWavesPerBlock][32];
+  __shared__ uint32_t s_ck[kWavesPerBlock][64];   // candidates (more than 128 experts)
+  __shared__ int s_ce[kWavesPerBlock][64];
+  __shared__ float s_cv[kWavesPerBlock][64];
   const int lane = threadIdx.x & 63, wib = threadIdx.x >> 6;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wib;
   if (t >= T) return;  // whole wave leaves together; no workgroup barrier below
@@ -98,39 +106,106 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void route_kernel(const float*
     key[i] = ok[i] ? order_key(val[i]) : 0u;   // padding: below every candidate tau | bit
   }
 
-  // the k-th largest key: the largest tau with #{key >= tau} >= k. Once a
-  // candidate has exactly k keys at or above it, those keys are the winners
-  // and the lower bits cannot change the selection below (every key equal to
-  // tau is then taken), so the search stops there: after about 15 of the 32
-  // rounds for distinct random logits.
-  uint32_t tau = 0;
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t cand = tau | (1u << b);
-    const int n = count_ge<PER_LANE>(key, cand);
-    if (n >= k) tau = cand;
-    if (n == k) break;
-  }
-  // winners: every key above tau, then the lowest-index keys equal to tau
-  int n_gt = 0;
+  // the k winners go to s_key / s_e / s_v (any order)
+  bool done = false;
+  if constexpr (PER_LANE >= 4) {
+    // lower bound: the k-th largest lane maximum (every lane holds a real
+    // key, and padding keys are 0, so a lane's maximum is one of its real
+    // keys and at least k real keys lie at or above the bound)
+    uint32_t lm = key[0];
 #pragma unroll
-  for (int i = 0; i < PER_LANE; ++i) n_gt += popc(__ballot(ok[i] && key[i] > tau));
-  const int n_eq_take = k - n_gt;
-  int eq_before = 0, sel_before = 0;
-#pragma unroll
-  for (int i = 0; i < PER_LANE; ++i) {
-    const uint64_t eq = __ballot(ok[i] && key[i] == tau);
-    const bool take_eq = ((eq >> lane) & 1ull) && eq_before + popc(eq & lt_mask) < n_eq_take;
-    eq_before += popc(eq);
-    const bool sel = (ok[i] && key[i] > tau) || take_eq;
-    const uint64_t sm = __ballot(sel);
-    if (sel) {
-      // compact in expert order: position among the winners
-      const int pos = sel_before + popc(sm & lt_mask);
-      s_key[wib][pos] = key[i];
-      s_e[wib][pos] = lane + 64 * i;
-      s_v[wib][pos] = val[i];
+    for (int i = 1; i < PER_LANE; ++i) lm = key[i] > lm ? key[i] : lm;
+    uint32_t t0 = 0;
+    for (int b = 31; b >= 0; --b) {
+      const uint32_t cand = t0 | (1u << b);
+      const int n = popc(__ballot(lm >= cand));
+      if (n >= k) t0 = cand;
+      if (n == k) break;
     }
-    sel_before += popc(sm);
+    uint64_t m[PER_LANE];
+    int total = 0;
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i) {
+      m[i] = __ballot(ok[i] && key[i] >= t0);
+      total += popc(m[i]);
+    }
+    if (total <= 64) {
+      // gather the candidates in expert order (slot-major: expert lane + 64 i)
+      int before = 0;
+#pragma unroll
+      for (int i = 0; i < PER_LANE; ++i) {
+        if ((m[i] >> lane) & 1ull) {
+          const int pos = before + popc(m[i] & lt_mask);
+          s_ck[wib][pos] = key[i];
+          s_ce[wib][pos] = lane + 64 * i;
+          s_cv[wib][pos] = val[i];
+        }
+        before += popc(m[i]);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const bool has = lane < total;
+      const uint32_t ck = has ? s_ck[wib][lane] : 0u;
+      const int ce = has ? s_ce[wib][lane] : 0;
+      const float cv = has ? s_cv[wib][lane] : 0.0f;
+      uint32_t tau = 0;
+      for (int b = 31; b >= 0; --b) {
+        const uint32_t cand = tau | (1u << b);
+        const int n = popc(__ballot(ck >= cand));
+        if (n >= k) tau = cand;
+        if (n == k) break;
+      }
+      // winners: every candidate above tau, then the first (lowest-expert) ones equal to it
+      const int n_gt = popc(__ballot(has && ck > tau));
+      const uint64_t eq = __ballot(has && ck == tau);
+      const bool take_eq = ((eq >> lane) & 1ull) && popc(eq & lt_mask) < k - n_gt;
+      const bool sel = (has && ck > tau) || take_eq;
+      const uint64_t sm = __ballot(sel);
+      if (sel) {
+        const int pos = popc(sm & lt_mask);
+        s_key[wib][pos] = ck;
+        s_e[wib][pos] = ce;
+        s_v[wib][pos] = cv;
+      }
+      done = true;
+    }
+  }
+  if (!done) {
+    // the k-th largest key: the largest tau with #{key >= tau} >= k. Once a
+    // candidate has exactly k keys at or above it, those keys are the winners
+    // and the lower bits cannot change the selection below (every key equal to
+    // tau is then taken), so the search stops there: after about 15 of the 32
+    // rounds for distinct random logits.
+    uint32_t tau = 0;
+    for (int b = 31; b >= 0; --b) {
+      const uint32_t cand = tau | (1u << b);
+      const int n = count_ge<PER_LANE>(key, cand);
+      if (n >= k) tau = cand;
+      if (n == k) break;
+    }
+    // winners: every key above tau, then the lowest-index keys equal to tau
+    int n_gt = 0;
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i) n_gt += popc(__ballot(ok[i] && key[i] > tau));
+    const int n_eq_take = k - n_gt;
+    int eq_before = 0, sel_before = 0;
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i) {
+      const uint64_t eq = __ballot(ok[i] && key[i] == tau);
+      const bool take_eq = ((eq >> lane) & 1ull) && eq_before + popc(eq & lt_mask) < n_eq_take;
+      eq_before += popc(eq);
+      const bool sel = (ok[i] && key[i] > tau) || take_eq;
+      const uint64_t sm = __ballot(sel);
+      if (sel) {
+        // compact in expert order: position among the winners
+        const int pos = sel_before + popc(sm & lt_mask);
+        s_key[wib][pos] = key[i];
+        s_e[wib][pos] = lane + 64 * i;
+        s_v[wib][pos] = val[i];
+      }
+      sel_before += popc(sm);
+    }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();

@@ -54,6 +54,42 @@ def test_route_edges_and_ties(T, E, k, score):
     assert_route_weights(w.cpu().numpy(), rw)
 
 
+def _candidate_logits(T, E, k, kind, rng):
+    if kind == "normal":
+        return rng.standard_normal((T, E)).astype(np.float32)
+    if kind == "top_ties":                      # the largest logit repeated on a few experts
+        x = rng.standard_normal((T, E)).astype(np.float32)
+        for t in range(T):
+            x[t, rng.choice(E, size=min(E, k + 3), replace=False)] = x[t].max()
+        return x
+    if kind == "ints":                          # many exact ties everywhere
+        return rng.integers(-50, 51, size=(T, E)).astype(np.float32)
+    # k = 1 and the maximum on exactly 64 (row 0) or 65 (row 1) experts, the
+    # most and one more than the candidate select takes; the rest below it
+    x = rng.uniform(-1.0, 0.5, size=(T, E)).astype(np.float32)
+    for t in range(T):
+        x[t, rng.choice(E, size=64 + (t % 2), replace=False)] = 3.0
+    return x
+
+
+@pytest.mark.parametrize("T,E,k,kind", [(300, 129, 5, "normal"), (300, 200, 16, "top_ties"), (257, 256, 8, "ints"),
+                                        (300, 300, 1, "normal"), (300, 512, 10, "top_ties"),
+                                        (200, 512, 32, "normal"), (300, 1000, 20, "ints"),
+                                        (4, 512, 1, "max_64_65"), (4, 1024, 1, "max_64_65")])
+def test_route_candidate_select(T, E, k, kind):
+    """More than 128 experts: the select over the keys at or above the k-th
+    largest lane maximum (at most 64 of them), or over every key when more
+    are; ids and weights as the oracle, ties to the lower expert."""
+    rng = np.random.default_rng(T * E + k)
+    logits = _candidate_logits(T, E, k, kind, rng)
+    say("route-candidates", T, E, k, kind)
+    ids, w = M.moe_route(cuda(torch.from_numpy(logits)), k, O.SCORE_SOFTMAX)
+    torch.cuda.synchronize()
+    rid, rw = O.route(logits, k, O.SCORE_SOFTMAX)
+    np.testing.assert_array_equal(ids.cpu().numpy(), rid)
+    assert_route_weights(w.cpu().numpy(), rw)
+
+
 @pytest.mark.parametrize("T,E,k,S", [(100, 16, 4, 1), (33, 64, 8, 3), (5, 4, 2, 2), (257, 512, 10, 1)])
 def test_route_shared_matches_oracle(T, E, k, S):
     rng = np.random.default_rng(T + E)
