@@ -107,6 +107,7 @@ struct Params {
   int64_t A;
   int M, N, K, E, block_m;
   uint32_t a_bytes, b_bytes;  // bytes of the operands (below 2^31)
+  uint32_t gu_bytes;          // kDh: bytes of gu and of dGU (below 2^31)
 };
 
 template <int MODE>
@@ -332,6 +333,62 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_bwd_kernel(Params p) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int nl = wn * TN + j * 32 + (lane & 31);
+      if constexpr (MODE == kDh) {
+        // dGU of this 32-row block: the saved pre-activations are all loaded
+        // before the first is used, the results are packed in place into the
+        // block's accumulators, and then all stored. (Loaded, computed and
+        // stored one pair at a time, every pair waited for its loads, and the
+        // registers' reuse made every pair wait for the stores before it too:
+        // 32 dependent round trips a task.)
+        // Buffer loads and stores with an out-of-range offset past column M
+        // (zeros / dropped) keep the block free of branches.
+        const int64_t r = row0 + nl;
+        const __amdgpu_buffer_rsrc_t gu_rs = make_rsrc(p.gu, p.gu_bytes), o_rs = make_rsrc(p.out, p.gu_bytes);
+        uint32_t goff[FM][4];
+        i32x2 gq[FM][4], uq[FM][4];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int m = m0 + wm * TM + i * 32 + g * 8 + (lane >> 5) * 4;
+            goff[i][g] = m < p.M ? static_cast<uint32_t>((r * 2 * p.M + m) * 2) : kOob;
+            gq[i][g] = __builtin_amdgcn_raw_buffer_load_b64(gu_rs, goff[i][g], 0, 0);
+            uq[i][g] = __builtin_amdgcn_raw_buffer_load_b64(gu_rs, goff[i][g] == kOob ? kOob : goff[i][g] + p.M * 2,
+                                                            0, 0);
+          }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const uint32_t gw[2] = {static_cast<uint32_t>(gq[i][g][0]), static_cast<uint32_t>(gq[i][g][1])};
+            const uint32_t uw[2] = {static_cast<uint32_t>(uq[i][g][0]), static_cast<uint32_t>(uq[i][g][1])};
+            float dg[4], du[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const float dh = acc[i][j][g * 4 + v];
+              const uint32_t gb = (gw[v >> 1] >> (16 * (v & 1))) & 0xFFFFu;
+              const uint32_t ub = (uw[v >> 1] >> (16 * (v & 1))) & 0xFFFFu;
+              const float gv = __uint_as_float(gb << 16), uv = __uint_as_float(ub << 16);
+              const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gv));
+              dg[v] = dh * uv * sg * (1.0f + gv * (1.0f - sg));
+              du[v] = dh * gv * sg;
+            }
+            acc[i][j][g * 4] = __uint_as_float(pack_bf16x2(dg[0], dg[1]));
+            acc[i][j][g * 4 + 1] = __uint_as_float(pack_bf16x2(dg[2], dg[3]));
+            acc[i][j][g * 4 + 2] = __uint_as_float(pack_bf16x2(du[0], du[1]));
+            acc[i][j][g * 4 + 3] = __uint_as_float(pack_bf16x2(du[2], du[3]));
+          }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const i32x2 dgw = {__float_as_int(acc[i][j][g * 4]), __float_as_int(acc[i][j][g * 4 + 1])};
+            const i32x2 duw = {__float_as_int(acc[i][j][g * 4 + 2]), __float_as_int(acc[i][j][g * 4 + 3])};
+            __builtin_amdgcn_raw_buffer_store_b64(dgw, o_rs, goff[i][g], 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(duw, o_rs, goff[i][g] == kOob ? kOob : goff[i][g] + p.M * 2, 0, 0);
+          }
+        continue;
+      }
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         if constexpr (MODE == kDx) {
@@ -372,25 +429,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_bwd_kernel(Params p) {
           const int m = m0 + wm * TM + i * 32 + g * 8 + (lane >> 5) * 4;
           if (m >= p.M) continue;
           const float a4[4] = {acc[i][j][g * 4], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2], acc[i][j][g * 4 + 3]};
-          if (MODE == kDh) {
-            const int64_t r = row0 + nl;
-            const uint2 gq = *reinterpret_cast<const uint2*>(p.gu + r * 2 * p.M + m);
-            const uint2 uq = *reinterpret_cast<const uint2*>(p.gu + r * 2 * p.M + p.M + m);
-            const uint32_t gw[2] = {gq.x, gq.y}, uw[2] = {uq.x, uq.y};
-            float dg[4], du[4];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const uint32_t gb = (gw[v >> 1] >> (16 * (v & 1))) & 0xFFFFu;
-              const uint32_t ub = (uw[v >> 1] >> (16 * (v & 1))) & 0xFFFFu;
-              const float gv = __uint_as_float(gb << 16), uv = __uint_as_float(ub << 16);
-              const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-gv));
-              dg[v] = a4[v] * uv * sg * (1.0f + gv * (1.0f - sg));
-              du[v] = a4[v] * gv * sg;
-            }
-            uint16_t* o = static_cast<uint16_t*>(p.out) + r * 2 * p.M + m;
-            *reinterpret_cast<uint2*>(o) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
-            *reinterpret_cast<uint2*>(o + p.M) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
-          } else {
+          {
             const int sid = p.sorted_ids[row0 + nl];
             if (sid < p.A) {
               uint16_t* o = static_cast<uint16_t*>(p.out) + static_cast<int64_t>(sid) * p.M + m;
@@ -432,6 +471,7 @@ hipError_t launch_bwd_dh(const BwdArgs& g, const DeviceInfo& dev, hipStream_t s)
   p.E = g.E;
   p.block_m = g.block_m;
   p.b_bytes = static_cast<uint32_t>(g.cap * g.H * 2);
+  p.gu_bytes = static_cast<uint32_t>(g.cap * 2 * g.I * 2);
   return launch<kDh>(p, (g.cap / g.block_m) * ((g.I + BO - 1) / BO), dev, s);
 }
 
