@@ -55,6 +55,7 @@ static_assert(2 * STAGE <= 160 * 1024 && 3 * T_TILE + 2 * N_TILE <= 160 * 1024 &
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef short v4s __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s* lds_v4s_ptr;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -330,6 +331,15 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_bwd_kernel(Params p) {
       continue;
     }
     // epilogue: lane holds M indices 8 (v / 4) + 4 (lane / 32) + v % 4 of N index lane % 32
+    // (dx: the assignment rows of the lane's N indices, loaded together, and
+    // branch-free buffer stores, so that the blocks do not wait one by one)
+    int dx_sid[FN];
+    __amdgpu_buffer_rsrc_t dx_rs = make_rsrc(p.out, 0);
+    if constexpr (MODE == kDx) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) dx_sid[j] = p.sorted_ids[row0 + wn * TN + j * 32 + (lane & 31)];
+      dx_rs = make_rsrc(p.out, static_cast<uint32_t>(p.A * p.M * 2));
+    }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int nl = wn * TN + j * 32 + (lane & 31);
@@ -398,7 +408,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_bwd_kernel(Params p) {
           // first operand for the lower lanes' second) leaves lane r groups 0,
           // 1 and lane r + 32 groups 2, 3 whole, stored 16 bytes at a time
           const int mb = m0 + wm * TM + i * 32;
-          const int sid = p.sorted_ids[row0 + nl];
+          const int sid = dx_sid[j];
           uint32_t o[4][2], from_lo[2][2], from_hi[2][2];
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
@@ -419,8 +429,9 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_bwd_kernel(Params p) {
             const int m = mb + (upper ? q + 2 : q) * 8;
             const uint4 st = upper ? make_uint4(from_lo[q][0], from_lo[q][1], o[q + 2][0], o[q + 2][1])
                                    : make_uint4(o[q][0], o[q][1], from_hi[q][0], from_hi[q][1]);
-            if (m < p.M && sid < p.A)
-              *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.out) + static_cast<int64_t>(sid) * p.M + m) = st;
+            const uint32_t off = m < p.M && sid < p.A ? static_cast<uint32_t>((static_cast<int64_t>(sid) * p.M + m) * 2)
+                                                      : kOob;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4v, st), dx_rs, off, 0, 0);
           }
           continue;
         }
