@@ -37,6 +37,7 @@ constexpr int kDh = 0;
 constexpr int kDx = 1;
 constexpr int kWgrad = 2;
 constexpr uint32_t kOob = 0x7FFFFFF0u;
+constexpr int kWgradGroupN = 8;   // weight gradients: n-tiles walked side by side (see the task order)
 constexpr int BK = 64;            // K per pipeline step
 constexpr int BO = 256;           // output tile: M (and N) extent per workgroup
 constexpr int WM = 4, WN = 2;     // waves along M and N
@@ -147,10 +148,24 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_bwd_kernel(Params p) {
     int e, m0, n0, nk;
     int64_t row0 = 0;          // dgrad: first sorted row of the row tile; wgrad: first row of expert e
     if (WGRAD) {
+      // Within an expert the n-tiles go in groups of G, n fastest: the tasks
+      // that run together share each P tile (m) and the group's Q tiles (n,
+      // 2 MB for 512 rows) stay in L2 while the m-tiles pass; G = 1 is m
+      // fastest, where every n-tile reads all of the expert's P rows again
+      // (several MB, from beyond L2: 12x the algorithmic bytes on the Scout
+      // shape) but the tasks that run together write whole rows of dW. Groups
+      // of 8 paid where the M side has at least as many tiles as the N side
+      // (Scout dW2, 32 x 20 tiles: 1490 -> 1370 us; Qwen3-30B-A3B dW1, 8 x 6:
+      // 767 -> 726 us) and cost where it has fewer (Scout dW1, 20 x 64: 2552
+      // -> 2793 us; Qwen3 dW2, 3 x 8, level), same-process medians.
+      const int G = ntm >= ntn_w ? kWgradGroupN : 1;
       e = static_cast<int>(task / (static_cast<int64_t>(ntn_w) * ntm));
       const int rem = static_cast<int>(task - static_cast<int64_t>(e) * ntn_w * ntm);
-      n0 = (rem / ntm) * BO;
-      m0 = (rem % ntm) * BO;
+      const int ng = rem / (G * ntm);
+      const int gn = ntn_w - ng * G < G ? ntn_w - ng * G : G;
+      const int loc = rem - ng * G * ntm;
+      m0 = (loc / gn) * BO;
+      n0 = (ng * G + loc % gn) * BO;
       row0 = p.offsets[e];
       nk = (p.offsets[e + 1] - p.offsets[e] + BK - 1) / BK;
     } else {
