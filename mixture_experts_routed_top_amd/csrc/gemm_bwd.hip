@@ -38,6 +38,7 @@ constexpr int kDx = 1;
 constexpr int kWgrad = 2;
 constexpr uint32_t kOob = 0x7FFFFFF0u;
 constexpr int kWgradGroupN = 8;   // weight gradients: n-tiles walked side by side (see the task order)
+constexpr int kDgradGroup = 4;    // dgrad: row tiles of one expert walked side by side (see the task order)
 constexpr int BK = 64;            // K per pipeline step
 constexpr int BO = 256;           // output tile: M (and N) extent per workgroup
 constexpr int WM = 4, WN = 2;     // waves along M and N
@@ -144,6 +145,15 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_bwd_kernel(Params p) {
   const int64_t t0 = total * (xcd * (G / kXcds) + (xcd < G % kXcds ? xcd : G % kXcds)) / G;
   const int64_t t1 = total * ((xcd + 1) * (G / kXcds) + (xcd + 1 < G % kXcds ? xcd + 1 : G % kXcds)) / G;
 
+  // dgrad task order: the row tiles of one expert (groups of up to
+  // kDgradGroup) walk the weight slices side by side, so that the tasks that
+  // read the same slice run together and share it in L2 (m fastest per row
+  // tile read every slice once per row tile: twice the weight bytes on the
+  // Scout shape); the tile-list probe is loaded one task ahead in the dx
+  // kernel and when the task starts in the dGU kernel (carried across the
+  // k-loop it needs one register more than that kernel has)
+  const int num_rt = WGRAD ? 0 : *p.num_tiles;
+  int probe = MODE == kDx && t0 + local < t1 ? grouped_probe(t0 + local, ntm, num_rt, p.tile_expert, lane) : 0;
   for (int64_t task = t0 + local; task < t1; task += per_xcd) {
     int e, m0, n0, nk;
     int64_t row0 = 0;          // dgrad: first sorted row of the row tile; wgrad: first row of expert e
@@ -169,9 +179,11 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_bwd_kernel(Params p) {
       row0 = p.offsets[e];
       nk = (p.offsets[e + 1] - p.offsets[e] + BK - 1) / BK;
     } else {
-      const int rt = static_cast<int>(task / ntm);
-      m0 = static_cast<int>(task - static_cast<int64_t>(rt) * ntm) * BO;
-      e = p.tile_expert[rt];
+      int mt, rt;
+      if (MODE == kDh) probe = grouped_probe(task, ntm, num_rt, p.tile_expert, lane);
+      grouped_task<kDgradGroup>(task, ntm, num_rt, p.tile_expert, lane, probe, mt, rt, e);
+      if (MODE == kDx && task + per_xcd < t1) probe = grouped_probe(task + per_xcd, ntm, num_rt, p.tile_expert, lane);
+      m0 = mt * BO;
       row0 = static_cast<int64_t>(rt) * p.block_m;
       n0 = 0;
       nk = (p.K + BK - 1) / BK;
