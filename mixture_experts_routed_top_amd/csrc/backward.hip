@@ -71,31 +71,40 @@ __global__ __launch_bounds__(256) void backward_combine_kernel(const uint16_t* _
   if (lane == 0) dw[a] = dot;
 }
 
-// one thread per (token, routed expert)
+// one wave per token: lane j < k holds slot j; the weighted sum over the
+// slots is formed once (in slot order, fused multiply-adds, as the per-slot
+// formula reads), and each lane writes its experts' entries of the row
+// (the gradient of the slot that selected the expert, else 0)
 __global__ __launch_bounds__(256) void route_backward_kernel(const float* __restrict__ w,
                                                              const int32_t* __restrict__ ids,
                                                              const float* __restrict__ dw, int64_t T, int E,
                                                              int k, int kk, int score,
                                                              float* __restrict__ dlogits) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= T * E) return;
-  const int64_t t = i / E;
-  const int e = static_cast<int>(i - t * E);
-  const float* wt = w + t * kk;
-  const float* dwt = dw + t * kk;
-  const int32_t* it = ids + t * kk;
+  const int lane = threadIdx.x & 63;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;   // whole wave
+  const bool slot = lane < k;
+  const float wj = slot ? w[t * kk + lane] : 0.0f;
+  const float dwj = slot ? dw[t * kk + lane] : 0.0f;
+  const int ej = slot ? ids[t * kk + lane] : -1;
+  // lane reads (the slot index is wave-uniform)
+  auto lane_f = [](float v, int j) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j)); };
   float g = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    if (it[j] != e) continue;
-    if (score == 0) {
-      float s = 0.0f;
-      for (int q = 0; q < k; ++q) s = __builtin_fmaf(wt[q], dwt[q], s);
-      g = wt[j] * (dwt[j] - s);
-    } else {
-      g = dwt[j] * wt[j] * (1.0f - wt[j]);
-    }
+  if (score == 0) {
+    float s = 0.0f;
+    for (int q = 0; q < k; ++q) s = __builtin_fmaf(lane_f(wj, q), lane_f(dwj, q), s);
+    g = wj * (dwj - s);
+  } else {
+    g = dwj * wj * (1.0f - wj);
   }
-  dlogits[i] = g;
+  float* row = dlogits + t * E;
+  for (int e0 = 0; e0 < E; e0 += 64) {
+    const int e = e0 + lane;
+    float v = 0.0f;
+    for (int j = 0; j < k; ++j)
+      if (__builtin_amdgcn_readlane(ej, j) == e) v = lane_f(g, j);
+    if (e < E) row[e] = v;
+  }
 }
 
 // one wave per sorted row
@@ -130,9 +139,8 @@ hipError_t launch_backward_combine(const uint16_t* dout, const float* w, const u
 
 hipError_t launch_route_backward(const float* w, const int32_t* ids, const float* dw, int64_t T, int E, int k,
                                  int kk, int score, float* dlogits, hipStream_t s) {
-  const int64_t n = T * E;
-  route_backward_kernel<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(w, ids, dw, T, E, k, kk, score,
-                                                                               dlogits);
+  route_backward_kernel<<<static_cast<unsigned>((T + 3) / 4), 256, 0, s>>>(w, ids, dw, T, E, k, kk, score,
+                                                                           dlogits);
   return hipGetLastError();
 }
 
