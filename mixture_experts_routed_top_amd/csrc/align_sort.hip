@@ -4,21 +4,21 @@
 // per-tile rescan of experts; Liger-Kernel PR #1463, Summary: empty experts
 // own no work).
 //
-// A deterministic counting sort in four launches (two for small problems,
-// where 2-4 run as one: scan_scatter_kernel below; one workgroup for at most
+// A deterministic counting sort in two launches (one workgroup for at most
 // 2048 assignments: one_block_kernel, the same steps in LDS):
 //   1. count_rank: each 1024-assignment chunk is split over 4 wavefronts; a
 //      wave ranks its 64 assignments at a time by matching equal expert ids
 //      with one ballot per id bit (a wave-wide "match any"), so each
 //      assignment gets its rank among the earlier, equal-expert assignments
 //      of its chunk; per-chunk expert counts go to the workspace.
-//   2. scan_chunks: one block per expert turns its column of chunk counts
-//      into exclusive prefixes (the chunk's base inside the expert) and the
-//      expert's total.
-//   3. offsets: one block pads each count to block_m and scans over experts.
-//   4. scatter: every assignment lands at offsets[e] + chunk base + rank;
-//      the same grid fills pad rows with the sentinel A and writes the tile
-//      queue (tile -> expert, -1 past the last tile).
+//   2. scan and scatter: every block reads all the chunk counts and forms
+//      each expert's total and the base of its own chunk inside each expert,
+//      pads the totals to block_m and scans them over the experts (offsets),
+//      then puts every assignment of its rows at offsets[e] + chunk base +
+//      rank, fills pad rows with the sentinel A and writes the tile queue
+//      (tile -> expert, -1 past the last tile). Small problems (E * chunks
+//      <= 2048) use blocks of 256 rows (scan_scatter_kernel), larger ones
+//      one block of 1024 threads per chunk (scan_scatter_wide_kernel).
 // Nothing depends on the order of atomic operations, so the output is the
 // stable order by (expert, assignment) on every run.
 #include <mutex>
@@ -90,73 +90,6 @@ __global__ __launch_bounds__(256) void count_rank_kernel(const int32_t* __restri
   }
 }
 
-// Exclusive scan of a block of 256 values; returns this thread's prefix and
-// writes the block total to *total (all threads).
-__device__ __forceinline__ int block_exclusive_scan(int v, int* total, int* sh /*[4]*/) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int inc = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(inc, o);
-    if (lane >= o) inc += u;
-  }
-  if (lane == 63) sh[wave] = inc;
-  __syncthreads();
-  int wbase = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const int s = sh[w];
-    if (w < wave) wbase += s;
-    tot += s;
-  }
-  __syncthreads();
-  *total = tot;
-  return wbase + inc - v;
-}
-
-__global__ __launch_bounds__(256) void scan_chunks_kernel(int32_t* __restrict__ chunk_counts, int nchunks,
-                                                          int E, int32_t* __restrict__ counts) {
-  __shared__ int sh[4];
-  const int e = blockIdx.x;
-  int carry = 0;
-  for (int c0 = 0; c0 < nchunks; c0 += 256) {
-    const int c = c0 + threadIdx.x;
-    const int v = c < nchunks ? chunk_counts[static_cast<int64_t>(c) * E + e] : 0;
-    int tot;
-    const int ex = block_exclusive_scan(v, &tot, sh);
-    if (c < nchunks) chunk_counts[static_cast<int64_t>(c) * E + e] = carry + ex;
-    carry += tot;
-  }
-  if (threadIdx.x == 0) counts[e] = carry;
-}
-
-__global__ __launch_bounds__(1024) void offsets_kernel(const int32_t* __restrict__ counts, int E, int block_m,
-                                                       int32_t* __restrict__ offsets,
-                                                       int32_t* __restrict__ num_tiles) {
-  __shared__ int sh[16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = tid < E ? counts[tid] : 0;
-  const int p = (c + block_m - 1) / block_m * block_m;
-  int inc = p;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(inc, o);
-    if (lane >= o) inc += u;
-  }
-  if (lane == 63) sh[wave] = inc;
-  __syncthreads();
-  int wbase = 0, tot = 0;
-  for (int w = 0; w < 16; ++w) {
-    if (w < wave) wbase += sh[w];
-    tot += sh[w];
-  }
-  if (tid < E) offsets[tid] = wbase + inc - p;
-  if (tid == 0) {
-    offsets[E] = tot;
-    *num_tiles = tot / block_m;
-  }
-}
-
 // Largest e in [0, E) with off[e] <= r (off non-decreasing, off[0] = 0 <= r).
 __device__ __forceinline__ int find_expert(const int32_t* off, int E, int r) {
   int lo = 0, hi = E - 1;
@@ -168,50 +101,12 @@ __device__ __forceinline__ int find_expert(const int32_t* off, int E, int r) {
   return lo;
 }
 
-__global__ __launch_bounds__(256) void scatter_kernel(const int32_t* __restrict__ ids,
-                                                      const int32_t* __restrict__ local_rank,
-                                                      const int32_t* __restrict__ chunk_base,
-                                                      const int32_t* __restrict__ counts,
-                                                      const int32_t* __restrict__ offsets, int64_t A,
-                                                      int E, int block_m, int64_t cap,
-                                                      int32_t* __restrict__ sorted_ids,
-                                                      int32_t* __restrict__ tile_expert) {
-  __shared__ int32_t off[kMaxE + 1];
-  __shared__ int32_t cnt[kMaxE];
-  for (int e = threadIdx.x; e <= E; e += 256) {
-    off[e] = offsets[e];
-    if (e < E) cnt[e] = counts[e];
-  }
-  __syncthreads();
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  const int total = off[E];
-  if (i < A) {
-    const int e = ids[i];
-    const int64_t c = i / kAlignChunk;
-    const int pos = off[e] + chunk_base[c * E + e] + local_rank[i];
-    sorted_ids[pos] = static_cast<int32_t>(i);
-  }
-  if (i < cap) {
-    const int r = static_cast<int>(i);
-    bool pad = r >= total;
-    if (!pad) {
-      const int e = find_expert(off, E, r);
-      pad = r - off[e] >= cnt[e];
-    }
-    if (pad) sorted_ids[r] = static_cast<int32_t>(A);
-  }
-  if (i < cap / block_m) {
-    const int r = static_cast<int>(i) * block_m;
-    tile_expert[i] = r < total ? find_expert(off, E, r) : -1;
-  }
-}
-
 // Steps 2-4 in one launch, for small problems (E * nchunks <= kFusedScan,
 // where a launch costs more than the work): every block of 256 assignments
 // reads all the chunk counts (coalesced) and adds them into per-expert
 // totals and per-expert prefixes before its own chunk with LDS atomics
 // (integer sums: the order does not matter), scans the padded offsets, then
-// scatters like scatter_kernel. Block 0 writes counts, offsets, num_tiles.
+// scatters its rows. Block 0 writes counts, offsets, num_tiles.
 constexpr int kFusedScan = 2048;
 
 __global__ __launch_bounds__(256) void scan_scatter_kernel(const int32_t* __restrict__ ids,
@@ -293,6 +188,123 @@ __global__ __launch_bounds__(256) void scan_scatter_kernel(const int32_t* __rest
     if (!pad) {
       const int e = find_expert(off, E, r);
       pad = r - off[e] >= tot[e];
+    }
+    if (pad) sorted_ids[r] = static_cast<int32_t>(A);
+  }
+  if (i < cap / block_m) {
+    const int r = static_cast<int>(i) * block_m;
+    tile_expert[i] = r < all ? find_expert(off, E, r) : -1;
+  }
+}
+
+// Steps 2-4 in one launch for the larger problems (E * nchunks > kFusedScan),
+// one block of 1024 threads per 1024 rows, so that block b scatters exactly
+// chunk b's assignments. Every block reads the whole chunk-count matrix (at
+// most a few hundred KB, from L2): thread (s, e), s < S = 1024 / E, adds
+// expert e's counts over the chunks s, s + S, s + 2S, ... in registers, 16
+// loads in flight, both in full (the expert's total) and over the chunks
+// before the block's own (its base inside the expert); the S slices are then
+// added in LDS. The padded scan over the experts and the scatter follow as in
+// scan_scatter_kernel. Integer sums: the result is the same stable order.
+// (It replaced three launches, a column scan per expert, the offsets and the
+// scatter, each a few us of launch and dependency time for almost no work:
+// 65536 assignments over 128 experts 12.5 -> 10.2 us, 64 experts 12.9 -> 9.2
+// us, 163840 over 512 experts 16.6 -> 15.0 us, back-to-back calls.)
+constexpr int kWideLoads = 16;
+static_assert(kAlignChunk == 1024, "one 1024-thread block per chunk");
+
+__global__ __launch_bounds__(1024) void scan_scatter_wide_kernel(const int32_t* __restrict__ ids,
+                                                                 const int32_t* __restrict__ local_rank,
+                                                                 const int32_t* __restrict__ chunk_counts,
+                                                                 int nchunks, int64_t A, int E, int block_m,
+                                                                 int64_t cap, int32_t* __restrict__ counts,
+                                                                 int32_t* __restrict__ offsets,
+                                                                 int32_t* __restrict__ num_tiles,
+                                                                 int32_t* __restrict__ sorted_ids,
+                                                                 int32_t* __restrict__ tile_expert) {
+  __shared__ int32_t ptot[1024];   // per (slice, expert): partial total
+  __shared__ int32_t ppre[1024];   // ... and partial sum over the chunks before this block's
+  __shared__ int32_t tot[kMaxE];
+  __shared__ int32_t pre[kMaxE];
+  __shared__ int32_t off[kMaxE + 1];
+  __shared__ int sh[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t i0 = static_cast<int64_t>(blockIdx.x) * kAlignChunk;
+  const int cb = i0 < A ? static_cast<int>(i0 / kAlignChunk) : nchunks;   // this block's chunk
+  const int S = 1024 / E;                                                  // E <= kMaxE = 1024
+  const int sl = tid / E, e = tid - sl * E;
+  int t_acc = 0, p_acc = 0;
+  if (sl < S) {
+    int c = sl;
+    for (; c + (kWideLoads - 1) * S < nchunks; c += kWideLoads * S) {
+      int v[kWideLoads];
+#pragma unroll
+      for (int u = 0; u < kWideLoads; ++u) v[u] = chunk_counts[static_cast<int64_t>(c + u * S) * E + e];
+#pragma unroll
+      for (int u = 0; u < kWideLoads; ++u) {
+        t_acc += v[u];
+        p_acc += c + u * S < cb ? v[u] : 0;
+      }
+    }
+    for (; c < nchunks; c += S) {
+      const int v = chunk_counts[static_cast<int64_t>(c) * E + e];
+      t_acc += v;
+      p_acc += c < cb ? v : 0;
+    }
+  }
+  ptot[tid] = t_acc;
+  ppre[tid] = p_acc;
+  __syncthreads();
+  if (tid < E) {
+    int a = 0, b = 0;
+    for (int q = 0; q < S; ++q) {
+      a += ptot[q * E + tid];
+      b += ppre[q * E + tid];
+    }
+    tot[tid] = a;
+    pre[tid] = b;
+  }
+  __syncthreads();
+  // padded offsets: exclusive scan over the experts, one a thread
+  const int p = tid < E ? (tot[tid] + block_m - 1) / block_m * block_m : 0;
+  int inc = p;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(inc, o);
+    if (lane >= o) inc += u;
+  }
+  if (lane == 63) sh[wave] = inc;
+  __syncthreads();
+  int wbase = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    if (w < wave) wbase += sh[w];
+    all += sh[w];
+  }
+  if (tid < E) off[tid] = wbase + inc - p;
+  if (tid == 0) off[E] = all;
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    if (tid < E) {
+      offsets[tid] = off[tid];
+      counts[tid] = tot[tid];
+    }
+    if (tid == 0) {
+      offsets[E] = all;   // E may be 1024, one past the last thread
+      *num_tiles = all / block_m;
+    }
+  }
+  const int64_t i = i0 + tid;
+  if (i < A) {
+    const int x = ids[i];
+    sorted_ids[off[x] + pre[x] + local_rank[i]] = static_cast<int32_t>(i);
+  }
+  if (i < cap) {
+    const int r = static_cast<int>(i);
+    bool pad = r >= all;
+    if (!pad) {
+      const int x = find_expert(off, E, r);
+      pad = r - off[x] >= tot[x];
     }
     if (pad) sorted_ids[r] = static_cast<int32_t>(A);
   }
@@ -483,10 +495,9 @@ hipError_t launch_align_sort(const int32_t* ids, int64_t T, int k, int E, int bl
     scan_scatter_kernel<<<blocks, 256, 0, s>>>(ids, local_rank, chunk_counts, nchunks, A, E, block_m, cap, counts,
                                                offsets, num_tiles, sorted_ids, tile_expert);
   } else {
-    scan_chunks_kernel<<<E, 256, 0, s>>>(chunk_counts, nchunks, E, counts);
-    offsets_kernel<<<1, 1024, 0, s>>>(counts, E, block_m, offsets, num_tiles);
-    scatter_kernel<<<blocks, 256, 0, s>>>(ids, local_rank, chunk_counts, counts, offsets, A, E, block_m, cap,
-                                          sorted_ids, tile_expert);
+    const unsigned wide = static_cast<unsigned>((n + kAlignChunk - 1) / kAlignChunk);
+    scan_scatter_wide_kernel<<<wide, 1024, 0, s>>>(ids, local_rank, chunk_counts, nchunks, A, E, block_m, cap,
+                                                   counts, offsets, num_tiles, sorted_ids, tile_expert);
   }
   return hipGetLastError();
 }

@@ -145,6 +145,21 @@ def test_align_sort_edges(T, E, k):
     _align_check(ids, E, 256)
 
 
+# Problems with more than 2048 (expert, chunk) counts take the one-launch
+# scan-and-scatter whose 1024 threads split the experts into 1024 // E slices:
+# one slice (E = 1000), E not dividing 1024 (E = 7, 146 slices), one expert
+# over 2051 chunks (1024 slices, two chunks each), and a ragged last chunk.
+@pytest.mark.parametrize("T,E,k", [(3000, 1000, 1), (300000, 7, 1), (2100000, 1, 1), (8191, 256, 3)])
+def test_align_sort_wide_scan(T, E, k):
+    rng = np.random.default_rng(T * 7 + E)
+    if k == 1:
+        ids = rng.integers(0, E, size=(T, 1)).astype(np.int32)
+    else:
+        ids = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    _align_check(ids, E, 32)
+    _align_check(ids, E, 256)
+
+
 def test_align_sort_all_tokens_one_expert():
     ids = np.full((2048, 1), 3, np.int32)        # experts 0..2 and 4..7 empty
     _align_check(ids, 8, 64)
