@@ -33,9 +33,16 @@
 //
 // One k-step stages 128 K elements: a 128-byte token row (E4M3), a 128-byte
 // (E4M3) or 64-byte (E2M1) weight row, and one 32-bit scale word per row
-// (the fp32 1x128 token scale, or four E8M0 bytes). LDS is double buffered;
-// 16-byte chunks are XOR-swizzled per row so that the fragment reads of 16
-// consecutive rows fall on distinct banks. The 32-row MX GEMM1 tile (small
+// (the fp32 1x128 token scale, or four E8M0 bytes). The 64- to 256-row tiles
+// split each k-step's LDS stage as the BF16 kernels do: token rows and their
+// scale words in one of two buffers, weight rows (with their MX scale words)
+// in one of three, so that the weight rows, most of the L2 misses, stream two
+// k-steps ahead, with one exact wait count per step (FP8 GEMM2 on the
+// 64-expert H 7168 shape 1517 -> 1437 us at T = 8192, 232 -> 209 us at
+// T = 512; MX T = 16384 GEMM1 807 -> 772 us, GEMM2 541 -> 513 us; same
+// process). The 32-row tiles keep whole stages, double (MX) or quadruple
+// (FP8) buffered. 16-byte chunks are XOR-swizzled per row so that the
+// fragment reads of 16 consecutive rows fall on distinct banks. The 32-row MX GEMM1 tile (small
 // token counts, bound by the weight stream) stages two such k-steps at once:
 // a 64-byte E2M1 slice is half an L2 line, and the number of requests a CU
 // keeps in flight, not their size, limits the stream, so whole 128-byte
@@ -70,7 +77,12 @@ __device__ __forceinline__ void store_codes_x32(uint8_t* dst, const uint32_t (&q
 
 template <int BM, int BN, int WM, int WN, bool GEMM1, int MODE, int NST_ = 2, int KSUB_ = 1>
 struct Cfg {
-  static constexpr int NST = NST_;                          // LDS stages (2 or 4)
+  // LDS stages: 2 or 4 whole stages, or 3 = split: the token rows of a k-step
+  // with their scale words in one of two buffers, its weight rows (with
+  // their MX scale words) in one of three, so that the weight rows stream two
+  // k-steps ahead
+  static constexpr int NST = NST_;
+  static constexpr bool SPLIT = NST_ == 3;
   // 128-K substeps per stage. MX stages two, so that a weight row's slice is
   // 128 bytes (256 E2M1): one whole L2 line per request instead of two halves
   static constexpr int KSUB = KSUB_;
@@ -97,6 +109,15 @@ struct Cfg {
   static constexpr int S_GROUPS = S_GROUPS_SUB * KSUB;
   static constexpr int SPW = (S_GROUPS + WAVES - 1) / WAVES;
   static constexpr int STAGE = A_REGION + W_REGION + S_GROUPS * 256;
+  // split stages: token buffer = token rows + their scale words, weight
+  // buffer = weight rows + (MX) their scale words; every wave issues GPW_T
+  // token, SPW_T token-scale, GPW_W weight and SPW_W weight-scale loads a
+  // k-step (spare scale slots load into a sink)
+  static constexpr int S_TOK_G = S_TOK / 64, S_W_G = MODE == kMx ? B_ROWS / 64 : 0;
+  static constexpr int T_BUF = A_REGION + S_TOK_G * 256, W_BUF = W_REGION + S_W_G * 256;
+  static constexpr int GPW_T = A_GROUPS / WAVES, GPW_W = W_GROUPS / WAVES;
+  static constexpr int SPW_T = (S_TOK_G + WAVES - 1) / WAVES, SPW_W = (S_W_G + WAVES - 1) / WAVES;
+  static constexpr int LDS_STAGES = SPLIT ? 2 * T_BUF + 3 * W_BUF + 1024 : NST * STAGE + (NST > 2 ? 1024 : 0);
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile is a multiple of 32");
   static_assert(BM % 8 == 0 && W_REGION % 1024 == 0, "whole 1 KB load groups");
   // FP8: a wave's weight rows must lie in one 128-row scale block: tiles start
@@ -104,9 +125,11 @@ struct Cfg {
   // TN dividing 128 keep every wave's rows inside one block
   static_assert(MODE != kFp8Block || (TN <= 128 && 128 % TN == 0 && (BN % 128 == 0 || 128 % BN == 0)),
                 "a wave's weight rows share one 128x128 scale block");
-  static_assert(NST == 2 || NST == 4, "double or quadruple buffering");
+  static_assert(NST == 2 || NST == 3 || NST == 4, "double, split or quadruple buffering");
+  static_assert(!SPLIT || (KSUB == 1 && A_GROUPS % WAVES == 0 && W_GROUPS % WAVES == 0 && B_ROWS % 64 == 0),
+                "split stages: one substep, the same token and weight loads in every wave");
   static_assert(KSUB == 1 || (KSUB == 2 && MODE == kMx && NST == 2), "two substeps: MX, double buffered");
-  static_assert(NST * STAGE + WN * BM * 4 + (NST > 2 ? 1024 : 0) <= 160 * 1024, "the stages fit in LDS");
+  static_assert(LDS_STAGES + WN * BM * 4 <= 160 * 1024, "the stages fit in LDS");
   static_assert((NST - 2) * (GPW + SPW) < 64, "outstanding loads fit the counter");
 };
 
@@ -197,6 +220,51 @@ __device__ __forceinline__ void issue_loads(char* stage, char* sink, int kt, int
   }
 }
 
+// Split stages: the direct-to-LDS loads of k-step kt's token rows (1 KB
+// groups) and their scale words (256 B groups) into token buffer `tb`, and of
+// its weight rows and (MX) their scale words into weight buffer `wb`. A wave
+// without a scale group of its own loads zeros into `sink`, so that every
+// wave issues the same count. k-steps past the end read zeros.
+template <class C>
+__device__ __forceinline__ void issue_split_tokens(char* tb, char* sink, int kt, int nk, int wave,
+                                                   __amdgpu_buffer_rsrc_t a_rsrc, __amdgpu_buffer_rsrc_t as_rsrc,
+                                                   const uint32_t (&toff)[C::GPW_T],
+                                                   const uint32_t (&tsoff)[C::SPW_T]) {
+  const bool live = kt < nk;
+#pragma unroll
+  for (int q = 0; q < C::GPW_T; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr_t)(tb + (wave * C::GPW_T + q) * 1024), 16,
+                                             live ? toff[q] : kOob, static_cast<uint32_t>(kt) * 128, 0, 0);
+#pragma unroll
+  for (int q = 0; q < C::SPW_T; ++q) {
+    const int g = wave + q * C::WAVES;
+    const bool real = g < C::S_TOK_G;
+    char* const dst = real ? tb + C::A_REGION + g * 256 : sink;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(as_rsrc, (lds_ptr_t)dst, 4, live && real ? tsoff[q] : kOob,
+                                             static_cast<uint32_t>(kt) * 4, 0, 0);
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void issue_split_weights(char* wb, char* sink, int kt, int nk, int wave,
+                                                    __amdgpu_buffer_rsrc_t w_rsrc, __amdgpu_buffer_rsrc_t ws_rsrc,
+                                                    const uint32_t (&woff)[C::GPW_W],
+                                                    const uint32_t (&wsoff)[C::SPW_W > 0 ? C::SPW_W : 1]) {
+  const bool live = kt < nk;
+#pragma unroll
+  for (int q = 0; q < C::GPW_W; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_ptr_t)(wb + (wave * C::GPW_W + q) * 1024), 16,
+                                             live ? woff[q] : kOob, static_cast<uint32_t>(kt) * C::W_BYTES, 0, 0);
+#pragma unroll
+  for (int q = 0; q < C::SPW_W; ++q) {
+    const int g = wave + q * C::WAVES;
+    const bool real = g < C::S_W_G;
+    char* const dst = real ? wb + C::W_REGION + g * 256 : sink;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ws_rsrc, (lds_ptr_t)dst, 4, live && real ? wsoff[q] : kOob,
+                                             static_cast<uint32_t>(kt) * 4, 0, 0);
+  }
+}
+
 struct Params {
   const uint8_t* a;          // GEMM1: x codes [T, H]; GEMM2: h codes [cap, I]
   const void* a_scale;       // fp32 [rows, K/128] or E8M0 [rows, K/32]
@@ -220,11 +288,18 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_scaled_kernel(Params p
   constexpr int WB = C::W_BYTES;
   // one LDS array per stage, so that the compiler can tell the stages being
   // filled by direct-to-LDS loads from the one being read
-  __shared__ __attribute__((aligned(1024))) char stage0[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) char stage1[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) char stage2[NST > 2 ? C::STAGE : 16];
-  __shared__ __attribute__((aligned(1024))) char stage3[NST > 2 ? C::STAGE : 16];
+  constexpr bool SPLIT = C::SPLIT;
+  __shared__ __attribute__((aligned(1024))) char stage0[SPLIT ? 16 : C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage1[SPLIT ? 16 : C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage2[NST == 4 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) char stage3[NST == 4 ? C::STAGE : 16];
   __shared__ __attribute__((aligned(1024))) char sink[NST > 2 ? 1024 : 16];   // target of the padding loads
+  // split stages: two token buffers (rows + scale words), three weight buffers
+  __shared__ __attribute__((aligned(1024))) char tbuf0[SPLIT ? C::T_BUF : 16];
+  __shared__ __attribute__((aligned(1024))) char tbuf1[SPLIT ? C::T_BUF : 16];
+  __shared__ __attribute__((aligned(1024))) char wbuf0[SPLIT ? C::W_BUF : 16];
+  __shared__ __attribute__((aligned(1024))) char wbuf1[SPLIT ? C::W_BUF : 16];
+  __shared__ __attribute__((aligned(1024))) char wbuf2[SPLIT ? C::W_BUF : 16];
   __shared__ float red[WN][BM];   // per-row partial amax of each n-wave (FP8 requantisation)
 
   // the wave index is uniform across the wave: keep it in a scalar register so
@@ -369,15 +444,17 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_scaled_kernel(Params p
 #pragma unroll
       for (int i = 0; i < C::FM; ++i) fprev[h][i] = 0.0f;
 
-    auto compute = [&](const char* base, int kt) {
+    // tbase: the k-step's token rows; wbase: its weight rows; sbase: the token
+    // rows' scale words; wsbase: (MX) the weight rows' scale words
+    auto compute = [&](const char* tbase, const char* wbase, const char* sbase, const char* wsbase, int kt) {
       const int hl = lane >> 5;   // which 32-deep half of a 64-deep MFMA step this lane holds
       if (MODE == kMx) {
 #pragma unroll
         for (int sub = 0; sub < C::KSUB; ++sub) {
           if (C::KSUB > 1 && kt * C::KSUB + sub >= nk128) break;   // K ends inside the stage
-          const char* abase = base + sub * C::A_SUB;
-          const uint32_t* sc =
-              reinterpret_cast<const uint32_t*>(base + C::A_REGION + C::W_REGION + sub * C::S_GROUPS_SUB * 256);
+          const char* abase = tbase + sub * C::A_SUB;
+          const uint32_t* sc = reinterpret_cast<const uint32_t*>(sbase + sub * C::S_GROUPS_SUB * 256);
+          const uint32_t* wsc = reinterpret_cast<const uint32_t*>(wsbase + sub * C::S_GROUPS_SUB * 256);
           uint32_t tsc[C::FM];
 #pragma unroll
           for (int i = 0; i < C::FM; ++i) tsc[i] = sc[wm * C::TM + i * 32 + (lane & 31)];
@@ -397,8 +474,8 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_scaled_kernel(Params p
 #pragma unroll
               for (int j = 0; j < C::FN; ++j) {
                 const int r = h * BN + wn * C::TN + j * 32 + (lane & 31);
-                const i32x8 wf = frag16(base + C::A_REGION + w_off<WB>(r, sub * 4 + s * 2 + hl));
-                const int ws = static_cast<int>((sc[C::S_TOK + r] >> (8 * blk)) & 0xFF);
+                const i32x8 wf = frag16(wbase + w_off<WB>(r, sub * 4 + s * 2 + hl));
+                const int ws = static_cast<int>((wsc[r] >> (8 * blk)) & 0xFF);
 #pragma unroll
                 for (int i = 0; i < C::FM; ++i)
                   acc[h][i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf, xf[i], acc[h][i][j], 4, 0, 0,
@@ -408,7 +485,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_scaled_kernel(Params p
           }
         }
       } else {
-        const uint32_t* sc = reinterpret_cast<const uint32_t*>(base + C::A_REGION + C::W_REGION);
+        const uint32_t* sc = reinterpret_cast<const uint32_t*>(sbase);
         // Per-128 promotion without a second accumulator set. Each scale s
         // splits into a power of two, which the MFMA applies itself through
         // its E8M0 operand scales (token: per lane, weight block: per wave),
@@ -456,15 +533,14 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_scaled_kernel(Params p
 #pragma unroll
           for (int i = 0; i < C::FM; ++i) {
             const int r = wm * C::TM + i * 32 + (lane & 31);
-            xf[i] = frag32(base + a_off(r, s * 4 + hl), base + a_off(r, s * 4 + 2 + hl));
+            xf[i] = frag32(tbase + a_off(r, s * 4 + hl), tbase + a_off(r, s * 4 + 2 + hl));
           }
 #pragma unroll
           for (int h = 0; h < C::HALVES; ++h) {
 #pragma unroll
             for (int j = 0; j < C::FN; ++j) {
               const int r = h * BN + wn * C::TN + j * 32 + (lane & 31);
-              const i32x8 wf = frag32(base + C::A_REGION + w_off<WB>(r, s * 4 + hl),
-                                      base + C::A_REGION + w_off<WB>(r, s * 4 + 2 + hl));
+              const i32x8 wf = frag32(wbase + w_off<WB>(r, s * 4 + hl), wbase + w_off<WB>(r, s * 4 + 2 + hl));
 #pragma unroll
               for (int i = 0; i < C::FM; ++i)
                 acc[h][i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf, xf[i], acc[h][i][j], 0, 0, 0,
@@ -475,22 +551,97 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_scaled_kernel(Params p
       }
     };
 
-    if (NST == 2) {
+    if constexpr (SPLIT) {
+      // Split stages (as in the BF16 kernels): k-step s reads its token rows
+      // and their scale words from token buffer s % 2 and its weight rows
+      // (and MX weight scale words) from weight buffer s % 3. Issue order per
+      // step: tokens of s + 1, then weights of s + 2; so when step s starts,
+      // everything but the newest GPW_W + SPW_W loads (the weights of s + 1)
+      // has landed. The barrier
+      // after that wait also means every wave has finished step s - 1, whose
+      // buffers step s refills. Six steps repeat the buffer pattern; k-steps
+      // past the end are loaded as zeros but not computed.
+      uint32_t toff[C::GPW_T], woff[C::GPW_W], tsoff[C::SPW_T], wsoff[C::SPW_W > 0 ? C::SPW_W : 1];
+#pragma unroll
+      for (int q = 0; q < C::GPW_T; ++q) {
+        const int row = (wave * C::GPW_T + q) * 8 + (lane >> 3), pc = lane & 7;
+        const int64_t src = token_row(row);
+        toff[q] = src >= 0 ? static_cast<uint32_t>(src * K + ((pc ^ swz128(row)) << 4)) : kOob;
+      }
+#pragma unroll
+      for (int q = 0; q < C::GPW_W; ++q) {
+        const int byte = (wave * C::GPW_W + q) * 1024 + lane * 16;
+        const int br = byte / WB, pc = (byte % WB) / 16;
+        const int lc = WB == 128 ? (pc ^ swz128(br)) : (pc ^ swz64(br));
+        const int wr = weight_row(br);
+        woff[q] = wr >= 0 ? static_cast<uint32_t>(wr) * wrow_bytes + (lc << 4) : kOob;
+      }
+#pragma unroll
+      for (int q = 0; q < C::SPW_T; ++q) {
+        const int r = (wave + q * C::WAVES) * 64 + lane;
+        const int64_t src = r < BM ? token_row(r) : -1;
+        tsoff[q] = src >= 0 ? static_cast<uint32_t>(src * srow_bytes) : kOob;
+      }
+#pragma unroll
+      for (int q = 0; q < (C::SPW_W > 0 ? C::SPW_W : 1); ++q) {
+        const int r = (wave + q * C::WAVES) * 64 + lane;
+        const int wr = C::SPW_W > 0 && r < C::B_ROWS ? weight_row(r) : -1;
+        wsoff[q] = wr >= 0 ? static_cast<uint32_t>(wr) * (K / 32) : kOob;
+      }
+      auto load_t = [&](char* tb, int kt) {
+        issue_split_tokens<C>(tb, sink, kt, nk, wave, a_rsrc, as_rsrc, toff, tsoff);
+      };
+      auto load_w = [&](char* wb, int kt) {
+        issue_split_weights<C>(wb, sink, kt, nk, wave, w_rsrc, ws_rsrc, woff, wsoff);
+      };
+      auto step = [&](char* tb, char* wb, char* tb_next, char* wb_next2, int kt) {
+        wait_vmcnt<C::GPW_W + C::SPW_W>();
+        barrier_no_fence();
+        load_t(tb_next, kt + 1);
+        load_w(wb_next2, kt + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(tb, wb, tb + C::A_REGION, wb + C::W_REGION, kt);
+      };
+      load_t(tbuf0, 0);
+      load_w(wbuf0, 0);
+      load_w(wbuf1, 1);
+      for (int kt = 0;; kt += 6) {
+        step(tbuf0, wbuf0, tbuf1, wbuf2, kt);
+        if (kt + 1 >= nk) break;
+        step(tbuf1, wbuf1, tbuf0, wbuf0, kt + 1);
+        if (kt + 2 >= nk) break;
+        step(tbuf0, wbuf2, tbuf1, wbuf1, kt + 2);
+        if (kt + 3 >= nk) break;
+        step(tbuf1, wbuf0, tbuf0, wbuf2, kt + 3);
+        if (kt + 4 >= nk) break;
+        step(tbuf0, wbuf1, tbuf1, wbuf0, kt + 4);
+        if (kt + 5 >= nk) break;
+        step(tbuf1, wbuf2, tbuf0, wbuf1, kt + 5);
+        if (kt + 6 >= nk) break;
+      }
+      // the loads issued past the end have landed and every wave is done
+      // with LDS before the epilogue and the next task's loads
+      wait_vmcnt<0>();
+      barrier_no_fence();
+    } else if constexpr (NST == 2) {
       // k-step s+1 streams into one stage while the MFMAs consume k-step s
       load(stage0, 0);
       __syncthreads();
       for (int kt = 0; kt < nk; kt += 2) {
         load(stage1, kt + 1);
         __builtin_amdgcn_sched_barrier(0);
-        compute(stage0, kt);
+        compute(stage0, stage0 + C::A_REGION, stage0 + C::A_REGION + C::W_REGION,
+                stage0 + C::A_REGION + C::W_REGION + C::S_TOK * 4, kt);
         __syncthreads();
         if (kt + 1 >= nk) break;
         load(stage0, kt + 2);
         __builtin_amdgcn_sched_barrier(0);
-        compute(stage1, kt + 1);
+        compute(stage1, stage1 + C::A_REGION, stage1 + C::A_REGION + C::W_REGION,
+                stage1 + C::A_REGION + C::W_REGION + C::S_TOK * 4, kt + 1);
         __syncthreads();
       }
     } else {
+      static_assert(NST == 4, "four whole stages");
       // four stages (tiles this small are bound by the weight stream, which
       // wants more bytes in flight): k-step s is read from one stage while
       // k-steps s+1 .. s+3 stream into the others. Each step waits for its
@@ -504,25 +655,29 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_scaled_kernel(Params p
         barrier_no_fence();
         load(stage3, kt + 3);
         __builtin_amdgcn_sched_barrier(0);
-        compute(stage0, kt);
+        compute(stage0, stage0 + C::A_REGION, stage0 + C::A_REGION + C::W_REGION,
+                stage0 + C::A_REGION + C::W_REGION + C::S_TOK * 4, kt);
         if (kt + 1 >= nk) break;
         wait_vmcnt<2 * (C::GPW + C::SPW)>();
         barrier_no_fence();
         load(stage0, kt + 4);
         __builtin_amdgcn_sched_barrier(0);
-        compute(stage1, kt + 1);
+        compute(stage1, stage1 + C::A_REGION, stage1 + C::A_REGION + C::W_REGION,
+                stage1 + C::A_REGION + C::W_REGION + C::S_TOK * 4, kt + 1);
         if (kt + 2 >= nk) break;
         wait_vmcnt<2 * (C::GPW + C::SPW)>();
         barrier_no_fence();
         load(stage1, kt + 5);
         __builtin_amdgcn_sched_barrier(0);
-        compute(stage2, kt + 2);
+        compute(stage2, stage2 + C::A_REGION, stage2 + C::A_REGION + C::W_REGION,
+                stage2 + C::A_REGION + C::W_REGION + C::S_TOK * 4, kt + 2);
         if (kt + 3 >= nk) break;
         wait_vmcnt<2 * (C::GPW + C::SPW)>();
         barrier_no_fence();
         load(stage2, kt + 6);
         __builtin_amdgcn_sched_barrier(0);
-        compute(stage3, kt + 3);
+        compute(stage3, stage3 + C::A_REGION, stage3 + C::A_REGION + C::W_REGION,
+                stage3 + C::A_REGION + C::W_REGION + C::S_TOK * 4, kt + 3);
       }
       // drain the loads issued past the end (zeros) and meet, before the
       // epilogue and the next task's loads
@@ -670,7 +825,7 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_scaled_kernel(Params p
 template <int BM, int BN, int WM, int WN, bool GEMM1, int MODE, int NST = 2, int OCC = 1, int KSUB = 1>
 hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s, int n_begin = 0, int n_end = -1) {
   using C = Cfg<BM, BN, WM, WN, GEMM1, MODE, NST, KSUB>;
-  static_assert(OCC * (NST * C::STAGE + WN * BM * 4 + (NST > 2 ? 1024 : 0)) <= 160 * 1024, "OCC workgroups fit in LDS");
+  static_assert(OCC * (C::LDS_STAGES + WN * BM * 4) <= 160 * 1024, "OCC workgroups fit in LDS");
   Params p;
   p.a = static_cast<const uint8_t*>(g.a);
   p.a_scale = g.a_scale;
@@ -701,18 +856,18 @@ hipError_t launch(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s, int n
 
 hipError_t launch_gemm1_mx_tiles(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   switch (g.block_m) {
-    case 256: return launch<256, 128, 4, 2, true, kMx>(g, dev, s);
+    case 256: return launch<256, 128, 4, 2, true, kMx, 3>(g, dev, s);
     case 128: {
       // I % 256 == 128 (the MXFP4 shape's 640): the last 256-column tile
       // would be half empty, a fifth of the MFMA work on zero weight rows;
       // 128-column tiles take the last 128 columns in a second launch
       // (same-process medians: T = 16384 827 -> 777 us, T = 8192 554 -> 524)
-      if (g.I % 256 == 0 || g.I < 256) return launch<128, 256, 4, 2, true, kMx>(g, dev, s);
-      const hipError_t e = launch<128, 256, 4, 2, true, kMx>(g, dev, s, 0, g.I - 128);
+      if (g.I % 256 == 0 || g.I < 256) return launch<128, 256, 4, 2, true, kMx, 3>(g, dev, s);
+      const hipError_t e = launch<128, 256, 4, 2, true, kMx, 3>(g, dev, s, 0, g.I - 128);
       if (e != hipSuccess) return e;
-      return launch<128, 128, 4, 2, true, kMx>(g, dev, s, g.I - 128);
+      return launch<128, 128, 4, 2, true, kMx, 3>(g, dev, s, g.I - 128);
     }
-    case 64: return launch<64, 256, 1, 8, true, kMx>(g, dev, s);
+    case 64: return launch<64, 256, 1, 8, true, kMx, 3>(g, dev, s);
     case 32: return launch<32, 256, 1, 8, true, kMx, 2, 1, 2>(g, dev, s);
     default: return hipErrorInvalidValue;
   }
@@ -720,9 +875,9 @@ hipError_t launch_gemm1_mx_tiles(const GemmArgs& g, const DeviceInfo& dev, hipSt
 
 hipError_t launch_gemm2_mx_tiles(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   switch (g.block_m) {
-    case 256: return launch<256, 256, 4, 2, false, kMx>(g, dev, s);
-    case 128: return launch<128, 512, 2, 4, false, kMx>(g, dev, s);
-    case 64: return launch<64, 512, 1, 8, false, kMx>(g, dev, s);
+    case 256: return launch<256, 256, 4, 2, false, kMx, 3>(g, dev, s);
+    case 128: return launch<128, 512, 2, 4, false, kMx, 3>(g, dev, s);
+    case 64: return launch<64, 512, 1, 8, false, kMx, 3>(g, dev, s);
     case 32: return launch<32, 512, 1, 8, false, kMx, 2, 2>(g, dev, s);
     default: return hipErrorInvalidValue;
   }
@@ -731,8 +886,8 @@ hipError_t launch_gemm2_mx_tiles(const GemmArgs& g, const DeviceInfo& dev, hipSt
 hipError_t launch_gemm1_fp8_tiles(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   switch (g.block_m) {
     case 256: return launch<256, 128, 4, 2, true, kFp8Block>(g, dev, s);
-    case 128: return launch<128, 128, 2, 4, true, kFp8Block>(g, dev, s);
-    case 64: return launch<64, 128, 2, 4, true, kFp8Block>(g, dev, s);
+    case 128: return launch<128, 128, 2, 4, true, kFp8Block, 3>(g, dev, s);
+    case 64: return launch<64, 128, 2, 4, true, kFp8Block, 3>(g, dev, s);
     case 32: return launch<32, 128, 1, 4, true, kFp8Block, 4>(g, dev, s);
     default: return hipErrorInvalidValue;
   }
@@ -740,9 +895,9 @@ hipError_t launch_gemm1_fp8_tiles(const GemmArgs& g, const DeviceInfo& dev, hipS
 
 hipError_t launch_gemm2_fp8_tiles(const GemmArgs& g, const DeviceInfo& dev, hipStream_t s) {
   switch (g.block_m) {
-    case 256: return launch<256, 128, 4, 2, false, kFp8Block>(g, dev, s);
-    case 128: return launch<128, 256, 2, 4, false, kFp8Block>(g, dev, s);
-    case 64: return launch<64, 256, 2, 4, false, kFp8Block>(g, dev, s);
+    case 256: return launch<256, 128, 4, 2, false, kFp8Block, 3>(g, dev, s);
+    case 128: return launch<128, 256, 2, 4, false, kFp8Block, 3>(g, dev, s);
+    case 64: return launch<64, 256, 2, 4, false, kFp8Block, 3>(g, dev, s);
     case 32: return launch<32, 256, 1, 4, false, kFp8Block, 4>(g, dev, s);
     default: return hipErrorInvalidValue;
   }
