@@ -168,9 +168,12 @@ int32_t moe_pick_block_m(int32_t dtype, int64_t T, int32_t k, int32_t E, int32_t
     return 32;
   }
   // FP8 128-block (same measurement over T = 256 .. 8192 of the 64-expert
-  // H 7168 shape): 256-row tiles from about 128 rows per expert, 128-row ones
-  // from 48 (at 64 rows 685 against 880 us with 64-row tiles)
-  if (mean >= 128) return 256;
+  // H 7168 shape): 256-row tiles from about 384 rows per expert (the 128- and
+  // 64-row tiles split their LDS stages, the 256-row GEMM1 tile cannot: at
+  // 256 rows 1097 against 1041 TFLOP/s with 256-row tiles, at 512 rows 1238
+  // against 1281), 128-row ones from 48 (at 64 rows 564 against 480 TFLOP/s
+  // with 64-row tiles)
+  if (mean >= 384) return 256;
   if (mean >= 48) return 128;
   if (mean >= 24) return 64;
   return 32;

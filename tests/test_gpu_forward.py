@@ -328,14 +328,15 @@ def test_qwen3_ragged_tokens_full_size():
     _sampled_compare(get_config("qwen3_30b_a3b_bf16").with_(T=8191), n_experts=4, n_tokens=6)
 
 
-@pytest.mark.parametrize("T,block_m", [(256, None), (512, None), (1024, None), (1024, 32)])
+@pytest.mark.parametrize("T,block_m", [(256, None), (512, None), (1024, None), (4096, None), (1024, 32)])
 def test_fp8_share_token_counts(T, block_m):
     """The FP8 64-expert H 7168 shape at the token counts where the row-tile
     rule picks 64-, 128- and 256-row tiles (the weight walk of each exceeds
     4 MB, so the grouped task order runs), and with 32-row tiles forced."""
     cfg = get_config("fp8_block128_share").with_(T=T)
     if block_m is None:
-        assert M.moe_pick_block_m(cfg.dtype, T, cfg.k, cfg.E, cfg.H, cfg.I) == {256: 64, 512: 128, 1024: 256}[T]
+        assert M.moe_pick_block_m(cfg.dtype, T, cfg.k, cfg.E, cfg.H, cfg.I) == \
+            {256: 64, 512: 128, 1024: 128, 4096: 256}[T]
     _sampled_compare(cfg, n_experts=4, n_tokens=2, block_m=block_m)
 
 
