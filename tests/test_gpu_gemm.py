@@ -242,6 +242,11 @@ SCALED_SHAPES = [  # T, H, E, k, I, block_m
     # 128-row tiles with I % 256 == 128: the MX GEMM1 takes the last 128 columns in a second launch
     (300, 512, 8, 4, 384, 128),
     (257, 1024, 16, 4, 640, 128),
+    # 64- to 256-row tiles split their LDS stages and run a six-step pipeline
+    # loop: with the shapes above, k-step counts 7 and 1 (H = 896, I = 128)
+    # end it at every position
+    (150, 896, 4, 2, 128, 64),
+    (600, 896, 4, 2, 128, 256),
 ]
 
 
