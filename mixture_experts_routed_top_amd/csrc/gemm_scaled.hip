@@ -41,7 +41,9 @@
 // 64-expert H 7168 shape 1517 -> 1437 us at T = 8192, 232 -> 209 us at
 // T = 512; MX T = 16384 GEMM1 807 -> 772 us, GEMM2 541 -> 513 us; same
 // process). The 32-row tiles keep whole stages, double (MX) or quadruple
-// (FP8) buffered. 16-byte chunks are XOR-swizzled per row so that the
+// (FP8) buffered, and so does the 256-row FP8 GEMM1 tile, whose split stages
+// would need 162 KB of LDS (with its token scales in registers instead they
+// fit in 160 KB, but ran 13% slower). 16-byte chunks are XOR-swizzled per row so that the
 // fragment reads of 16 consecutive rows fall on distinct banks. The 32-row MX GEMM1 tile (small
 // token counts, bound by the weight stream) stages two such k-steps at once:
 // a 64-byte E2M1 slice is half an L2 line, and the number of requests a CU
