@@ -43,9 +43,10 @@
 // process). The 32-row tiles keep whole stages, double (MX) or quadruple
 // (FP8) buffered, and so does the 256-row FP8 GEMM1 tile, whose split stages
 // would need 162 KB of LDS (with its token scales in registers instead they
-// fit in 160 KB, but ran 13% slower). 16-byte chunks are XOR-swizzled per row so that the
-// fragment reads of 16 consecutive rows fall on distinct banks. The 32-row MX GEMM1 tile (small
-// token counts, bound by the weight stream) stages two such k-steps at once:
+// fit in 160 KB, but ran 13% slower). 16-byte chunks are XOR-swizzled per
+// row so that the fragment reads of 16 consecutive rows fall on distinct
+// banks. The 32-row MX GEMM1 tile (small token counts, bound by the weight
+// stream) stages two such k-steps at once:
 // a 64-byte E2M1 slice is half an L2 line, and the number of requests a CU
 // keeps in flight, not their size, limits the stream, so whole 128-byte
 // weight slices carry twice the bytes per request.
