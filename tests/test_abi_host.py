@@ -67,6 +67,20 @@ def test_capacity_and_block_m_rejections():
             assert M.moe_pick_block_m(dt, T, 8, 128, 2048, 768) in (16, 32, 64, 128, 256)
 
 
+# The row-tile rule at the named shapes' token counts (mean rows per expert in
+# brackets), as measured with the current kernels: BF16 Qwen3-30B-A3B shape,
+# FP8 64-expert H 7168 shape (256-row tiles from 384 rows, since its 64- and
+# 128-row tiles split their LDS stages and the 256-row GEMM1 cannot), MXFP4
+# 512-expert shape.
+@pytest.mark.parametrize("dt,T,k,E,H,I,bm", [
+    (0, 512, 8, 128, 2048, 768, 64), (0, 2048, 8, 128, 2048, 768, 128), (0, 8192, 8, 128, 2048, 768, 256),
+    (1, 256, 8, 64, 7168, 2048, 64), (1, 512, 8, 64, 7168, 2048, 128), (1, 2048, 8, 64, 7168, 2048, 128),
+    (1, 4096, 8, 64, 7168, 2048, 256), (1, 8192, 8, 64, 7168, 2048, 256),
+    (2, 128, 10, 512, 2560, 640, 32), (2, 2048, 10, 512, 2560, 640, 64), (2, 16384, 10, 512, 2560, 640, 128)])
+def test_pick_block_m_rule(dt, T, k, E, H, I, bm):
+    assert M.moe_pick_block_m(dt, T, k, E, H, I) == bm
+
+
 def test_workspace_bytes():
     assert M.moe_align_sort_workspace_bytes(0, 8, 128) == 0
     assert M.moe_align_sort_workspace_bytes(64, 2, 8) == 4 * (1 * 8 + 128)
