@@ -227,3 +227,26 @@ def test_device_check_without_gpu():
         pytest.skip("a GPU is present: fake pointers would be dereferenced")
     L = _lib()
     assert L.moe_route(FAKE, 4, 8, 2, 0, FAKE, FAKE, NULL) == M._binding.MOE_ERR_DEVICE
+
+
+def test_compute_calls_reject_host_tensors():
+    """Every compute call takes device tensors only: a host tensor is rejected
+    with ValueError before the library is called, so nothing ever falls back
+    to a CPU computation."""
+    import torch
+    logits = torch.zeros((4, 8), dtype=torch.float32)
+    x = torch.zeros((4, 256), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        M.moe_route(logits, 2)
+    with pytest.raises(ValueError):
+        M.moe_route_shared(logits, 2, 0, 1)
+    with pytest.raises(ValueError):
+        M.moe_align_sort(torch.zeros((4, 2), dtype=torch.int32), 8, 32)
+    with pytest.raises(ValueError):
+        M.moe_quantize_fp8(x, 1)
+    with pytest.raises(ValueError):
+        M.moe_quantize_mxfp8(x)
+    with pytest.raises(ValueError):
+        M.moe_quantize_mxfp4(x)
+    with pytest.raises(ValueError):
+        M.moe_combine(torch.zeros((8, 256), dtype=torch.bfloat16), torch.zeros((4, 2), dtype=torch.float32))
